@@ -1,0 +1,163 @@
+/*
+ * w4a16.h -- C ABI of libw4a16.so, a fused W4A16 linear layer for AMD
+ * Instinct MI355X (gfx950):
+ *
+ *     C[M, N] = A[M, K] @ dequant(W)^T (+ bias),   dequant(W)[n, k] = (q - z) * s
+ *
+ * W is N x K 4-bit codes q with one fp16/bf16 scale s per row and group of G
+ * consecutive k, and a zero z that is the constant 8 (symmetric "uint4b8") or
+ * a stored 4-bit zero point (asymmetric "uint4"). A, scales, bias and C share
+ * one activation dtype (fp16 or bf16); products accumulate in fp32 and C is
+ * rounded once (round to nearest even).
+ *
+ * Where the operations come from (page title, section):
+ *  - the checkpoint layout the repack accepts: "triton_w4a16.py" (Triton-based
+ *    W4A16 GEMM for ROCm MI300), module docstring -- weight_packed [N, K/8]
+ *    int32 with GPTQ sequential packing (eight codes per word, code i at bits
+ *    4i), weight_scale [N, K/G], weight_zero_point [N/8, K/G] int32 packed
+ *    along N (row n at bits 4*(n%8) of word n/8, as the
+ *    `_triton_w4a16_skinny_fmt_kernel` docstring of the "rdna_hybrid_w4a16"
+ *    page, build 58181, states).
+ *  - dequantisation w = (q - z) * s with z = 8 for uint4b8: the
+ *    `triton_w4a16_gemm_kernel` docstring (MI300 page) and
+ *    `dequantize_w4a16` ("rdna_hybrid_w4a16", build 61746).
+ *  - group_size -1 meaning K, and uint4b8 ignoring any zero-point tensor:
+ *    `apply_weights` (MI300 page).
+ *  - one weight buffer serving a small-M ("skinny") kernel and a tiled
+ *    prefill kernel, with a dispatch on M: the module docstring and
+ *    `_rdna_hybrid_w4a16_apply_impl` ("rdna_hybrid_w4a16", both builds).
+ *  - the load-time repack into a kernel-native layout: `process_weights_after_
+ *    loading` on both pages (here a GPU kernel into the layout defined below).
+ *  - the bias added to the output: `apply_weights` (both pages); here it is
+ *    fused in fp32 before the single rounding of C.
+ *
+ * Conventions shared by every call:
+ *  - Pointers are device pointers unless a parameter says "host". All device
+ *    memory is owned by the caller; the library never allocates, frees or
+ *    synchronises (calls are asynchronous on `stream`, NULL = default stream).
+ *  - Every call validates its arguments before any HIP call. A failure
+ *    returns a negative w4a16_status and sets a message readable with
+ *    w4a16_last_error() on the same thread (e.g. "K=4100 must be divisible by
+ *    group_size=128"). Nothing is launched after a validation failure. The
+ *    library never aborts and no exception crosses the ABI.
+ *  - qtype is a w4a16_qtype, dtype a w4a16_dtype, path a w4a16_path (passed
+ *    as int32_t so the ABI does not depend on enum sizes).
+ *  - Shapes: N % 16 == 0, K % 128 == 0; group_size in {-1, 32, 64, 128, 256}
+ *    or group_size == K, with K % group_size == 0; uint4 zero points also need
+ *    N % 8 == 0 (implied). Other shapes return W4A16_ERR_UNSUPPORTED.
+ *
+ * Device layout of the packed buffer (written by w4a16_repack, read by
+ * w4a16_gemm; Ge = K if group_size == -1 else group_size, Kg = K / Ge,
+ * align256(x) rounds x up to a multiple of 256; words are little-endian):
+ *  - Codes at byte 0, N*K/2 bytes: 1024-byte tiles; tile (nt, kt), nt in
+ *    [0, N/16), kt in [0, K/128), starts at ((nt * (K/128)) + kt) * 1024.
+ *    32-bit word 4*l + s of a tile (l in [0, 64), s in [0, 4)) holds the codes
+ *    of row n = 16*nt + l%16 at k = 128*kt + 32*s + 8*(l/16) + i, i = 0..7,
+ *    code i in bits [4*(i/2) + 16*(i%2), +4). One 16-byte load per lane of a
+ *    64-wide wavefront moves a whole tile, and word s of lane l is the B
+ *    operand of a 16x16x32 fp16/bf16 MFMA over k in [128*kt + 32*s, +32).
+ *  - Scales at S0 = align256(N*K/2): N*Kg raw 2-byte fp16/bf16 values;
+ *    element (nt, g, r) = weight_scale[16*nt + r][g] at S0 + ((nt*Kg + g)*16 + r)*2.
+ *  - Zeros (uint4 only) at Z0 = align256(S0 + N*Kg*2): N*Kg bytes, element
+ *    (nt, g, r) = zero of (row 16*nt + r, group g) at Z0 + (nt*Kg + g)*16 + r;
+ *    all 0 when the checkpoint has no zero points.
+ *  - Total size = align256(end of the last region) = w4a16_packed_size().
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_ABI_VERSION 1
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum, stride < width */
+    W4A16_ERR_UNSUPPORTED = -2, /* a shape or group size the device layout cannot hold */
+    W4A16_ERR_SIZE = -3,        /* a caller buffer (packed, workspace) is too small */
+    W4A16_ERR_HIP = -4          /* a HIP call or kernel launch failed */
+} w4a16_status;
+
+typedef enum { W4A16_UINT4B8 = 0, W4A16_UINT4 = 1 } w4a16_qtype;
+typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
+typedef enum { W4A16_PATH_AUTO = 0, W4A16_PATH_SKINNY = 1, W4A16_PATH_MFMA = 2 } w4a16_path;
+
+/* The ABI version this library implements (W4A16_ABI_VERSION). */
+int32_t w4a16_abi_version(void);
+
+/* The message of the last failed call on this thread ("" if none). The pointer
+ * stays valid until the next library call on this thread. */
+const char *w4a16_last_error(void);
+
+/* Bytes of the packed buffer for an N x K weight (layout above). out_bytes is
+ * a host pointer. Fails like w4a16_repack on an unsupported shape. */
+w4a16_status w4a16_packed_size(int64_t N, int64_t K, int32_t group_size, int32_t qtype, size_t *out_bytes);
+
+/* One-time repack of a checkpoint into the packed buffer (bit-exact and
+ * deterministic; checkpoint layout as above):
+ *   weight_packed     [N, K/8] int32, row-major, contiguous
+ *   weight_scale      [N, Kg] fp16/bf16 bits (copied as raw 16-bit values)
+ *   weight_zero_point [N/8, Kg] int32, or NULL; read only for uint4 (NULL
+ *                     means every zero is 0); ignored for uint4b8
+ *   packed            output, packed_bytes >= w4a16_packed_size(...)
+ * The inputs must not overlap the output. W4A16_ERR_SIZE if packed_bytes is
+ * too small. */
+w4a16_status w4a16_repack(const int32_t *weight_packed, const void *weight_scale, const int32_t *weight_zero_point,
+                          int64_t N, int64_t K, int32_t group_size, int32_t qtype, void *packed, size_t packed_bytes,
+                          hipStream_t stream);
+
+/* Test support: the inverse of w4a16_repack. Reads the packed buffer and
+ * writes codes [N, K] (one code per byte, row-major), scale_bits [N, Kg]
+ * (raw 16-bit values) and, for uint4, zeros [N, Kg] bytes. Any output may be
+ * NULL to skip it (zeros is ignored for uint4b8). */
+w4a16_status w4a16_unpack(const void *packed, int64_t N, int64_t K, int32_t group_size, int32_t qtype,
+                          uint8_t *codes, uint16_t *scale_bits, uint8_t *zeros, hipStream_t stream);
+
+/* Bytes of device workspace w4a16_gemm needs for these arguments (0 if none).
+ * out_bytes is a host pointer. The workspace holds split-K partial sums and
+ * arrival counters. Its first w4a16_workspace_counter_bytes() bytes must be
+ * zero before it is first used; every completed w4a16_gemm call leaves them
+ * zero again, so a workspace can be reused for any shape. Calls that share a
+ * workspace must be ordered (same stream); overlapping calls race. */
+w4a16_status w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t path,
+                                  int32_t skinny_max_m, size_t *out_bytes);
+
+/* Size of the counter region at the start of every workspace (a constant). */
+size_t w4a16_workspace_counter_bytes(void);
+
+/* Which kernel w4a16_gemm runs for M rows: W4A16_PATH_SKINNY when
+ * path == AUTO and M <= skinny_max_m (skinny_max_m <= 0 means 16), else the
+ * forced path; W4A16_PATH_MFMA otherwise. Returns a negative status for a
+ * bad path. */
+int32_t w4a16_select_path(int64_t M, int32_t path, int32_t skinny_max_m);
+
+/* C[M, N] = A[M, K] @ dequant(W)^T (+ bias):
+ *   A       [M, lda] act dtype, row-major, lda >= K (unit column stride)
+ *   packed  the buffer written by w4a16_repack for the same N, K,
+ *           group_size and qtype (the call cannot check this)
+ *   bias    [N] act dtype, or NULL
+ *   C       [M, ldc] act dtype, ldc >= N; must not overlap A, packed or bias
+ *   path    AUTO dispatches on M (see w4a16_select_path); SKINNY forces the
+ *           small-M kernel (M > 16 runs it over 16-row slices); MFMA forces
+ *           the tiled kernel
+ *   workspace, workspace_bytes  device workspace, >= w4a16_workspace_size();
+ *           may be NULL when that size is 0
+ * M == 0 is a no-op. The result does not depend on the workspace contents or
+ * on earlier calls (no float atomics: the order of every sum is fixed). */
+w4a16_status w4a16_gemm(const void *A, int64_t M, int64_t lda, const void *packed, int64_t N, int64_t K,
+                        int32_t group_size, int32_t qtype, int32_t dtype, const void *bias, void *C, int64_t ldc,
+                        int32_t path, int32_t skinny_max_m, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

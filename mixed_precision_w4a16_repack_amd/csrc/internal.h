@@ -1,0 +1,70 @@
+// internal.h -- host-side plumbing shared by the C-ABI and the kernel files
+// of libw4a16.so (not installed, not part of the ABI).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace w4a16 {
+
+// Geometry of one packed weight (see the layout in include/w4a16.h).
+struct Geometry {
+    int64_t N = 0, K = 0;
+    int32_t Ge = 0;       // effective group size
+    int64_t Kg = 0;       // groups per row
+    int32_t gshift = 0;   // log2(Ge) when Kg > 1 (Ge is then a power of two)
+    int32_t qtype = 0;    // 0 uint4b8, 1 uint4
+    size_t codes_bytes = 0, scales_off = 0, zeros_off = 0, total_bytes = 0;
+};
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Split-K skinny launch plan (M <= 16 rows per launch).
+struct SkinnyPlan {
+    int WN = 4;      // n-tiles per workgroup (one per wave column)
+    int WK = 1;      // k-slices per workgroup (waves splitting K inside it)
+    int KT = 4;      // k-tiles (128 k) per wave
+    int ksplit = 1;  // workgroups splitting K (reduced through the workspace)
+    int64_t n_groups = 0;
+    size_t partial_bytes = 0;  // fp32 partial sums in the workspace
+    size_t counter_bytes = 0;  // arrival counters in the workspace
+};
+
+// Tiled MFMA launch plan.
+struct MfmaPlan {
+    int BM = 256;  // rows per workgroup
+    int BN = 256;  // columns per workgroup
+};
+
+// Raises a kernel's dynamic-LDS limit (needed above 64 KB); cached per kernel
+// (the template parameter is the kernel itself, so each has its own cache).
+template <auto Kernel>
+inline hipError_t allow_lds(size_t bytes) {
+    static size_t granted = 64 * 1024;
+    if (bytes <= granted) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) granted = bytes;
+    return e;
+}
+
+constexpr size_t kCounterRegionBytes = 64 * 1024;  // 16384 u32 arrival counters
+
+SkinnyPlan plan_skinny(int64_t M, const Geometry& g);
+MfmaPlan plan_mfma(int64_t M, const Geometry& g);
+
+// Launchers; each returns hipSuccess or the launch error. Shapes are already
+// validated by the caller.
+hipError_t launch_repack(const int32_t* wq, const uint16_t* ws, const int32_t* wzp, const Geometry& g, void* packed,
+                         hipStream_t stream);
+hipError_t launch_unpack(const void* packed, const Geometry& g, uint8_t* codes, uint16_t* scale_bits, uint8_t* zeros,
+                         hipStream_t stream);
+hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* packed, const Geometry& g, int dtype,
+                         const void* bias, void* C, int64_t ldc, const SkinnyPlan& p, void* workspace,
+                         hipStream_t stream);
+hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed, const Geometry& g, int dtype,
+                       const void* bias, void* C, int64_t ldc, const MfmaPlan& p, hipStream_t stream);
+
+}  // namespace w4a16

@@ -1,0 +1,238 @@
+// w4a16_api.cpp -- the C ABI of libw4a16.so (declared in include/w4a16.h):
+// argument validation, geometry of the packed buffer, the dispatch on M and
+// error reporting. No kernel code lives here.
+//
+// Validation follows the eligibility rules and launcher asserts of the pages
+// (`can_implement` on the "rdna_hybrid_w4a16" pages and the MI300
+// "triton_w4a16.py" page: supported quant types, fp16/bf16 activations,
+// group sizes {-1, 32, 64, 128, 256}, K % group_size; the launcher asserts of
+// `triton_w4a16_skinny_fmt_gemm`: unit column stride, N % 8 with zero points),
+// plus the N % 16 and K % 128 alignment the gfx950 layout needs. Every message
+// names the rule that failed.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+#include "w4a16.h"
+
+namespace w4a16 {
+namespace {
+
+thread_local char g_err[512] = "";
+
+w4a16_status fail(w4a16_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+w4a16_status hip_fail(const char* what, hipError_t e) {
+    return fail(W4A16_ERR_HIP, "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int64_t x) {
+    int l = 0;
+    while ((int64_t(1) << l) < x) ++l;
+    return l;
+}
+
+// Shape and type rules shared by every call that takes a weight.
+w4a16_status make_geometry(int64_t N, int64_t K, int32_t group_size, int32_t qtype, Geometry* g) {
+    if (N <= 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "N=%lld and K=%lld must be positive", (long long)N, (long long)K);
+    if (qtype != W4A16_UINT4B8 && qtype != W4A16_UINT4)
+        return fail(W4A16_ERR_INVALID_ARG, "qtype=%d is not a w4a16_qtype (0 uint4b8, 1 uint4)", qtype);
+    if (N % 16 != 0) return fail(W4A16_ERR_UNSUPPORTED, "N=%lld must be divisible by 16", (long long)N);
+    if (K % 128 != 0) return fail(W4A16_ERR_UNSUPPORTED, "K=%lld must be divisible by 128", (long long)K);
+    const int64_t Ge = group_size == -1 ? K : group_size;
+    const bool listed = group_size == -1 || group_size == 32 || group_size == 64 || group_size == 128 ||
+                        group_size == 256 || (int64_t)group_size == K;
+    if (!listed)
+        return fail(W4A16_ERR_UNSUPPORTED, "group_size=%d not supported; supported: -1, 32, 64, 128, 256 or K=%lld",
+                    group_size, (long long)K);
+    if (K % Ge != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "K=%lld must be divisible by group_size=%d", (long long)K, group_size);
+    g->N = N;
+    g->K = K;
+    g->Ge = (int32_t)Ge;
+    g->Kg = K / Ge;
+    if (g->Kg > 1 && !is_pow2(Ge))
+        return fail(W4A16_ERR_UNSUPPORTED, "group_size=%d must be a power of two when K/group_size > 1", group_size);
+    g->gshift = g->Kg > 1 ? ilog2(Ge) : 0;
+    g->qtype = qtype;
+    g->codes_bytes = (size_t)N * (size_t)K / 2;
+    g->scales_off = align256(g->codes_bytes);
+    size_t end = g->scales_off + (size_t)N * (size_t)g->Kg * 2;
+    if (qtype == W4A16_UINT4) {
+        g->zeros_off = align256(end);
+        end = g->zeros_off + (size_t)N * (size_t)g->Kg;
+    } else {
+        g->zeros_off = 0;
+    }
+    g->total_bytes = align256(end);
+    return W4A16_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t resolve_path(int64_t M, int32_t path, int32_t skinny_max_m) {
+    const int64_t t = skinny_max_m <= 0 ? 16 : skinny_max_m;
+    if (path == W4A16_PATH_SKINNY || path == W4A16_PATH_MFMA) return path;
+    return M <= t ? W4A16_PATH_SKINNY : W4A16_PATH_MFMA;
+}
+
+size_t skinny_workspace(const SkinnyPlan& p) {
+    return p.ksplit > 1 ? kCounterRegionBytes + p.partial_bytes : 0;
+}
+
+}  // namespace
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+int32_t w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_last_error(void) { return g_err; }
+
+size_t w4a16_workspace_counter_bytes(void) { return kCounterRegionBytes; }
+
+w4a16_status w4a16_packed_size(int64_t N, int64_t K, int32_t group_size, int32_t qtype, size_t* out_bytes) {
+    clear_error();
+    if (out_bytes == nullptr) return fail(W4A16_ERR_INVALID_ARG, "out_bytes is NULL");
+    Geometry g;
+    w4a16_status st = make_geometry(N, K, group_size, qtype, &g);
+    if (st != W4A16_OK) return st;
+    *out_bytes = g.total_bytes;
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_repack(const int32_t* weight_packed, const void* weight_scale, const int32_t* weight_zero_point,
+                          int64_t N, int64_t K, int32_t group_size, int32_t qtype, void* packed, size_t packed_bytes,
+                          hipStream_t stream) {
+    clear_error();
+    Geometry g;
+    w4a16_status st = make_geometry(N, K, group_size, qtype, &g);
+    if (st != W4A16_OK) return st;
+    if (weight_packed == nullptr) return fail(W4A16_ERR_INVALID_ARG, "weight_packed is NULL");
+    if (weight_scale == nullptr) return fail(W4A16_ERR_INVALID_ARG, "weight_scale is NULL");
+    if (packed == nullptr) return fail(W4A16_ERR_INVALID_ARG, "packed is NULL");
+    if ((reinterpret_cast<uintptr_t>(weight_packed) & 3u) || (reinterpret_cast<uintptr_t>(weight_scale) & 1u) ||
+        (reinterpret_cast<uintptr_t>(weight_zero_point) & 3u))
+        return fail(W4A16_ERR_INVALID_ARG, "checkpoint tensors must be aligned to their element size");
+    if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
+    if (packed_bytes < g.total_bytes)
+        return fail(W4A16_ERR_SIZE, "packed_bytes=%zu is smaller than the %zu bytes the layout needs", packed_bytes,
+                    g.total_bytes);
+    hipError_t e = launch_repack(weight_packed, static_cast<const uint16_t*>(weight_scale),
+                                 qtype == W4A16_UINT4 ? weight_zero_point : nullptr, g, packed, stream);
+    if (e != hipSuccess) return hip_fail("repack launch", e);
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_unpack(const void* packed, int64_t N, int64_t K, int32_t group_size, int32_t qtype,
+                          uint8_t* codes, uint16_t* scale_bits, uint8_t* zeros, hipStream_t stream) {
+    clear_error();
+    Geometry g;
+    w4a16_status st = make_geometry(N, K, group_size, qtype, &g);
+    if (st != W4A16_OK) return st;
+    if (packed == nullptr) return fail(W4A16_ERR_INVALID_ARG, "packed is NULL");
+    if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
+    if (reinterpret_cast<uintptr_t>(scale_bits) & 1u) return fail(W4A16_ERR_INVALID_ARG, "scale_bits must be 2-byte aligned");
+    hipError_t e = launch_unpack(packed, g, codes, scale_bits, zeros, stream);
+    if (e != hipSuccess) return hip_fail("unpack launch", e);
+    return W4A16_OK;
+}
+
+int32_t w4a16_select_path(int64_t M, int32_t path, int32_t skinny_max_m) {
+    clear_error();
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_MFMA)
+        return fail(W4A16_ERR_INVALID_ARG, "path=%d is not a w4a16_path (0 auto, 1 skinny, 2 mfma)", path);
+    return resolve_path(M, path, skinny_max_m);
+}
+
+w4a16_status w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t path,
+                                  int32_t skinny_max_m, size_t* out_bytes) {
+    clear_error();
+    if (out_bytes == nullptr) return fail(W4A16_ERR_INVALID_ARG, "out_bytes is NULL");
+    if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M=%lld must be >= 0", (long long)M);
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_MFMA)
+        return fail(W4A16_ERR_INVALID_ARG, "path=%d is not a w4a16_path (0 auto, 1 skinny, 2 mfma)", path);
+    Geometry g;
+    // The workspace does not depend on qtype; uint4b8 has the simpler rules.
+    w4a16_status st = make_geometry(N, K, group_size, W4A16_UINT4B8, &g);
+    if (st != W4A16_OK) return st;
+    *out_bytes = 0;
+    if (M > 0 && resolve_path(M, path, skinny_max_m) == W4A16_PATH_SKINNY) {
+        const SkinnyPlan p = plan_skinny(M < 16 ? M : 16, g);
+        if (p.n_groups * (int64_t)sizeof(uint32_t) > (int64_t)kCounterRegionBytes)
+            return fail(W4A16_ERR_UNSUPPORTED, "N=%lld needs more split-K counters than the workspace holds",
+                        (long long)N);
+        *out_bytes = skinny_workspace(p);
+    }
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packed, int64_t N, int64_t K,
+                        int32_t group_size, int32_t qtype, int32_t dtype, const void* bias, void* C, int64_t ldc,
+                        int32_t path, int32_t skinny_max_m, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    clear_error();
+    Geometry g;
+    w4a16_status st = make_geometry(N, K, group_size, qtype, &g);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+        return fail(W4A16_ERR_INVALID_ARG, "dtype=%d is not a w4a16_dtype (0 fp16, 1 bf16)", dtype);
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_MFMA)
+        return fail(W4A16_ERR_INVALID_ARG, "path=%d is not a w4a16_path (0 auto, 1 skinny, 2 mfma)", path);
+    if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M=%lld must be >= 0", (long long)M);
+    if (M == 0) return W4A16_OK;
+    if (A == nullptr || packed == nullptr || C == nullptr)
+        return fail(W4A16_ERR_INVALID_ARG, "A, packed and C must not be NULL");
+    if (lda < K) return fail(W4A16_ERR_INVALID_ARG, "lda=%lld must be >= K=%lld", (long long)lda, (long long)K);
+    if (ldc < N) return fail(W4A16_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc, (long long)N);
+    if (!aligned16(A) || lda % 8 != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "A must be 16-byte aligned with lda %% 8 == 0 (lda=%lld)", (long long)lda);
+    if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(C) & 1u) || (reinterpret_cast<uintptr_t>(bias) & 1u))
+        return fail(W4A16_ERR_INVALID_ARG, "C and bias must be 2-byte aligned");
+
+    const int32_t which = resolve_path(M, path, skinny_max_m);
+    if (which == W4A16_PATH_MFMA) {
+        const MfmaPlan p = plan_mfma(M, g);
+        hipError_t e = launch_mfma(A, M, lda, packed, g, dtype, bias, C, ldc, p, stream);
+        if (e != hipSuccess) return hip_fail("mfma kernel launch", e);
+        return W4A16_OK;
+    }
+
+    const SkinnyPlan p = plan_skinny(M < 16 ? M : 16, g);
+    if (p.n_groups * (int64_t)sizeof(uint32_t) > (int64_t)kCounterRegionBytes)
+        return fail(W4A16_ERR_UNSUPPORTED, "N=%lld needs more split-K counters than the workspace holds", (long long)N);
+    const size_t need = skinny_workspace(p);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(W4A16_ERR_SIZE, "workspace of %zu bytes is smaller than the %zu bytes this call needs",
+                        workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(W4A16_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    }
+    // M > 16 on the forced skinny path: 16-row slices, one launch each.
+    const uint16_t* a16 = static_cast<const uint16_t*>(A);
+    uint16_t* c16 = static_cast<uint16_t*>(C);
+    for (int64_t m0 = 0; m0 < M; m0 += 16) {
+        const int64_t mm = M - m0 < 16 ? M - m0 : 16;
+        hipError_t e = launch_skinny(a16 + m0 * lda, mm, lda, packed, g, dtype, bias, c16 + m0 * ldc, ldc, p,
+                                     need > 0 ? workspace : nullptr, stream);
+        if (e != hipSuccess) return hip_fail("skinny kernel launch", e);
+    }
+    return W4A16_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+"""C-ABI boundary checks that need no GPU (CPU only).
+
+The library must load, export every function include/w4a16.h declares, and
+reject invalid arguments with the documented status and message before any
+HIP call (so these calls are safe on a host without a GPU).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_precision_w4a16_repack_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+OK, INVALID, UNSUPPORTED, SIZE = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4.LIB_PATH):
+        from mixed_precision_w4a16_repack_amd import build
+
+        build.build()
+    return w4.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_signatures():
+    assert set(_declared_functions()) == set(w4.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(w4.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_abi_version(lib):
+    assert w4.abi_version() == 1
+
+
+def test_packed_size_values(lib):
+    # codes N*K/2, scales N*Kg*2 at align256, zeros N*Kg at align256
+    assert w4.packed_size(16, 128, 128, w4.UINT4B8) == 1280
+    assert w4.packed_size(16, 128, -1, w4.UINT4) == 1536
+    assert w4.packed_size(4096, 4096, 128, w4.UINT4B8) == 4096 * 2048 + 4096 * 32 * 2
+    assert w4.packed_size(6144, 4096, 32, w4.UINT4) == 6144 * 2048 + 6144 * 128 * 3
+    # G = K behaves like G = -1
+    assert w4.packed_size(4096, 14336, 14336, w4.UINT4) == w4.packed_size(4096, 14336, -1, w4.UINT4)
+
+
+@pytest.mark.parametrize(
+    "N,K,G,qtype,status,needle",
+    [
+        (4100, 4096, 128, 0, UNSUPPORTED, "N=4100 must be divisible by 16"),
+        (4096, 4100, 128, 0, UNSUPPORTED, "K=4100 must be divisible by 128"),
+        (4096, 4096, 96, 0, UNSUPPORTED, "group_size=96 not supported"),
+        (4096, 4096, 16, 0, UNSUPPORTED, "group_size=16 not supported"),
+        (4096, 384, 256, 0, UNSUPPORTED, "K=384 must be divisible by group_size=256"),
+        (4096, 4096, 128, 3, INVALID, "qtype=3"),
+        (0, 4096, 128, 0, INVALID, "must be positive"),
+        (4096, -128, 128, 0, INVALID, "must be positive"),
+    ],
+)
+def test_packed_size_rejects(lib, N, K, G, qtype, status, needle):
+    out = ctypes.c_size_t(0)
+    st = lib.w4a16_packed_size(N, K, G, qtype, ctypes.byref(out))
+    assert st == status
+    assert needle in w4.last_error()
+
+
+def test_null_out_pointer(lib):
+    assert lib.w4a16_packed_size(16, 128, 128, 0, None) == INVALID
+    assert "out_bytes is NULL" in w4.last_error()
+
+
+def _gemm(lib, **kw):
+    args = dict(A=ctypes.c_void_p(4096), M=4, lda=4096, packed=ctypes.c_void_p(4096), N=4096, K=4096, G=128,
+                qtype=0, dtype=0, bias=None, C=ctypes.c_void_p(4096), ldc=4096, path=0, smax=0, ws=None, wsb=0)
+    args.update(kw)
+    return lib.w4a16_gemm(args["A"], args["M"], args["lda"], args["packed"], args["N"], args["K"], args["G"],
+                          args["qtype"], args["dtype"], args["bias"], args["C"], args["ldc"], args["path"],
+                          args["smax"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,needle",
+    [
+        (dict(dtype=2), INVALID, "dtype=2"),
+        (dict(path=5), INVALID, "path=5"),
+        (dict(M=-1), INVALID, "M=-1"),
+        (dict(A=None), INVALID, "must not be NULL"),
+        (dict(C=None), INVALID, "must not be NULL"),
+        (dict(lda=4000), INVALID, "lda=4000 must be >= K=4096"),
+        (dict(ldc=100), INVALID, "ldc=100 must be >= N=4096"),
+        (dict(lda=4100), UNSUPPORTED, "lda % 8 == 0"),
+        (dict(A=ctypes.c_void_p(4104)), UNSUPPORTED, "16-byte aligned"),
+        (dict(packed=ctypes.c_void_p(4100)), INVALID, "256-byte aligned"),
+        (dict(K=4000, lda=4000), UNSUPPORTED, "K=4000 must be divisible by 128"),
+        # the skinny path of this shape splits K and needs a workspace
+        (dict(M=1), SIZE, "workspace of 0 bytes is smaller"),
+        (dict(M=1, ws=ctypes.c_void_p(4096), wsb=16), SIZE, "workspace of 16 bytes is smaller"),
+    ],
+)
+def test_gemm_rejects_before_any_hip_call(lib, kw, status, needle):
+    assert _gemm(lib, **kw) == status
+    assert needle in w4.last_error()
+
+
+def test_gemm_m_zero_is_a_noop(lib):
+    # Pointers are never dereferenced for M == 0.
+    assert _gemm(lib, M=0) == OK
+    assert w4.last_error() == ""
+
+
+def test_repack_rejects(lib):
+    p = ctypes.c_void_p(4096)
+    assert lib.w4a16_repack(None, p, None, 16, 128, 128, 0, p, 1 << 20, None) == INVALID
+    assert "weight_packed is NULL" in w4.last_error()
+    assert lib.w4a16_repack(p, p, None, 16, 128, 128, 0, p, 1000, None) == SIZE
+    assert "packed_bytes=1000" in w4.last_error()
+    assert lib.w4a16_repack(p, p, None, 16, 128, 128, 0, ctypes.c_void_p(4160), 1 << 20, None) == INVALID
+    assert "256-byte aligned" in w4.last_error()
+
+
+def test_select_path(lib):
+    assert w4.select_path(1) == w4.PATH_SKINNY
+    assert w4.select_path(16) == w4.PATH_SKINNY
+    assert w4.select_path(17) == w4.PATH_MFMA
+    assert w4.select_path(32, skinny_max_m=32) == w4.PATH_SKINNY
+    assert w4.select_path(1, path=w4.PATH_MFMA) == w4.PATH_MFMA
+    assert w4.select_path(4096, path=w4.PATH_SKINNY) == w4.PATH_SKINNY
+    with pytest.raises(RuntimeError, match="path=9"):
+        w4.select_path(1, path=9)
+
+
+def test_workspace_size(lib):
+    assert w4.workspace_size(256, 4096, 4096, 128) == 0  # tiled path needs none
+    ws = w4.workspace_size(16, 4096, 4096, 128)
+    assert ws > w4.workspace_counter_bytes()
+    # sized for 16 rows, so every M <= 16 fits the same workspace
+    assert w4.workspace_size(1, 4096, 4096, 128) == ws
+    assert w4.workspace_size(300, 4096, 4096, 128, path=w4.PATH_SKINNY) == ws
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(w4, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        w4.load_library(str(tmp_path / "libw4a16.so"))

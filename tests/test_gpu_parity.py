@@ -1,0 +1,269 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+* repack / unpack: bit-exact against the oracle's layout encoder and unpack;
+* dequantisation: identity activations make C equal RN_act((q - z) * s)
+  bit for bit on both kernels;
+* GEMM: max|C - C_ref| / max|C_ref| within 2e-3 (fp16) / 1e-2 (bf16) on every
+  workload shape at full size (all rows for M <= 64, sampled rows above), on
+  the forced skinny and MFMA kernels and on the dispatcher;
+* edge cases: M = 0, ragged M and N tails, strided A and C, bias, minimal K,
+  G = -1 vs G = K, uint4 without zero points, determinism, workspace reuse.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_w4a16_repack_amd as w4
+import oracle
+import w4a16_inputs as wi
+from tests.gpu_cases import DEV, expected_codes_scales_zeros, oracle_ref, rel_err_rows, repack, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+UINT4B8, UINT4 = wi.UINT4B8, wi.UINT4
+SKINNY, MFMA, AUTO = w4.PATH_SKINNY, w4.PATH_MFMA, w4.PATH_AUTO
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    w4.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _case(cfg, M, N, K, G, qtype, dtype, **kw):
+    return wi.make_case(cfg, M, N, K, G, qtype, dtype, **kw)
+
+
+# ------------------------------------------------------------------ repack
+
+
+REPACK_SHAPES = [
+    # (N, K, G, qtype, with_zero_point)
+    (16, 128, 128, UINT4B8, False),
+    (16, 128, -1, UINT4, True),
+    (48, 384, 32, UINT4, True),
+    (32, 256, 64, UINT4, False),  # uint4 without zero points: zeros are 0
+    (256, 512, 128, UINT4B8, False),
+    (4096, 4096, 128, UINT4B8, False),
+    (6144, 4096, 32, UINT4, True),
+    (14336, 4096, 64, UINT4B8, False),
+    (4096, 14336, 256, UINT4, True),
+    (14336, 4096, -1, UINT4, True),
+]
+
+
+@pytest.mark.parametrize("N,K,G,qtype,zp", REPACK_SHAPES, ids=[f"{s[0]}x{s[1]}g{s[2]}q{s[3]}z{int(s[4])}" for s in REPACK_SHAPES])
+def test_repack_bit_exact(N, K, G, qtype, zp):
+    case = _case(11, 1, N, K, G, qtype, "bf16" if qtype == UINT4 else "f16", with_zero_point=zp)
+    packed = repack(case)
+    codes, scales, zeros = expected_codes_scales_zeros(case)
+    expect = oracle.encode_device(codes, scales, zeros, qtype, G)
+    got = packed.cpu().numpy()
+    assert got.shape == expect.shape
+    mism = np.flatnonzero(got != expect)
+    assert mism.size == 0, f"{mism.size} bytes differ, first at {mism[:8]}"
+    # and the inverse
+    c2, s2, z2 = w4.unpack(packed, N, K, G, qtype)
+    np.testing.assert_array_equal(c2.cpu().numpy(), codes)
+    np.testing.assert_array_equal(s2.cpu().numpy(), scales.view(torch.int16).numpy())
+    if qtype == UINT4:
+        np.testing.assert_array_equal(z2.cpu().numpy(), zeros)
+
+
+def test_repack_is_deterministic_and_ignores_prior_contents():
+    case = _case(12, 1, 64, 512, 64, UINT4, "f16")
+    wq, ws, zp, _, _ = to_dev(case)
+    a = w4.repack(wq, ws, zp, 64, UINT4)
+    b = torch.full_like(a, 0xA5)
+    w4.repack(wq, ws, zp, 64, UINT4, out=b)
+    assert torch.equal(a, b)
+
+
+def test_repack_symmetric_ignores_zero_points():
+    case = _case(13, 1, 64, 256, 32, UINT4, "f16")
+    wq, ws, zp, _, _ = to_dev(case)
+    assert torch.equal(w4.repack(wq, ws, zp, 32, UINT4B8), w4.repack(wq, ws, None, 32, UINT4B8))
+
+
+# ------------------------------------------------------------------ dequant
+
+
+IDENTITY = [
+    # (N, K, G, qtype, dtype, path)
+    (48, 128, 32, UINT4, "f16", SKINNY),
+    (64, 256, 128, UINT4B8, "bf16", SKINNY),
+    (32, 256, -1, UINT4, "bf16", SKINNY),
+    (48, 128, 32, UINT4, "bf16", MFMA),
+    (272, 256, 64, UINT4B8, "f16", MFMA),
+    (64, 256, -1, UINT4, "f16", MFMA),
+]
+
+
+@pytest.mark.parametrize("N,K,G,qtype,dtype,path", IDENTITY)
+def test_identity_activations_give_rounded_weights(N, K, G, qtype, dtype, path):
+    # A = I_K: C[m, n] = (q - z) * s rounded once to the act dtype, whether a
+    # kernel scales before or after the products (the product is exact in fp32).
+    case = _case(14, 1, N, K, G, qtype, dtype)
+    packed = repack(case)
+    A = torch.eye(K, dtype=case.torch_dtype, device=DEV)
+    C = w4.gemm(A, packed, N, K, G, qtype, path=path)
+    W = oracle.dequant(case.weight_packed, case.weight_scale, case.weight_zero_point, qtype, G)
+    expect = torch.from_numpy(W.T.copy()).to(case.torch_dtype)
+    got = C.cpu()
+    bad = (got.view(torch.int16) != expect.view(torch.int16)).sum().item()
+    assert bad == 0, f"{bad} of {got.numel()} values differ from RN((q - z) * s)"
+
+
+# ------------------------------------------------------------------ GEMM parity
+
+
+def _workload_cases():
+    out = []
+    for name in ("tiny", "decode_sym", "decode_asym", "crossover"):
+        wl = wi.WORKLOADS[name]
+        for (M, N, K) in wl["shapes"]:
+            paths = [AUTO] if name != "crossover" else [SKINNY, MFMA]
+            for p in paths:
+                out.append((name, wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], wl["sigma"], p))
+    wl = wi.WORKLOADS["prefill"]
+    for (G, qt) in wl["variants"]:
+        for (M, N, K) in wl["shapes"]:
+            out.append(("prefill", wl["cfg_id"], M, N, K, G, qt, wl["dtype"], wl["sigma"], AUTO))
+    return out
+
+
+WORKLOAD_CASES = _workload_cases()
+
+
+@pytest.mark.parametrize(
+    "name,cfg,M,N,K,G,qtype,dtype,sigma,path", WORKLOAD_CASES,
+    ids=[f"{c[0]}-M{c[2]}-N{c[3]}-K{c[4]}-G{c[5]}-q{c[6]}-p{c[9]}" for c in WORKLOAD_CASES],
+)
+def test_workload_parity(name, cfg, M, N, K, G, qtype, dtype, sigma, path):
+    case = _case(cfg, M, N, K, G, qtype, dtype, sigma=sigma)
+    print(f"[case] {name} M={M} N={N} K={K} G={G} qtype={qtype} {dtype} path={path}", flush=True)
+    packed = repack(case)
+    A = case.A.to(DEV)
+    C = w4.gemm(A, packed, N, K, G, qtype, path=path)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    ref = oracle_ref(case, rows=rows)
+    err = rel_err_rows(C, ref, rows)
+    tol = oracle.TOLERANCE[dtype]
+    assert err <= tol, f"rel err {err:.3e} > {tol}"
+    if path == AUTO:
+        forced = SKINNY if M <= 16 else MFMA
+        C2 = w4.gemm(A, packed, N, K, G, qtype, path=forced)
+        assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "dispatcher picked another kernel"
+
+
+# ------------------------------------------------------------------ edges
+
+
+@pytest.mark.parametrize("path", [SKINNY, MFMA])
+@pytest.mark.parametrize("qtype,dtype", [(UINT4B8, "f16"), (UINT4, "bf16")])
+def test_bias_strides_and_ragged_tails(path, qtype, dtype):
+    # N = 400 is not a multiple of any tile width; M ragged for both kernels.
+    M = 11 if path == SKINNY else 300
+    N, K, G = 400, 640, 64
+    case = _case(15, M, N, K, G, qtype, dtype, with_bias=True)
+    packed = repack(case)
+    A_big = torch.zeros((M, K + 64), dtype=case.torch_dtype, device=DEV)
+    A_big[:, :K] = case.A.to(DEV)
+    A = A_big[:, :K]  # lda = K + 64
+    C_big = torch.full((M, N + 48), 7.0, dtype=case.torch_dtype, device=DEV)
+    C = C_big[:, :N]  # ldc = N + 48
+    w4.gemm(A, packed, N, K, G, qtype, bias=case.bias.to(DEV), out=C, path=path)
+    ref = oracle_ref(case)
+    assert oracle.rel_err(C.cpu(), ref) <= oracle.TOLERANCE[dtype]
+    assert torch.all(C_big[:, N:] == 7.0), "wrote outside [M, N]"
+
+
+@pytest.mark.parametrize("path", [SKINNY, MFMA])
+def test_zero_weights_give_bias_exactly(path):
+    # All codes equal to the zero point: C = bias exactly (one rounding of bias).
+    M, N, K, G = 24, 64, 256, 32
+    rng = np.random.default_rng(16)
+    z = rng.integers(0, 16, size=(N, K // G))
+    words = oracle.pack_codes(np.repeat(z, G, axis=1))
+    zp = oracle.pack_zeros(z)
+    scales = torch.from_numpy(rng.uniform(0.005, 0.02, size=(N, K // G))).to(torch.float16)
+    bias = torch.from_numpy(rng.normal(0, 1, size=(N,))).to(torch.float16)
+    A = torch.from_numpy(rng.normal(0, 1, size=(M, K))).to(torch.float16)
+    packed = w4.repack(torch.from_numpy(words).to(DEV), scales.to(DEV), torch.from_numpy(zp).to(DEV), G, UINT4)
+    C = w4.gemm(A.to(DEV), packed, N, K, G, UINT4, bias=bias.to(DEV), path=path)
+    assert torch.equal(C.cpu(), bias.expand(M, N))
+    C0 = w4.gemm(A.to(DEV), packed, N, K, G, UINT4, path=path)
+    assert torch.all(C0 == 0)
+
+
+@pytest.mark.parametrize("path", [SKINNY, MFMA])
+def test_every_small_m(path):
+    N, K, G = 256, 1024, 128
+    case = _case(17, 16, N, K, G, UINT4B8, "f16")
+    packed = repack(case)
+    ref = oracle_ref(case)
+    A = case.A.to(DEV)
+    for M in range(1, 17):
+        C = w4.gemm(A[:M], packed, N, K, G, UINT4B8, path=path)
+        err = oracle.rel_err(C.cpu(), ref[:M])
+        assert err <= oracle.TOLERANCE["f16"], f"M={M}: {err}"
+
+
+def test_forced_skinny_slices_large_m():
+    N, K, G = 512, 512, 64
+    case = _case(18, 40, N, K, G, UINT4, "bf16")
+    packed = repack(case)
+    C = w4.gemm(case.A.to(DEV), packed, N, K, G, UINT4, path=SKINNY)
+    assert oracle.rel_err(C.cpu(), oracle_ref(case)) <= oracle.TOLERANCE["bf16"]
+
+
+@pytest.mark.parametrize("path", [SKINNY, MFMA])
+def test_group_minus_one_equals_group_k(path):
+    N, K = 128, 512
+    case = _case(19, 8 if path == SKINNY else 64, N, K, -1, UINT4, "f16")
+    wq, ws, zp, A, _ = to_dev(case)
+    p1 = w4.repack(wq, ws, zp, -1, UINT4)
+    p2 = w4.repack(wq, ws, zp, K, UINT4)
+    assert torch.equal(p1, p2)
+    C1 = w4.gemm(A, p1, N, K, -1, UINT4, path=path)
+    C2 = w4.gemm(A, p2, N, K, K, UINT4, path=path)
+    assert torch.equal(C1, C2)
+    assert oracle.rel_err(C1.cpu(), oracle_ref(case)) <= oracle.TOLERANCE["f16"]
+
+
+@pytest.mark.parametrize("path", [SKINNY, MFMA])
+def test_uint4_without_zero_points(path):
+    N, K, G = 64, 256, 64
+    case = _case(20, 4 if path == SKINNY else 40, N, K, G, UINT4, "bf16", with_zero_point=False)
+    packed = repack(case)
+    C = w4.gemm(case.A.to(DEV), packed, N, K, G, UINT4, path=path)
+    assert oracle.rel_err(C.cpu(), oracle_ref(case)) <= oracle.TOLERANCE["bf16"]
+
+
+def test_m_zero_is_a_noop():
+    case = _case(21, 1, 64, 256, 64, UINT4B8, "f16")
+    packed = repack(case)
+    A = torch.empty((0, 256), dtype=torch.float16, device=DEV)
+    C = w4.gemm(A, packed, 64, 256, 64, UINT4B8)
+    assert C.shape == (0, 64)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (1, 14336, 4096), (256, 4096, 14336)])
+def test_deterministic_and_workspace_returns_to_zero(M, N, K):
+    case = _case(22, M, N, K, 128, UINT4B8, "f16")
+    packed = repack(case)
+    A = case.A.to(DEV)
+    ws = w4.Workspace(DEV)
+    C1 = w4.gemm(A, packed, N, K, 128, UINT4B8, workspace=ws)
+    C2 = w4.gemm(A, packed, N, K, 128, UINT4B8, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    if ws.buf is not None:
+        nctr = w4.workspace_counter_bytes()
+        assert torch.all(ws.buf[:nctr] == 0)
