@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""W4A16 GEMM benchmark on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+
+A step is one pass of the decode workload through the C ABI: the symmetric
+uint4b8 fp16 GEMMs with G = 128 for M in {1, 4, 8, 16} and (N, K) in
+{(4096, 4096), (14336, 4096), (4096, 14336)}: twelve GEMMs, each dispatched on
+M to the skinny kernel. Inputs are synthetic (seeded, w4a16_inputs) and
+already repacked in HBM before timing (the repack is a one-time load step,
+timed separately). Every launch reads a different copy of its weights from a
+rotation pool larger than 1 GB, so neither L2 nor the 256 MB MALL can serve
+them. Steps are captured into HIP graphs (one per weight-copy set) and
+replayed; W untimed steps, then K timed steps between a device
+synchronisation and HIP events on the launch stream.
+
+Prints one JSON line: value = weight-stream GB/s of the whole step
+(codes + scales [+ zeros] bytes per GEMM, summed, over the step time), the
+roofline of the skinny kernel (algorithmic bytes incl. activations and
+output per launch over its average duration, against 8 TB/s), the oracle's
+CPU rate on a bounded sample, and extras: per-shape decode rates, the
+skinny-vs-MFMA crossover and the prefill TFLOP/s of the MFMA kernel.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import mixed_precision_w4a16_repack_amd as w4  # noqa: E402
+import w4a16_inputs as wi  # noqa: E402
+
+METRIC = "W4A16 GEMM: weight-stream GB/s (M<=16) and TFLOP/s (M>=2048) vs peak, 1 GPU"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2516.6  # dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+DEV = "cuda:0"
+ROTATE_BYTES = 1 << 30
+
+
+def weight_stream_bytes(N, K, G, qtype, with_zero_point):
+    """Checkpoint bytes of one weight: codes + scales (+ packed zero points)."""
+    Kg = K // wi.effective_group(K, G)
+    b = N * K // 2 + N * Kg * 2
+    if qtype == wi.UINT4 and with_zero_point:
+        b += (N // 8) * Kg * 4
+    return b
+
+
+def algorithmic_bytes(M, N, K, G, qtype, with_zero_point):
+    """Weight stream + activations read + output written (2-byte act)."""
+    return weight_stream_bytes(N, K, G, qtype, with_zero_point) + M * K * 2 + M * N * 2
+
+
+class Gemm:
+    """One GEMM configuration with a rotation pool of packed weight copies."""
+
+    def __init__(self, cfg_id, M, N, K, G, qtype, dtype, sigma, copies, path=w4.PATH_AUTO):
+        case = wi.make_case(cfg_id, M, N, K, G, qtype, dtype, sigma=sigma)
+        self.M, self.N, self.K, self.G, self.qtype, self.dtype = M, N, K, G, qtype, dtype
+        self.path = path
+        self.zp = case.weight_zero_point is not None
+        wq = torch.from_numpy(case.weight_packed).to(DEV)
+        ws = case.weight_scale.to(DEV)
+        zp = None if case.weight_zero_point is None else torch.from_numpy(case.weight_zero_point).to(DEV)
+        first = w4.repack(wq, ws, zp, G, qtype)
+        self.packed = [first] + [first.clone() for _ in range(copies - 1)]
+        self.A = case.A.to(DEV)
+        self.C = torch.empty((M, N), dtype=case.torch_dtype, device=DEV)
+        self.ws = w4.Workspace(DEV)
+        self.ws.get(w4.workspace_size(M, N, K, G, path))
+        self._repack_args = (wq, ws, zp)
+
+    def launch(self, copy: int):
+        w4.gemm(self.A, self.packed[copy % len(self.packed)], self.N, self.K, self.G, self.qtype,
+                out=self.C, path=self.path, workspace=self.ws)
+
+    @property
+    def weight_bytes(self):
+        return weight_stream_bytes(self.N, self.K, self.G, self.qtype, self.zp)
+
+    @property
+    def algo_bytes(self):
+        return algorithmic_bytes(self.M, self.N, self.K, self.G, self.qtype, self.zp)
+
+    @property
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def time_repack(self, reps=5):
+        wq, ws, zp = self._repack_args
+        out = torch.empty_like(self.packed[0])
+        w4.repack(wq, ws, zp, self.G, self.qtype, out=out)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            w4.repack(wq, ws, zp, self.G, self.qtype, out=out)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e3  # us
+
+
+def capture_graphs(launch_fns_per_graph):
+    """One HIP graph per list of launch callables (warmed up eagerly first)."""
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fns in launch_fns_per_graph:
+            for f in fns:
+                f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for fns in launch_fns_per_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graphs(graphs, reps, warmup):
+    """Replays graphs round-robin; returns elapsed ms of `reps` replays."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e)
+
+
+def copies_for(total_bytes_per_round, minimum=2):
+    return max(minimum, -(-ROTATE_BYTES // max(1, total_bytes_per_round)))
+
+
+def decode_cases():
+    wl = wi.WORKLOADS["decode_sym"]
+    step_bytes = sum(weight_stream_bytes(N, K, wl["G"], wl["qtype"], False) for (_, N, K) in wl["shapes"])
+    copies = copies_for(step_bytes)
+    cases = [Gemm(wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], wl["sigma"], copies)
+             for (M, N, K) in wl["shapes"]]
+    return cases, copies
+
+
+def per_case_rate(g: Gemm, launches=None, reps=20):
+    """Average duration of one launch of g, from graphs of back-to-back
+    launches over its rotating copies."""
+    n = launches or len(g.packed)
+    graphs = capture_graphs([[(lambda c=c: g.launch(c)) for c in range(n)]])
+    ms = time_graphs(graphs, reps, 3)
+    return ms * 1e3 / (reps * n)  # us per launch
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (fp64, all host threads) on the decode workload's GEMMs,
+    repeated until about budget_s seconds of CPU work."""
+    import oracle
+
+    wl = wi.WORKLOADS["decode_sym"]
+    cases = [wi.make_case(wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], sigma=wl["sigma"])
+             for (M, N, K) in wl["shapes"]]
+    done_bytes, done_gemms, used = 0, 0, 1
+    t0 = time.perf_counter()
+    while True:
+        for c in cases:
+            _, used = oracle.gemm(c.A, c.weight_packed, c.weight_scale, None, c.qtype, c.G)
+            done_bytes += weight_stream_bytes(c.N, c.K, c.G, c.qtype, False)
+            done_gemms += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(done_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(used),
+        "kind": "oracle",
+        "sample": f"{done_gemms} decode GEMMs (the step's 12 shapes in order, fp64 C oracle, all of each output) "
+                  f"in {dt:.1f} s; weight-stream bytes / time",
+    }
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("skinny.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "mixed_precision_w4a16_repack_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM traffic per launch of the skinny kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "skinny_decode_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def extras(warmup):
+    out = {}
+    # Crossover workload: skinny (16-row slices) vs MFMA at M = 32..256.
+    wl = wi.WORKLOADS["crossover"]
+    cross = []
+    for (M, N, K) in wl["shapes"]:
+        row = {"M": M}
+        for name, path in (("skinny_us", w4.PATH_SKINNY), ("mfma_us", w4.PATH_MFMA)):
+            g = Gemm(wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], wl["sigma"],
+                     copies_for(weight_stream_bytes(N, K, wl["G"], wl["qtype"], False)), path=path)
+            row[name] = round(per_case_rate(g, reps=10), 2)
+            del g
+        row["mfma_tflops"] = round(2.0 * M * N * K / row["mfma_us"] / 1e6, 1)
+        cross.append(row)
+    out["crossover"] = {"workload": "N=14336, K=4096, G=64, uint4b8, fp16", "rows": cross,
+                        "crossover_M": next((r["M"] for r in cross if r["mfma_us"] < r["skinny_us"]), None)}
+    # Prefill workload on the MFMA kernel.
+    wl = wi.WORKLOADS["prefill"]
+    rows, tot_flop, tot_us = [], 0.0, 0.0
+    for (G, qt) in wl["variants"]:
+        for (M, N, K) in wl["shapes"]:
+            g = Gemm(wl["cfg_id"], M, N, K, G, qt, wl["dtype"], wl["sigma"], 2)
+            us = per_case_rate(g, launches=2, reps=5)
+            tf = g.flops / us / 1e6
+            rows.append({"M": M, "N": N, "K": K, "G": G, "qtype": qt, "us": round(us, 1), "tflops": round(tf, 1),
+                         "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4)})
+            tot_flop += g.flops
+            tot_us += us
+            del g
+            torch.cuda.empty_cache()
+    out["prefill"] = {
+        "workload": "M in {2048,8192} x (N,K) in {(14336,4096),(4096,14336)} x G in {-1,256} x {uint4b8, uint4+zp}, bf16",
+        "tflops": round(tot_flop / tot_us / 1e6, 1),
+        "frac_of_peak": round(tot_flop / tot_us / 1e6 / MFMA_PEAK_TFLOPS, 4),
+        "peak_tflops": MFMA_PEAK_TFLOPS,
+        "rows": rows,
+    }
+    # Decode asymmetric bf16 workload and the tiny case.
+    wl = wi.WORKLOADS["decode_asym"]
+    asym = []
+    for (M, N, K) in wl["shapes"]:
+        g = Gemm(wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], wl["sigma"],
+                 copies_for(weight_stream_bytes(N, K, wl["G"], wl["qtype"], True)))
+        us = per_case_rate(g)
+        asym.append({"M": M, "N": N, "K": K, "us": round(us, 2), "weight_GBps": round(g.weight_bytes / us / 1e3, 1)})
+    out["decode_asym"] = {"workload": "N=6144, K=4096, G=32, uint4 + zero points, bf16", "rows": asym}
+    wl = wi.WORKLOADS["tiny"]
+    (M, N, K) = wl["shapes"][0]
+    g = Gemm(wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], wl["sigma"], 4)
+    out["tiny_us"] = round(per_case_rate(g), 2)
+    # One-time repack of the largest decode weight.
+    g = Gemm(2, 1, 14336, 4096, 128, wi.UINT4B8, "f16", 1.0, 1)
+    us = g.time_repack()
+    out["repack"] = {"N": 14336, "K": 4096, "us": round(us, 1),
+                     "GBps_read_plus_write": round(2 * g.weight_bytes / us / 1e3, 1)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the W4A16 path here is a single-GPU kernel; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w4.load_library()
+    torch.cuda.set_device(0)
+
+    cases, copies = decode_cases()
+    step_weight_bytes = sum(c.weight_bytes for c in cases)
+    step_algo_bytes = sum(c.algo_bytes for c in cases)
+    # One graph per copy index: graph j runs the 12 GEMMs on copy j.
+    graphs = capture_graphs([[(lambda c=c, j=j: c.launch(j)) for c in cases] for j in range(copies)])
+    torch.cuda.synchronize()
+    ms = time_graphs(graphs, args.steps, args.warmup)
+    ms_per_step = ms / args.steps
+    value = step_weight_bytes / (ms_per_step * 1e-3) / 1e9
+    launches = len(cases)
+    avg_launch_us = ms_per_step * 1e3 / launches
+    achieved = (step_algo_bytes / launches) / (avg_launch_us * 1e-6) / 1e9
+
+    breakdown = []
+    for c in cases:
+        us = per_case_rate(c, reps=10)
+        breakdown.append({"M": c.M, "N": c.N, "K": c.K, "us": round(us, 2),
+                          "weight_GBps": round(c.weight_bytes / us / 1e3, 1),
+                          "frac_of_hbm_peak": round(c.weight_bytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode-shape symmetric W4A16 GEMM: M in {1,4,8,16} x (N,K) in "
+                        "{(4096,4096),(14336,4096),(4096,14336)}, G=128, uint4b8, fp16 (12 GEMMs per step)",
+            "weight_bytes_per_step": step_weight_bytes,
+            "weight_copies": copies,
+            "rotation_bytes": step_weight_bytes * copies,
+            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "kernel": "skinny_kernel (split-K decode GEMM)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(avg_launch_us, 3),
+            "algorithmic_bytes_per_launch": step_algo_bytes / launches,
+        },
+        "decode_breakdown": breakdown,
+    }
+    del graphs
+    if not args.no_extras:
+        result["extras"] = extras(args.warmup)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,6 +35,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // constant c = -(128 + z) * s (exact: an 8-bit integer times an 8-bit
 // significand) yields (q - z) * s exactly in fp32 (every partial sum is
 // representable); v_cvt_pk_bf16_f32 then rounds to nearest even once.
+//
+// The pair extraction (w >> 4p) & 0x000F000F | magic is one v_and_or_b32 per
+// pair (plus the shift). The mask and magic are passed in registers: gfx9
+// VOP3 instructions cannot encode two literal constants, and given literals
+// the compiler splits the operation into v_and_b32 + v_or_b32.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(magic));
+    return r;
+}
+
 template <int DT>
 struct Dequant;
 
@@ -52,11 +63,12 @@ struct Dequant<0> {
         p.ss = half2_t{s, s};
         return p;
     }
-    static __device__ __forceinline__ u32x4 apply(uint32_t w, const Params& p) {
+    // mask = 0x000F000F, magic = 0x64006400.
+    static __device__ __forceinline__ u32x4 apply(uint32_t w, const Params& p, uint32_t mask, uint32_t magic) {
         u32x4 out;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t x = ((w >> (4 * q)) & 0x000F000Fu) | 0x64006400u;
+            const uint32_t x = and_or(w >> (4 * q), mask, magic);
             half2_t h = __builtin_bit_cast(half2_t, x);
             h = (h + p.zz) * p.ss;
             out[q] = __builtin_bit_cast(uint32_t, h);
@@ -80,11 +92,12 @@ struct Dequant<1> {
         p.c = -(128.0f + (float)z) * s;
         return p;
     }
-    static __device__ __forceinline__ u32x4 apply(uint32_t w, const Params& p) {
+    // mask = 0x000F000F, magic = 0x43004300.
+    static __device__ __forceinline__ u32x4 apply(uint32_t w, const Params& p, uint32_t mask, uint32_t magic) {
         u32x4 out;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t x = ((w >> (4 * q)) & 0x000F000Fu) | 0x43004300u;
+            const uint32_t x = and_or(w >> (4 * q), mask, magic);
             const bf16x2_t b = __builtin_bit_cast(bf16x2_t, x);
             const float lo = __builtin_amdgcn_fdot2_f32_bf16(b, p.slo, p.c, false);
             const float hi = __builtin_amdgcn_fdot2_f32_bf16(b, p.shi, p.c, false);
@@ -112,6 +125,10 @@ __device__ __forceinline__ floatx4 mfma16x16x32<1>(const u32x4& a, const u32x4& 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    acc, 0, 0, 0);
 }
+
+// The magic constant of the pair extraction for each act dtype.
+template <int DT>
+constexpr uint32_t kMagic = DT == 0 ? 0x64006400u : 0x43004300u;
 
 // fp32 -> act dtype bits, round to nearest even; and act bits -> fp32.
 template <int DT>

@@ -21,14 +21,21 @@ struct Geometry {
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Split-K skinny launch plan (M <= 16 rows per launch).
+// Skinny launch plan (M <= 16 rows per launch). Persistent variant: n_groups
+// workgroups of WK waves, each owning n-tiles blockIdx.x + i * n_groups and
+// walking K in phases of WK * KT k-tiles.
+// Split-K variant: a workgroup is 4 waves; each wave owns NW consecutive
+// n-tiles (16 rows each) and all KT k-tiles (128 k each) of the workgroup's
+// K range, so the workgroup covers 4*NW n-tiles x KT k-tiles and ksplit
+// workgroups split K.
 struct SkinnyPlan {
-    int WN = 4;      // n-tiles per workgroup (one per wave column)
-    int WK = 1;      // k-slices per workgroup (waves splitting K inside it)
-    int KT = 4;      // k-tiles (128 k) per wave
-    int ksplit = 1;  // workgroups splitting K (reduced through the workspace)
-    int64_t n_groups = 0;
-    size_t partial_bytes = 0;  // fp32 partial sums in the workspace
+    bool full_k = false;  // persistent variant: K not split across workgroups
+    int WK = 1;           // waves per workgroup (persistent variant)
+    int NW = 2;
+    int KT = 4;
+    int ksplit = 1;
+    int64_t n_groups = 0;      // workgroups along N
+    size_t partial_bytes = 0;  // fp32 partial sums in the workspace (16 rows)
     size_t counter_bytes = 0;  // arrival counters in the workspace
 };
 
@@ -49,6 +56,12 @@ inline hipError_t allow_lds(size_t bytes) {
     if (e == hipSuccess) granted = bytes;
     return e;
 }
+
+// The persistent skinny variant (no split of K across workgroups) is used
+// when N/16 reaches this many n-tiles, enough to occupy most of the CUs.
+constexpr int64_t kFullKMinTiles = 192;
+constexpr int64_t kCUs = 256;                 // MI355X compute units
+constexpr int64_t kMaxTilesPerWGHost = 4;     // n-tiles per persistent workgroup
 
 constexpr size_t kCounterRegionBytes = 64 * 1024;  // 16384 u32 arrival counters
 

@@ -112,6 +112,10 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
         }
     };
 
+    // Dequant operands in registers (see and_or).
+    uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
+    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
+
     floatx4 acc[MB][WNT];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
             for (int nb = 0; nb < WNT; ++nb) {
                 const int u = s / (4 / SPT);
-                bq[nb] = Dequant<DT>::apply(braw[nb][s], Dequant<DT>::make(sb[nb][u], zb[nb][u]));
+                bq[nb] = Dequant<DT>::apply(braw[nb][s], Dequant<DT>::make(sb[nb][u], zb[nb][u]), dq_mask, dq_magic);
             }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {

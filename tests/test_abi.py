@@ -108,9 +108,10 @@ def _gemm(lib, **kw):
         (dict(A=ctypes.c_void_p(4104)), UNSUPPORTED, "16-byte aligned"),
         (dict(packed=ctypes.c_void_p(4100)), INVALID, "256-byte aligned"),
         (dict(K=4000, lda=4000), UNSUPPORTED, "K=4000 must be divisible by 128"),
-        # the skinny path of this shape splits K and needs a workspace
-        (dict(M=1), SIZE, "workspace of 0 bytes is smaller"),
-        (dict(M=1, ws=ctypes.c_void_p(4096), wsb=16), SIZE, "workspace of 16 bytes is smaller"),
+        (dict(bias=ctypes.c_void_p(4097)), INVALID, "2-byte aligned"),
+        # a narrow weight (64 n-tiles) splits K on the skinny path and needs a workspace
+        (dict(M=1, N=1024, ldc=1024), SIZE, "workspace of 0 bytes is smaller"),
+        (dict(M=1, N=1024, ldc=1024, ws=ctypes.c_void_p(4096), wsb=16), SIZE, "workspace of 16 bytes is smaller"),
     ],
 )
 def test_gemm_rejects_before_any_hip_call(lib, kw, status, needle):
@@ -147,11 +148,12 @@ def test_select_path(lib):
 
 def test_workspace_size(lib):
     assert w4.workspace_size(256, 4096, 4096, 128) == 0  # tiled path needs none
-    ws = w4.workspace_size(16, 4096, 4096, 128)
+    assert w4.workspace_size(16, 4096, 4096, 128) == 0  # wide weights: K is not split
+    ws = w4.workspace_size(16, 1024, 4096, 128)  # narrow weights split K
     assert ws > w4.workspace_counter_bytes()
     # sized for 16 rows, so every M <= 16 fits the same workspace
-    assert w4.workspace_size(1, 4096, 4096, 128) == ws
-    assert w4.workspace_size(300, 4096, 4096, 128, path=w4.PATH_SKINNY) == ws
+    assert w4.workspace_size(1, 1024, 4096, 128) == ws
+    assert w4.workspace_size(300, 1024, 4096, 128, path=w4.PATH_SKINNY) == ws
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

@@ -6,8 +6,9 @@
 * GEMM: max|C - C_ref| / max|C_ref| within 2e-3 (fp16) / 1e-2 (bf16) on every
   workload shape at full size (all rows for M <= 64, sampled rows above), on
   the forced skinny and MFMA kernels and on the dispatcher;
-* edge cases: M = 0, ragged M and N tails, strided A and C, bias, minimal K,
-  G = -1 vs G = K, uint4 without zero points, determinism, workspace reuse.
+* edge cases: M = 0, ragged M and N tails, strided A and C, bias, minimal and
+  very large K, G = -1 vs G = K, uint4 without zero points, determinism and
+  workspace reuse.
 """
 
 from __future__ import annotations
@@ -254,16 +255,35 @@ def test_m_zero_is_a_noop():
     assert C.shape == (0, 64)
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (1, 14336, 4096), (256, 4096, 14336)])
+@pytest.mark.parametrize(
+    "M,N,K", [(16, 4096, 4096), (1, 14336, 4096), (7, 4096, 14336), (256, 4096, 14336), (1, 1024, 14336), (16, 512, 4096)]
+)
 def test_deterministic_and_workspace_returns_to_zero(M, N, K):
+    # Split-K partials meet through the workspace; repeated calls must give
+    # identical bits and leave every arrival counter at zero.
     case = _case(22, M, N, K, 128, UINT4B8, "f16")
     packed = repack(case)
     A = case.A.to(DEV)
     ws = w4.Workspace(DEV)
     C1 = w4.gemm(A, packed, N, K, 128, UINT4B8, workspace=ws)
-    C2 = w4.gemm(A, packed, N, K, 128, UINT4B8, workspace=ws)
+    for _ in range(20):
+        C2 = w4.gemm(A, packed, N, K, 128, UINT4B8, workspace=ws)
+        assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
     torch.cuda.synchronize()
-    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
     if ws.buf is not None:
         nctr = w4.workspace_counter_bytes()
         assert torch.all(ws.buf[:nctr] == 0)
+    if M <= 16:
+        rows = sample_rows(M)
+        assert rel_err_rows(C1, oracle_ref(case, rows=rows), rows) <= oracle.TOLERANCE["f16"]
+
+
+@pytest.mark.parametrize("K", [128, 384, 16384, 20480])
+def test_skinny_k_extremes(K):
+    # One tile (K = 128), a ragged last wave chunk (K = 384), the largest K
+    # with one chunk per wave (16384) and beyond it, where waves loop (20480).
+    N, G = 64, 128
+    case = _case(23, 5, N, K, G, UINT4, "bf16")
+    packed = repack(case)
+    C = w4.gemm(case.A.to(DEV), packed, N, K, G, UINT4, path=SKINNY)
+    assert oracle.rel_err(C.cpu(), oracle_ref(case)) <= oracle.TOLERANCE["bf16"]
