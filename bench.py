@@ -285,6 +285,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-shape decode timings")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized buffer 10 times (a known-size workload that calibrates the "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -293,8 +297,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    w4.load_library()
     torch.cuda.set_device(0)
+    if args.calibration_copy:
+        n = args.calibration_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=DEV)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "copies": 10}), flush=True)
+        return
+    w4.load_library()
 
     cases, copies = decode_cases()
     step_weight_bytes = sum(c.weight_bytes for c in cases)
@@ -310,7 +323,7 @@ def main():
     achieved = (step_algo_bytes / launches) / (avg_launch_us * 1e-6) / 1e9
 
     breakdown = []
-    for c in cases:
+    for c in ([] if args.no_breakdown else cases):
         us = per_case_rate(c, reps=10)
         breakdown.append({"M": c.M, "N": c.N, "K": c.K, "us": round(us, 2),
                           "weight_GBps": round(c.weight_bytes / us / 1e3, 1),
@@ -339,7 +352,7 @@ def main():
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         },
         "roofline": {
-            "kernel": "skinny_kernel (split-K decode GEMM)",
+            "kernel": "skinny decode GEMM (skinny_persist_kernel at these shapes)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
