@@ -150,7 +150,10 @@ int32_t w4a16_select_path(int64_t M, int32_t path, int32_t skinny_max_m);
  *   workspace, workspace_bytes  device workspace, >= w4a16_workspace_size();
  *           may be NULL when that size is 0
  * M == 0 is a no-op. The result does not depend on the workspace contents or
- * on earlier calls (no float atomics: the order of every sum is fixed). */
+ * on earlier calls (no float atomics: the order of every sum is fixed).
+ * The skinny kernel addresses the (at most 16) rows of one launch with 32-bit
+ * byte offsets: it returns W4A16_ERR_UNSUPPORTED when
+ * ((min(M, 16) - 1) * lda + K) * 2 >= 2^31. */
 w4a16_status w4a16_gemm(const void *A, int64_t M, int64_t lda, const void *packed, int64_t N, int64_t K,
                         int32_t group_size, int32_t qtype, int32_t dtype, const void *bias, void *C, int64_t ldc,
                         int32_t path, int32_t skinny_max_m, void *workspace, size_t workspace_bytes,

@@ -21,16 +21,21 @@ struct Geometry {
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Skinny launch plan (M <= 16 rows per launch). Persistent variant: n_groups
-// workgroups of WK waves, each owning n-tiles blockIdx.x + i * n_groups and
-// walking K in phases of WK * KT k-tiles.
-// Split-K variant: a workgroup is 4 waves; each wave owns NW consecutive
-// n-tiles (16 rows each) and all KT k-tiles (128 k each) of the workgroup's
-// K range, so the workgroup covers 4*NW n-tiles x KT k-tiles and ksplit
-// workgroups split K.
+// Skinny launch plan (M <= 16 rows per launch).
+// Full-K variants (mode kRegisters / kResident / kStreamed): n_groups
+// workgroups of up to 8 waves, each owning at most nn_max n-tiles
+// (blockIdx.x + i * n_groups) and all of K; wave w takes k-tiles
+// [w * ktw, (w + 1) * ktw).
+// Split-K variant (mode kSplitK): a workgroup is 4 waves; each wave owns NW
+// consecutive n-tiles (16 rows each) and all KT k-tiles (128 k each) of the
+// workgroup's K range, so the workgroup covers 4*NW n-tiles x KT k-tiles and
+// ksplit workgroups split K.
 struct SkinnyPlan {
-    bool full_k = false;  // persistent variant: K not split across workgroups
-    int WK = 1;           // waves per workgroup (persistent variant)
+    enum Mode { kSplitK = 0, kRegisters = 1, kResident = 2, kStreamed = 3 };
+    Mode mode = kSplitK;
+    bool full_k = false;  // mode != kSplitK: K not split across workgroups
+    int nn_max = 1;       // full-K: n-tiles per workgroup, at most
+    int ktw = 1;          // full-K: k-tiles per wave
     int NW = 2;
     int KT = 4;
     int ksplit = 1;
@@ -57,11 +62,11 @@ inline hipError_t allow_lds(size_t bytes) {
     return e;
 }
 
-// The persistent skinny variant (no split of K across workgroups) is used
+// The full-K skinny variants (no split of K across workgroups) are used
 // when N/16 reaches this many n-tiles, enough to occupy most of the CUs.
 constexpr int64_t kFullKMinTiles = 192;
-constexpr int64_t kCUs = 256;                 // MI355X compute units
-constexpr int64_t kMaxTilesPerWGHost = 4;     // n-tiles per persistent workgroup
+constexpr int64_t kCUs = 256;          // MI355X compute units
+constexpr int64_t kMaxTilesPerWG = 16; // full-K: n-tiles per workgroup (LDS for the wave partials)
 
 constexpr size_t kCounterRegionBytes = 64 * 1024;  // 16384 u32 arrival counters
 

@@ -55,6 +55,7 @@ struct SkinnyArgs {
     int64_t n_groups;
     int xcd_map;
     uint32_t mask, magic;  // dequant operands, kept in registers (see Dequant)
+    uint32_t a_bytes;      // bytes from A to the end of row M-1: ((M-1)*lda + K)*2 < 2^31
 };
 
 // Cross-workgroup exchange of split-K partial sums. Every access carries the
@@ -267,224 +268,475 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + ng, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Persistent variant, used when the n-tiles alone can occupy the chip: one
-// workgroup of up to 8 waves per CU (grid = min(N/16, CUs)), n-tiles nt =
-// blockIdx.x + i * gridDim.x. K is walked in phases of PT = waves * KT
-// k-tiles; the activation rows of a phase sit in LDS (staged once per
-// workgroup instead of once per n-tile, double-buffered: phase p+1 is
-// fetched while phase p is multiplied). Within a phase, wave w takes k-tiles
-// [w*KT, +KT) of every n-tile, and the weights of the next (phase, n-tile)
-// unit are always in flight while the current one is multiplied.
+// Full-K streaming variants, used when the n-tiles alone can occupy the chip.
+// A workgroup of 8 waves owns n-tiles nt = blockIdx.x + i * gridDim.x
+// (i < nn) and the whole K range; wave w takes k-tiles [w*ktw, (w+1)*ktw) of
+// each of them, so no partial sum leaves the workgroup. The grid holds
+// ceil(NT / nn_max) workgroups, nn_max = ceil(NT / 256), so every workgroup
+// gets nn_max or nn_max - 1 n-tiles and no CU gets two workgroups.
+//
+// A decode GEMM streams each weight byte once and does little arithmetic per
+// byte, so its duration is set by how many HBM requests are in flight. Each
+// wave therefore requests its data before any arithmetic, in the order it
+// is consumed, so the hardware counter waits let it compute on the first
+// tiles while the rest arrive:
+//  * skinny_res_kernel (at most 4 k-tiles per wave and 16 units per wave):
+//    the activation fragments of the wave's k-tiles are loaded once and stay
+//    in registers for all its n-tiles; every weight tile, scale and zero of
+//    the wave is requested at once.
+//  * skinny_str_kernel (longer K ranges or more n-tiles): a ring of D units,
+//    each one weight tile with its activation fragments, scales and zeros;
+//    unit u + D is requested as soon as unit u is consumed.
+// Partial sums over the waves meet in LDS after one barrier; wave q then
+// finishes n-tiles q, q + 8, ...: a fixed-order sum, + bias, one rounding.
 //
 // Offset-corrected dequantisation: the MFMA B operand is the exact magic
 // value m + q (m = 1024 for fp16, 128 for bf16), one v_and_or_b32 per pair
 // of codes. Over a fold block of FW words (FW*32 consecutive k, never
 // crossing a group) the MFMA sums P = sum_k A*(m + q); one more MFMA against
-// an all-ones B gives S = sum_k A for the block (once per phase, shared by
-// all n-tiles). Then acc += s * (P - (m + z) * S) in fp32, which equals
-// s * sum_k A*(q - z): the scale is applied to an exact-integer-weight sum
-// instead of to every weight (more accurate than rounding each (q - z) * s,
-// and with A = I it is (q - z) * s exactly, rounded once at the end).
-constexpr int kMaxTilesPerWG = 4;  // n-tiles per workgroup (accumulators per wave)
-constexpr int kPersistThreads = 512;
-constexpr int kStageChunks = 8;    // 16-byte A chunks per thread per phase (M * PT <= 256)
-
-struct PersistArgs {
-    int PT;        // k-tiles per phase (waves * KT)
-    int phases;
-    int lds_ld;    // LDS row stride of a staged phase, in elements
-    int buf_bytes; // bytes of one phase buffer
-};
+// an all-ones B gives S = sum_k A for the block. Then
+// acc += s * (P - (m + z) * S) in fp32, which equals s * sum_k A*(q - z):
+// the scale is applied to an exact-integer-weight sum instead of to every
+// weight (more accurate than rounding each (q - z) * s, and with A = I it is
+// (q - z) * s exactly, rounded once at the end).
+constexpr int kStreamWaves = 8;
+constexpr int kStreamThreads = 64 * kStreamWaves;
+constexpr int kResMaxKt = 4;  // k-tiles per wave in skinny_res_kernel
+constexpr int kStrDepth = 8;  // units in flight per wave in skinny_str_kernel
 
 template <int DT>
 __device__ __forceinline__ float magic_base() { return DT == 0 ? 1024.0f : 128.0f; }
 
-template <int DT, int QT, int KT, int FW>
-__global__ __launch_bounds__(kPersistThreads) void skinny_persist_kernel(SkinnyArgs a, PersistArgs ph) {
-    constexpr int WORDS = 4 * KT;      // weight words per lane per unit
-    constexpr int NB = WORDS / FW;     // fold blocks per unit
+template <int DT>
+__device__ __forceinline__ u32x4 ones_operand() {
+    const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
+    return u32x4{one2, one2, one2, one2};
+}
+
+// Loads through buffer descriptors. Reads past a descriptor's size return
+// zeros without a memory access, which the full-K kernels use twice:
+//  * activation lanes of padding rows (r >= M) read past the end of A, so at
+//    small M most fragment lanes cost no load bandwidth;
+//  * a unit that does not exist (past the wave's k-tiles, past the
+//    workgroup's n-tiles, or past the end of a streamed wave's work) gets a
+//    descriptor of 0 bytes. Every load is then issued unconditionally and in
+//    the order the data is consumed, so the counter wait before each use is
+//    exact, and the extra loads cost only issue slots.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Activation rows [0, M) of one launch; a_bytes = ((M-1)*lda + K)*2 < 2^31.
+struct ActRows {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lane_off;  // byte offset of this lane's row and 8-element slice
+    __device__ ActRows(const SkinnyArgs& a, int r, int g4)
+        : rsrc(make_rsrc(a.A, a.a_bytes)),
+          lane_off(r < a.M ? (uint32_t)(((int64_t)r * a.lda + 8 * g4) * 2) : 0x80000000u) {}
+    // Word s of k-tile kt: A[r][128*kt + 32*s + 8*g4 .. +7]; zeros if !valid.
+    __device__ __forceinline__ u32x4 load(int64_t kt, int s, bool valid) const {
+        const uint32_t off = (lane_off + (uint32_t)(kt * 256 + 64 * s)) | (valid ? 0u : 0x80000000u);
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+    }
+};
+
+// Weight tile (nt, kt) (1 KB, one 16-byte word group per lane), streamed
+// once: nontemporal.
+__device__ __forceinline__ u32x4 load_tile(const SkinnyArgs& a, int64_t nt, int64_t kt, int lane, bool valid) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.codes + (valid ? nt : 0) * a.KTT * 64,
+                                                valid ? (uint32_t)(a.KTT * 1024) : 0u);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((kt * 64 + lane) * 16), 0, 2));
+}
+
+// Scale (and zero) of row 16*nt + r for the fold block that starts at
+// k-tile kt, word f*FW.
+template <int FW>
+__device__ __forceinline__ uint32_t group_of(const SkinnyArgs& a, int64_t kt, int f) {
+    const int64_t k = kt * 128 + f * FW * 32;
+    return a.one_group ? 0u : (uint32_t)(k >> a.gshift);
+}
+template <int QT, int FW>
+__device__ __forceinline__ void load_scale_zero(const SkinnyArgs& a, int64_t nt, int64_t kt, int f, int r, bool valid,
+                                                uint16_t& sb, uint8_t& zb) {
+    const uint32_t g = group_of<FW>(a, kt, f);
+    const int64_t base = (valid ? nt : 0) * a.Kg * 16;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + base, valid ? (uint32_t)(a.Kg * 32) : 0u);
+    sb = __builtin_amdgcn_raw_buffer_load_b16(rs, (g * 16 + r) * 2, 0, 0);
+    if (QT) {
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.zeros + base, valid ? (uint32_t)(a.Kg * 16) : 0u);
+        zb = __builtin_amdgcn_raw_buffer_load_b8(rz, g * 16 + r, 0, 0);
+    }
+}
+
+// B operand of exact magic values m + q for the 8 codes of word wv.
+__device__ __forceinline__ u32x4 magic_operand(uint32_t wv, uint32_t mask, uint32_t magic) {
+    u32x4 b;
+    b[0] = and_or(wv, mask, magic);
+    b[1] = and_or(wv >> 4, mask, magic);
+    b[2] = and_or(wv >> 8, mask, magic);
+    b[3] = and_or(wv >> 12, mask, magic);
+    return b;
+}
+
+// (No inline asm may touch sbits or z: the compiler does not wait for a
+// pending buffer load before an asm operand tied to its register.)
+template <int DT, int QT>
+__device__ __forceinline__ void fold(floatx4& acc, const floatx4& P, const floatx4& S, uint16_t sbits, uint8_t z) {
+    const float sf = act_to_float<DT>(sbits);
+    const float zf = -(magic_base<DT>() + (QT ? (float)z : 8.0f));
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(sf, __builtin_fmaf(zf, S[jj], P[jj]), acc[jj]);
+}
+
+// The first `nwa` waves have written red[wave][i][lane] for i < nn; wave q
+// of the workgroup's nw waves sums them, in wave order, for n-tiles q,
+// q + nw, ..., adds the bias, rounds once and stores rows < M.
+template <int DT>
+__device__ __forceinline__ void finish_tiles(const SkinnyArgs& a, const floatx4* red, int nn, int nwa) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g4 = lane >> 4;
+    const int nw = blockDim.x >> 6;  // short K: fewer than 8 waves
+    for (int i = wave; i < nn; i += nw) {
+        floatx4 tot = red[(0 * nn + i) * 64 + lane];
+        for (int q = 1; q < nwa; ++q) tot += red[(q * nn + i) * 64 + lane];
+        const int64_t n = (blockIdx.x + (int64_t)i * gridDim.x) * 16 + r;
+        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int m = 4 * g4 + jj;
+            if (m < a.M) a.C[(int64_t)m * a.ldc + n] = to_act_bits<DT>(tot[jj] + bv);
+        }
+    }
+}
+
+template <int DT, int QT, int FW, int NNM>
+__global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a) {
+    constexpr int KTM = kResMaxKt;  // k-tiles per wave (the grid has ceil(KTT / 4) waves)
+    constexpr int NB = 4 / FW;      // fold blocks per k-tile
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    floatx4* red = reinterpret_cast<floatx4*>(smem);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+    const int nwaves = blockDim.x >> 6;
+    const int r = lane & 15, g4 = lane >> 4;
+    const int nn = (int)((a.NT - blockIdx.x + gridDim.x - 1) / gridDim.x);
+    const int64_t kt0 = (int64_t)wave * KTM;
+    const int kc = (int)(a.KTT - kt0 < KTM ? a.KTT - kt0 : KTM);  // >= 1
+
+    uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
+    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
+
+    // 1. Activation fragments: lane (r, g4) of word s of k-tile j holds
+    //    A[r][128*(kt0+j) + 32*s + 8*g4 .. +7] (zeros for rows r >= M).
+    const ActRows act(a, r, g4);
+    u32x4 af[KTM][4];
+#pragma unroll
+    for (int j = 0; j < KTM; ++j) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) af[j][s] = act.load(kt0 + j, s, j < kc);
+    }
+    // 2. Weight tiles, scales and zeros of every (n-tile, k-tile) unit, in
+    //    consumption order.
+    u32x4 w[NNM][KTM];
+    uint16_t sb[NNM][KTM][NB];
+    uint8_t zb[NNM][KTM][NB];
+#pragma unroll
+    for (int i = 0; i < NNM; ++i) {
+        const int64_t nt = blockIdx.x + (int64_t)i * gridDim.x;
+#pragma unroll
+        for (int j = 0; j < KTM; ++j) {
+            const bool valid = i < nn && j < kc;
+            w[i][j] = load_tile(a, nt, kt0 + j, lane, valid);
+#pragma unroll
+            for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(a, nt, kt0 + j, f, r, valid, sb[i][j][f], zb[i][j][f]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. S per fold block, once per k-tile (shared by the n-tiles).
+    const u32x4 ones = ones_operand<DT>();
+    floatx4 S[KTM][NB];
+#pragma unroll
+    for (int j = 0; j < KTM; ++j) {
+#pragma unroll
+        for (int f = 0; f < NB; ++f) {
+            S[j][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ww = 0; ww < FW; ++ww) S[j][f] = mfma16x16x32<DT>(af[j][f * FW + ww], ones, S[j][f]);
+        }
+    }
+
+    // 4. Multiply and fold, n-tile by n-tile.
+#pragma unroll
+    for (int i = 0; i < NNM; ++i) {
+        if (i < nn) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KTM; ++j) {
+                if (j < kc) {
+#pragma unroll
+                    for (int f = 0; f < NB; ++f) {
+                        floatx4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ww = 0; ww < FW; ++ww) {
+                            const int word = f * FW + ww;
+                            P = mfma16x16x32<DT>(af[j][word], magic_operand(w[i][j][word], dq_mask, dq_magic), P);
+                        }
+                        fold<DT, QT>(acc, P, S[j][f], sb[i][j][f], QT ? zb[i][j][f] : (uint8_t)8);
+                    }
+                }
+            }
+            red[(wave * nn + i) * 64 + lane] = acc;
+        }
+    }
+    __syncthreads();
+    finish_tiles<DT>(a, red, nn, nwaves);
+}
+
+// LDS row stride (halves) of a wave's activation slice of KTW k-tiles: 16
+// bytes of padding per row spread the rows over the LDS banks.
+template <int KTW>
+constexpr int act_lds_ld() { return KTW * 128 + 8; }
+
+template <int DT, int QT, int FW, int NNM, int KTW>
+__global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a) {
+    constexpr int NB = 4 / FW;                   // fold blocks per k-tile
+    constexpr int LD = act_lds_ld<KTW>();
+    constexpr int kMaxRows = KTW <= 4 ? 16 : 4;  // M this variant is launched for (LDS budget)
+    constexpr int kMaxChunks = (kMaxRows * KTW * 16 + 63) / 64;  // 16-byte activation chunks per lane
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
     const int nwaves = blockDim.x >> 6;
     const int r = lane & 15, g4 = lane >> 4;
     const int rr = r < a.M ? r : a.M - 1;
-    const int nn = (int)((a.NT - blockIdx.x + gridDim.x - 1) / gridDim.x);  // n-tiles of this workgroup
-    const int Kp = ph.PT * 128;
-    floatx4* red = reinterpret_cast<floatx4*>(smem + 2 * ph.buf_bytes);
+    const int nn = (int)((a.NT - blockIdx.x + gridDim.x - 1) / gridDim.x);
+    const int64_t kt0 = (int64_t)wave * KTW;
+    const int kc = (int)(a.KTT - kt0 < KTW ? a.KTT - kt0 : KTW);  // >= 1: the grid has ceil(KTT / KTW) waves
+    uint16_t* As = reinterpret_cast<uint16_t*>(smem) + (size_t)wave * a.M * LD;
 
-    // Dequant operands in registers (see and_or) and the all-ones B operand.
     uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
-    const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
-    const u32x4 ones = {one2, one2, one2, one2};
 
-    // Phase staging: M rows x Kp columns of A, zero past K; chunk c of 8
-    // elements -> row c / (Kp/8), column 8 * (c % (Kp/8)).
-    const int cpr = Kp / 8;
-    const int nchunks = a.M * cpr;
-    auto stage_load = [&](int p, u32x4 (&v)[kStageChunks]) {
+    // 1. The wave's activation slice, rows [0, M) x k in [128*kt0, 128*(kt0+kc)),
+    //    into registers (16-byte chunks, row-major over the slice). Only the M
+    //    real rows are read: the padding rows of the MFMA operand come from
+    //    LDS later, which has about three times the return bandwidth.
+    //    Chunk c is row c / CPR, column chunk c % CPR (CPR = KTW*16, a
+    //    constant); columns past the wave's kc k-tiles are not loaded.
+    constexpr int CPR = KTW * 16;
+    const int nch = a.M * CPR;
+    const int ccols = kc * 16;
+    u32x4 ach[kMaxChunks];
 #pragma unroll
-        for (int t = 0; t < kStageChunks; ++t) {
-            const int c = threadIdx.x + t * kPersistThreads;
-            v[t] = u32x4{0u, 0u, 0u, 0u};
-            if (c < nchunks) {
-                const int m = c / cpr;
-                const int64_t col = (int64_t)p * Kp + 8 * (c - m * cpr);
-                if (col < a.KTT * 128) v[t] = *reinterpret_cast<const u32x4*>(a.A + (int64_t)m * a.lda + col);
+    for (int t = 0; t < kMaxChunks; ++t) {
+        const int c = lane + 64 * t;
+        const int m = c / CPR, col = c - m * CPR;
+        if (c < nch && col < ccols)
+            ach[t] = *reinterpret_cast<const u32x4*>(a.A + (int64_t)m * a.lda + kt0 * 128 + 8 * col);
+    }
+    // 2. Every weight tile, scale and zero of the wave, in consumption order
+    //    (k-tile outer, n-tile inner). Units past the workgroup's n-tiles or
+    //    the wave's k-tiles use zero-size descriptors (see make_rsrc).
+    u32x4 w[KTW][NNM];
+    uint16_t sb[KTW][NNM][NB];
+    uint8_t zb[KTW][NNM][NB];
+#pragma unroll
+    for (int j = 0; j < KTW; ++j) {
+#pragma unroll
+        for (int i = 0; i < NNM; ++i) {
+            const int64_t nt = blockIdx.x + (int64_t)i * gridDim.x;
+            const bool valid = i < nn && j < kc;
+            w[j][i] = load_tile(a, nt, kt0 + j, lane, valid);
+#pragma unroll
+            for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(a, nt, kt0 + j, f, r, valid, sb[j][i][f], zb[j][i][f]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. Activation slice into this wave's LDS region (no other wave reads
+    //    it, and a wave's LDS accesses complete in order: no barrier).
+#pragma unroll
+    for (int t = 0; t < kMaxChunks; ++t) {
+        const int c = lane + 64 * t;
+        const int m = c / CPR, col = c - m * CPR;
+        if (c < nch && col < ccols) *reinterpret_cast<u32x4*>(As + m * LD + 8 * col) = ach[t];
+    }
+
+    // 4. k-tile by k-tile: the activation fragments (padding rows read row
+    //    M-1) and S once, then every n-tile.
+    const u32x4 ones = ones_operand<DT>();
+    floatx4 acc[NNM];
+#pragma unroll
+    for (int i = 0; i < NNM; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KTW; ++j) {
+        if (j < kc) {
+            u32x4 af[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[s] = *reinterpret_cast<const u32x4*>(As + rr * LD + j * 128 + 32 * s + 8 * g4);
+            floatx4 S[NB];
+#pragma unroll
+            for (int f = 0; f < NB; ++f) {
+                S[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ww = 0; ww < FW; ++ww) S[f] = mfma16x16x32<DT>(af[f * FW + ww], ones, S[f]);
+            }
+#pragma unroll
+            for (int i = 0; i < NNM; ++i) {
+                if (i < nn) {
+#pragma unroll
+                    for (int f = 0; f < NB; ++f) {
+                        floatx4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ww = 0; ww < FW; ++ww) {
+                            const int word = f * FW + ww;
+                            P = mfma16x16x32<DT>(af[word], magic_operand(w[j][i][word], dq_mask, dq_magic), P);
+                        }
+                        fold<DT, QT>(acc[i], P, S[f], sb[j][i][f], QT ? zb[j][i][f] : (uint8_t)8);
+                    }
+                }
             }
         }
-    };
-    auto stage_store = [&](int buf, const u32x4 (&v)[kStageChunks]) {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(smem + buf * ph.buf_bytes);
+    }
+    // 5. Partials over the waves through LDS (reusing the activation area
+    //    once every wave is done with it), fixed-order sum, bias, store.
+    __syncthreads();
+    floatx4* red = reinterpret_cast<floatx4*>(smem);
 #pragma unroll
-        for (int t = 0; t < kStageChunks; ++t) {
-            const int c = threadIdx.x + t * kPersistThreads;
-            if (c < nchunks) {
-                const int m = c / cpr;
-                *reinterpret_cast<u32x4*>(dst + m * ph.lds_ld + 8 * (c - m * cpr)) = v[t];
-            }
-        }
-    };
+    for (int i = 0; i < NNM; ++i)
+        if (i < nn) red[(wave * nn + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    finish_tiles<DT>(a, red, nn, nwaves);
+}
 
-    // One unit = (phase p, n-tile i): this wave's KT weight tiles and the
-    // scale (and zero) of each fold block.
-    struct Unit {
-        u32x4 w[KT];
+template <int DT, int QT, int FW>
+__global__ __launch_bounds__(kStreamThreads) void skinny_str_kernel(SkinnyArgs a, int ktw) {
+    constexpr int D = FW == 1 ? kStrDepth - 2 : kStrDepth;  // a scale (and zero) per word: fewer units fit
+    constexpr int NB = 4 / FW;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    floatx4* red = reinterpret_cast<floatx4*>(smem);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g4 = lane >> 4;
+    const int nn = (int)((a.NT - blockIdx.x + gridDim.x - 1) / gridDim.x);
+    const int64_t kt0 = (int64_t)wave * ktw;
+    const int kc = kt0 >= a.KTT ? 0 : (int)(a.KTT - kt0 < ktw ? a.KTT - kt0 : ktw);
+    const int nwa = (int)((a.KTT + ktw - 1) / ktw);  // waves with k-tiles
+    const int U = nn * kc;  // units of this wave: (n-tile i, k-tile j), j fastest
+
+    uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
+    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
+    const ActRows act(a, r, g4);
+
+    struct Slot {
+        u32x4 af[4];
+        u32x4 w;
         uint16_t sb[NB];
         uint8_t zb[NB];
     };
-    const int64_t KTT = a.KTT;
-    auto unit_load = [&](int p, int i, Unit& u) {
-        const int64_t nt = blockIdx.x + (int64_t)i * gridDim.x;
-        const int64_t kt0 = (int64_t)p * ph.PT + wave * KT;
-        const u32x4* src = a.codes + (nt * KTT + kt0) * 64 + lane;
+    Slot ring[D];
+    // Requests unit (pi, pj) into a slot and advances. Positions past the
+    // wave's units load nothing (zero-size descriptors) and are never
+    // consumed, so the ring is refilled unconditionally.
+    int pi = 0, pj = 0;
+    auto request = [&](Slot& sl) {
+        const bool valid = pi < nn && kc > 0;
+        const int64_t nt = blockIdx.x + (int64_t)pi * gridDim.x;
+        const int64_t kt = kt0 + pj;
 #pragma unroll
-        for (int j = 0; j < KT; ++j) {
-            u.w[j] = u32x4{0u, 0u, 0u, 0u};
-            if (kt0 + j < KTT) u.w[j] = __builtin_nontemporal_load(src + j * 64);
-        }
-        const int64_t sbase = nt * a.Kg * 16 + r;
+        for (int s = 0; s < 4; ++s) sl.af[s] = act.load(kt, s, valid);
+        sl.w = load_tile(a, nt, kt, lane, valid);
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            int64_t k = kt0 * 128 + bb * FW * 32;
-            if (k >= KTT * 128) k = KTT * 128 - 1;
-            const int64_t g = a.one_group ? 0 : (k >> a.gshift);
-            u.sb[bb] = a.scales[sbase + g * 16];
-            u.zb[bb] = QT ? a.zeros[sbase + g * 16] : (uint8_t)8;
+        for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(a, nt, kt, f, r, valid, sl.sb[f], sl.zb[f]);
+        if (++pj >= kc) {
+            pj = 0;
+            ++pi;
         }
+        // Keep the loads of a unit together and in unit order: the counter
+        // waits are in issue order, so a unit consumed first must be issued
+        // first.
+        __builtin_amdgcn_sched_barrier(0);
     };
-
-    floatx4 acc[kMaxTilesPerWG];
 #pragma unroll
-    for (int i = 0; i < kMaxTilesPerWG; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < D; ++s) request(ring[s]);
 
-    // Prologue: the first unit's weights are requested before phase 0 of A
-    // is staged, so the two fetches overlap.
-    Unit cur, nxt;
-    unit_load(0, 0, cur);
-    {
-        u32x4 v[kStageChunks];
-        stage_load(0, v);
-        stage_store(0, v);
-    }
-    __syncthreads();
-
-    for (int p = 0; p < ph.phases; ++p) {
-        const int buf = p & 1;
-        const bool more = p + 1 < ph.phases;
-        u32x4 stg[kStageChunks];
-        if (more) stage_load(p + 1, stg);
-        const uint16_t* As = reinterpret_cast<const uint16_t*>(smem + buf * ph.buf_bytes);
-        const uint16_t* arow = As + rr * ph.lds_ld + wave * KT * 128 + 8 * g4;
-
-        // S of each fold block of this wave's k-range (shared by the n-tiles).
-        floatx4 S[NB];
+    const u32x4 ones = ones_operand<DT>();
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    int ci = 0, cj = 0;  // unit being consumed
+    const int rounds = (U + D - 1) / D;
+    for (int rnd = 0; rnd < rounds; ++rnd) {
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            S[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < D; ++s) {
+            Slot& sl = ring[s];
+            if (rnd * D + s < U) {
 #pragma unroll
-            for (int ww = 0; ww < FW; ++ww) {
-                const int word = bb * FW + ww;
-                const u32x4 av = *reinterpret_cast<const u32x4*>(arow + (word >> 2) * 128 + 32 * (word & 3));
-                S[bb] = mfma16x16x32<DT>(av, ones, S[bb]);
-            }
-        }
-
-#pragma unroll
-        for (int i = 0; i < kMaxTilesPerWG; ++i) {
-            if (i < nn) {
-                // Prefetch the next unit: the next n-tile, or the first
-                // n-tile of the next phase.
-                if (i + 1 < nn) unit_load(p, i + 1, nxt);
-                else if (more) unit_load(p + 1, 0, nxt);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int bb = 0; bb < NB; ++bb) {
-                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+                for (int f = 0; f < NB; ++f) {
+                    floatx4 P = {0.f, 0.f, 0.f, 0.f}, S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ww = 0; ww < FW; ++ww) {
-                        const int word = bb * FW + ww;
-                        const uint32_t wv = cur.w[word >> 2][word & 3];
-                        u32x4 bq;
-                        bq[0] = and_or(wv, dq_mask, dq_magic);
-                        bq[1] = and_or(wv >> 4, dq_mask, dq_magic);
-                        bq[2] = and_or(wv >> 8, dq_mask, dq_magic);
-                        bq[3] = and_or(wv >> 12, dq_mask, dq_magic);
-                        const u32x4 av = *reinterpret_cast<const u32x4*>(arow + (word >> 2) * 128 + 32 * (word & 3));
-                        t = mfma16x16x32<DT>(av, bq, t);
+                        const int word = f * FW + ww;
+                        S = mfma16x16x32<DT>(sl.af[word], ones, S);
+                        P = mfma16x16x32<DT>(sl.af[word], magic_operand(sl.w[word], dq_mask, dq_magic), P);
                     }
-                    const float sf = act_to_float<DT>(cur.sb[bb]);
-                    const float zf = -(magic_base<DT>() + (float)cur.zb[bb]);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = __builtin_fmaf(sf, __builtin_fmaf(zf, S[bb][jj], t[jj]), acc[i][jj]);
+                    fold<DT, QT>(acc, P, S, sl.sb[f], QT ? sl.zb[f] : (uint8_t)8);
                 }
-                cur = nxt;
-            }
-        }
-        if (more) stage_store(buf ^ 1, stg);
-        __syncthreads();
-    }
-
-    // Reduce each n-tile's accumulators over the waves (fixed order), add the
-    // bias, round once, store.
-#pragma unroll
-    for (int i = 0; i < kMaxTilesPerWG; ++i) {
-        if (i < nn) {
-            red[wave * 64 + lane] = acc[i];
-            __syncthreads();
-            if (wave == 0) {
-                floatx4 tot = acc[i];
-                for (int q = 1; q < nwaves; ++q) tot += red[q * 64 + lane];
-                const int64_t n = (blockIdx.x + (int64_t)i * gridDim.x) * 16 + r;
-                const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int m = 4 * g4 + jj;
-                    if (m < a.M) a.C[(int64_t)m * a.ldc + n] = to_act_bits<DT>(tot[jj] + bv);
+                if (++cj == kc) {
+                    red[(wave * nn + ci) * 64 + lane] = acc;
+                    acc = floatx4{0.f, 0.f, 0.f, 0.f};
+                    cj = 0;
+                    ++ci;
                 }
             }
-            __syncthreads();
+            request(sl);
         }
     }
+    __syncthreads();
+    finish_tiles<DT>(a, red, nn, nwa < kStreamWaves ? nwa : kStreamWaves);
 }
 
-template <int DT, int QT, int KT, int FW>
-hipError_t launch_persist_fw(const SkinnyArgs& a, const PersistArgs& ph, dim3 grid, dim3 block, size_t lds,
-                             hipStream_t stream) {
-    hipError_t e = allow_lds<skinny_persist_kernel<DT, QT, KT, FW>>(lds);
-    if (e == hipSuccess) hipLaunchKernelGGL((skinny_persist_kernel<DT, QT, KT, FW>), grid, block, lds, stream, a, ph);
+template <int DT, int QT, int FW, int NNM>
+hipError_t launch_reg(const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
+    hipLaunchKernelGGL((skinny_reg_kernel<DT, QT, FW, NNM>), grid, block, lds, stream, a);
+    return hipSuccess;
+}
+
+template <int DT, int QT, int FW, int NNM, int KTW>
+hipError_t launch_res(const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
+    hipError_t e = allow_lds<skinny_res_kernel<DT, QT, FW, NNM, KTW>>(lds);
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_res_kernel<DT, QT, FW, NNM, KTW>), grid, block, lds, stream, a);
     return e;
 }
 
-template <int DT, int QT, int KT>
-hipError_t launch_persist_t(const SkinnyArgs& a, const PersistArgs& ph, int fw, dim3 grid, dim3 block, size_t lds,
-                            hipStream_t stream) {
-    switch (fw) {
-        case 1: return launch_persist_fw<DT, QT, KT, 1>(a, ph, grid, block, lds, stream);
-        case 2: return launch_persist_fw<DT, QT, KT, 2>(a, ph, grid, block, lds, stream);
-        default: return launch_persist_fw<DT, QT, KT, 4>(a, ph, grid, block, lds, stream);
+template <int DT, int QT, int FW>
+hipError_t launch_stream_fw(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_t stream) {
+    const dim3 grid((unsigned)p.n_groups);
+    const size_t lds = (size_t)kStreamWaves * p.nn_max * 64 * sizeof(floatx4);
+    if (p.mode == SkinnyPlan::kRegisters) {
+        const dim3 block((unsigned)(64 * ((a.KTT + kResMaxKt - 1) / kResMaxKt)));
+        hipError_t e = hipSuccess;
+        if (p.nn_max == 1) e = launch_reg<DT, QT, FW, 1>(a, grid, block, lds, stream);
+        else if (p.nn_max == 2 || FW == 1) e = launch_reg<DT, QT, FW, 2>(a, grid, block, lds, stream);
+        else e = launch_reg<DT, QT, FW, (FW == 1 ? 2 : 4)>(a, grid, block, lds, stream);
+        return e;
     }
+    if (p.mode == SkinnyPlan::kResident) {
+        const dim3 block((unsigned)(64 * ((a.KTT + p.ktw - 1) / p.ktw)));
+        const size_t lds_a = (size_t)kStreamWaves * a.M * p.ktw * 128 * 2 + (size_t)kStreamWaves * a.M * 16;
+        const size_t lds_r = lds > lds_a ? lds : lds_a;
+        hipError_t e = hipSuccess;
+        // Instantiated shapes (n-tiles per workgroup x k-tiles per wave); the
+        // planner only picks these.
+        // (FW == 1, a scale per word, only with up to 2 n-tiles.)
+        if (p.ktw == 4 && p.nn_max == 1) e = launch_res<DT, QT, FW, 1, 4>(a, grid, block, lds_r, stream);
+        else if (p.ktw == 4 && (p.nn_max == 2 || FW == 1)) e = launch_res<DT, QT, FW, 2, 4>(a, grid, block, lds_r, stream);
+        else if (p.ktw == 4) e = launch_res<DT, QT, FW, (FW == 1 ? 2 : 4), 4>(a, grid, block, lds_r, stream);
+        else e = launch_res<DT, QT, FW, 1, 14>(a, grid, block, lds_r, stream);
+        return e;
+    }
+    hipError_t e = allow_lds<skinny_str_kernel<DT, QT, FW>>(lds);
+    if (e == hipSuccess)
+        hipLaunchKernelGGL((skinny_str_kernel<DT, QT, FW>), grid, dim3(kStreamThreads), lds, stream, a, p.ktw);
+    return e;
 }
 
 template <int DT, int QT, int NW, int KT>
@@ -497,21 +749,13 @@ void launch_skinny_t(const SkinnyArgs& a, int spt, dim3 grid, hipStream_t stream
 }
 
 template <int DT, int QT>
-hipError_t launch_persist_q(const SkinnyArgs& a, const SkinnyPlan& p, int spt, hipStream_t stream) {
-    PersistArgs ph;
-    ph.PT = p.WK * p.KT;
-    ph.phases = (int)((a.KTT + ph.PT - 1) / ph.PT);
-    ph.lds_ld = ph.PT * 128 + 8;
-    ph.buf_bytes = (a.M * ph.lds_ld * 2 + 15) / 16 * 16;
-    const size_t lds = 2 * (size_t)ph.buf_bytes + (size_t)p.WK * 64 * sizeof(floatx4);
-    const dim3 grid((unsigned)p.n_groups), block((unsigned)(64 * p.WK));
+hipError_t launch_stream_q(const SkinnyArgs& a, const SkinnyPlan& p, int spt, hipStream_t stream) {
     // Fold width: words per fold block, at most one group (G / 32 words) and
     // at most 4 (one k-tile); spt = groups per k-tile.
-    const int fw = spt >= 4 ? 1 : (spt == 2 ? 2 : 4);
-    switch (p.KT) {
-        case 1: return launch_persist_t<DT, QT, 1>(a, ph, fw, grid, block, lds, stream);
-        case 2: return launch_persist_t<DT, QT, 2>(a, ph, fw, grid, block, lds, stream);
-        default: return launch_persist_t<DT, QT, 4>(a, ph, fw, grid, block, lds, stream);
+    switch (spt) {
+        case 1: return launch_stream_fw<DT, QT, 4>(a, p, stream);
+        case 2: return launch_stream_fw<DT, QT, 2>(a, p, stream);
+        default: return launch_stream_fw<DT, QT, 1>(a, p, stream);
     }
 }
 
@@ -535,23 +779,35 @@ void launch_skinny_q(const SkinnyArgs& a, const SkinnyPlan& p, int spt, dim3 gri
 }  // namespace
 
 SkinnyPlan plan_skinny(int64_t M, const Geometry& g) {
-    (void)M;  // sized for 16 rows, so one workspace serves every M <= 16
-    SkinnyPlan p;
+    SkinnyPlan p;  // the workspace is sized for 16 rows, so one serves every M <= 16
     const int64_t NT = g.N / 16, KTT = g.K / 128;
     if (NT >= kFullKMinTiles) {
-        // Persistent: one workgroup of up to 8 waves per CU, at most
-        // kMaxTilesPerWGHost n-tiles each. Phases of PT = waves * KT k-tiles
-        // with M * PT <= 256, so two phase buffers of M rows take at most
-        // 129 KB of LDS; as many k-tiles per wave as that allows, up to 4.
+        // Full K: one workgroup per CU while N allows, n-tiles spread evenly.
         p.full_k = true;
-        p.NW = 1;
-        p.n_groups = NT < kCUs ? NT : kCUs;
-        if ((NT + p.n_groups - 1) / p.n_groups > kMaxTilesPerWGHost)
-            p.n_groups = (NT + kMaxTilesPerWGHost - 1) / kMaxTilesPerWGHost;
-        const int64_t m = M < 1 ? 1 : M;
-        p.WK = (int)(KTT < 8 ? KTT : 8);
-        p.KT = 1;
-        while (p.KT < 4 && (int64_t)p.WK * p.KT * 2 * m <= 256 && (int64_t)p.WK * p.KT * 2 <= KTT) p.KT *= 2;
+        const int64_t per = (NT + kCUs - 1) / kCUs;
+        p.nn_max = (int)(per < kMaxTilesPerWG ? per : kMaxTilesPerWG);
+        p.n_groups = (NT + p.nn_max - 1) / p.nn_max;
+        // Every weight tile of a wave in registers (at most 16): with K <=
+        // 4096, 4 k-tiles per wave (ceil(KTT / 4) <= 8 waves) and up to 4
+        // n-tiles. The activation fragments either stay in registers for all
+        // of the wave's n-tiles (kRegisters: several n-tiles share them, or
+        // few rows), or are staged per wave in LDS (kResident: one n-tile and
+        // 8 or more rows, where registers would carry 16 rows of padding
+        // through the load path). With K = 14336: 14 k-tiles per wave, one
+        // n-tile, activations in LDS for up to 4 rows (the slices of the 8
+        // waves must fit the 160 KB of LDS). Otherwise the streamed variant.
+        const int64_t m = M < 1 ? 1 : (M > 16 ? 16 : M);
+        const int nb = g.Kg == 1 || g.Ge >= 128 ? 1 : (int)(128 / g.Ge);  // fold blocks per k-tile
+        if (KTT <= 32 && p.nn_max <= (nb < 4 ? 4 : 2)) {
+            p.mode = (p.nn_max >= 2 || m < 8) ? SkinnyPlan::kRegisters : SkinnyPlan::kResident;
+            p.ktw = kResMaxKt;
+        } else if (KTT == 112 && p.nn_max == 1 && m <= 4) {
+            p.mode = SkinnyPlan::kResident;
+            p.ktw = 14;
+        } else {
+            p.mode = SkinnyPlan::kStreamed;
+            p.ktw = (int)((KTT + kStreamWaves - 1) / kStreamWaves);
+        }
         p.ksplit = 1;
         return p;
     }
@@ -598,14 +854,15 @@ hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* pack
     a.n_groups = p.n_groups;
     const int64_t nblocks = p.n_groups * p.ksplit;
     a.xcd_map = !p.full_k && (nblocks % 8 == 0) && ((nblocks / 8) % p.ksplit == 0);
+    a.a_bytes = (uint32_t)(((M - 1) * lda + g.K) * 2);
     a.mask = 0x000F000Fu;
     a.magic = dtype == 0 ? 0x64006400u : 0x43004300u;
     const int spt = g.Kg == 1 ? 1 : (g.Ge >= 128 ? 1 : 128 / g.Ge);
     const dim3 grid((unsigned)nblocks);
     if (p.full_k) {
         hipError_t e;
-        if (dtype == 0) e = g.qtype ? launch_persist_q<0, 1>(a, p, spt, stream) : launch_persist_q<0, 0>(a, p, spt, stream);
-        else e = g.qtype ? launch_persist_q<1, 1>(a, p, spt, stream) : launch_persist_q<1, 0>(a, p, spt, stream);
+        if (dtype == 0) e = g.qtype ? launch_stream_q<0, 1>(a, p, spt, stream) : launch_stream_q<0, 0>(a, p, spt, stream);
+        else e = g.qtype ? launch_stream_q<1, 1>(a, p, spt, stream) : launch_stream_q<1, 0>(a, p, spt, stream);
         return e != hipSuccess ? e : hipGetLastError();
     }
     if (dtype == 0) {

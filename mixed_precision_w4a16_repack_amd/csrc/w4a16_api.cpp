@@ -212,7 +212,13 @@ w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packe
         return W4A16_OK;
     }
 
-    const SkinnyPlan p = plan_skinny(M < 16 ? M : 16, g);
+    // The skinny kernels address the activation rows of one launch (at most
+    // 16) with 32-bit byte offsets.
+    const int64_t rows = M < 16 ? M : 16;
+    if (((rows - 1) * lda + K) * 2 > (int64_t)INT32_MAX)
+        return fail(W4A16_ERR_UNSUPPORTED, "lda=%lld is too large for the skinny path: need ((M-1)*lda + K)*2 < 2^31",
+                    (long long)lda);
+    const SkinnyPlan p = plan_skinny(rows, g);
     if (p.n_groups * (int64_t)sizeof(uint32_t) > (int64_t)kCounterRegionBytes)
         return fail(W4A16_ERR_UNSUPPORTED, "N=%lld needs more split-K counters than the workspace holds", (long long)N);
     const size_t need = skinny_workspace(p);

@@ -287,3 +287,50 @@ def test_skinny_k_extremes(K):
     packed = repack(case)
     C = w4.gemm(case.A.to(DEV), packed, N, K, G, UINT4, path=SKINNY)
     assert oracle.rel_err(C.cpu(), oracle_ref(case)) <= oracle.TOLERANCE["bf16"]
+
+
+# Full-K skinny kernels (N >= 3072): activations in registers or staged in
+# LDS, all weight tiles of a wave in registers, or a streamed ring. Each case
+# names the variant and edge it reaches.
+FULL_K = [
+    # (N, K, M, G, qtype, dtype, bias)
+    (4096, 128, 16, 128, UINT4B8, "f16", True),   # one k-tile, one wave, LDS activations
+    (4096, 384, 3, 64, UINT4, "bf16", False),     # one wave with 3 k-tiles, register activations
+    (4096, 640, 9, 32, UINT4, "f16", True),       # two waves (4 and 1 k-tiles), a scale per word
+    (4112, 1024, 5, 128, UINT4B8, "bf16", False), # 257 n-tiles: 2 per workgroup, the last has 1
+    (14416, 512, 2, 64, UINT4, "f16", True),      # 901 n-tiles: 4 per workgroup, ragged last ones
+    (14336, 4096, 2, 64, UINT4, "f16", False),    # 4 n-tiles per workgroup with zeros, 2 fold blocks
+    (4096, 4224, 16, 128, UINT4B8, "f16", False), # 33 k-tiles: streamed, a wave with no k-tile
+    (3072, 14336, 3, 128, UINT4, "bf16", True),   # 14 k-tiles per wave, LDS activations
+    (4096, 16384, 12, -1, UINT4B8, "f16", False), # streamed, one group per row
+    (6144, 4096, 16, 32, UINT4, "bf16", True),    # 2 n-tiles per workgroup, a scale per word
+]
+
+
+@pytest.mark.parametrize("N,K,M,G,qtype,dtype,bias", FULL_K,
+                         ids=[f"N{c[0]}-K{c[1]}-M{c[2]}-G{c[3]}-q{c[4]}-{c[5]}" for c in FULL_K])
+def test_full_k_variants(N, K, M, G, qtype, dtype, bias):
+    print(f"[case] full-K N={N} K={K} M={M} G={G} qtype={qtype} {dtype} bias={bias}", flush=True)
+    case = _case(24, M, N, K, G, qtype, dtype, with_bias=bias)
+    packed = repack(case)
+    _, _, _, A, b = to_dev(case)
+    C = w4.gemm(A, packed, N, K, G, qtype, bias=b, path=SKINNY)
+    assert oracle.rel_err(C.cpu(), oracle_ref(case)) <= oracle.TOLERANCE[dtype]
+
+
+@pytest.mark.parametrize("N,dtype,qtype,G", [(4096, "f16", UINT4B8, 128), (4096, "bf16", UINT4, 32),
+                                             (14336, "f16", UINT4, 64)])
+def test_identity_through_full_k(N, dtype, qtype, G):
+    # A = I_128 over 16-row slices of the full-K skinny kernels (one n-tile per
+    # workgroup with LDS activations; four with register activations):
+    # bit-exact RN_act((q - z) * s), as in the identity test above.
+    K = 128
+    print(f"[case] identity full-K N={N} {dtype} G={G}", flush=True)
+    case = _case(25, 1, N, K, G, qtype, dtype)
+    packed = repack(case)
+    A = torch.eye(K, dtype=case.torch_dtype, device=DEV)
+    C = w4.gemm(A, packed, N, K, G, qtype, path=SKINNY)
+    W = oracle.dequant(case.weight_packed, case.weight_scale, case.weight_zero_point, qtype, G)
+    expect = torch.from_numpy(W.T.copy()).to(case.torch_dtype)
+    bad = (C.cpu().view(torch.int16) != expect.view(torch.int16)).sum().item()
+    assert bad == 0, f"{bad} of {C.numel()} values differ from RN((q - z) * s)"
