@@ -22,10 +22,11 @@ struct Geometry {
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Skinny launch plan (M <= 16 rows per launch).
-// Full-K variants (mode kRegisters / kResident / kStreamed): n_groups
-// workgroups of up to 8 waves, each owning at most nn_max n-tiles
-// (blockIdx.x + i * n_groups) and all of K; wave w takes k-tiles
-// [w * ktw, (w + 1) * ktw).
+// Wide-weight variants (full_k; mode kRegisters / kResident / kStreamed):
+// n_groups x ksplit workgroups of up to 8 waves; workgroup (g, c) owns at
+// most nn_max n-tiles (g + i * n_groups) and K chunk c (all of K unless
+// kRegisters splits it into chunks of kc_tiles k-tiles); wave w takes
+// k-tiles [w * ktw, (w + 1) * ktw) of its chunk.
 // Split-K variant (mode kSplitK): a workgroup is 4 waves; each wave owns NW
 // consecutive n-tiles (16 rows each) and all KT k-tiles (128 k each) of the
 // workgroup's K range, so the workgroup covers 4*NW n-tiles x KT k-tiles and
@@ -33,9 +34,10 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct SkinnyPlan {
     enum Mode { kSplitK = 0, kRegisters = 1, kResident = 2, kStreamed = 3 };
     Mode mode = kSplitK;
-    bool full_k = false;  // mode != kSplitK: K not split across workgroups
+    bool full_k = false;  // mode != kSplitK: one of the wide-weight variants
     int nn_max = 1;       // full-K: n-tiles per workgroup, at most
     int ktw = 1;          // full-K: k-tiles per wave
+    int kc_tiles = 0;     // kRegisters with ksplit > 1: k-tiles per K chunk
     int NW = 2;
     int KT = 4;
     int ksplit = 1;

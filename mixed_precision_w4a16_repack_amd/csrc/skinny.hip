@@ -56,6 +56,9 @@ struct SkinnyArgs {
     int xcd_map;
     uint32_t mask, magic;  // dequant operands, kept in registers (see Dequant)
     uint32_t a_bytes;      // bytes from A to the end of row M-1: ((M-1)*lda + K)*2 < 2^31
+    int kc_tiles;          // split register variant: k-tiles per K chunk
+    int nn_max;            // full-K variants: n-tiles per workgroup, at most
+    uint32_t codes_bytes, scales_bytes, zeros_bytes;  // region sizes (< 2^31 on the full-K paths)
 };
 
 // Cross-workgroup exchange of split-K partial sums. Every access carries the
@@ -340,12 +343,23 @@ struct ActRows {
     }
 };
 
+// One descriptor per region of the packed weight (codes, scales, zeros);
+// a unit that does not exist reads at offset 2^31, past every region.
+struct WeightBufs {
+    __amdgpu_buffer_rsrc_t codes, scales, zeros;
+    __device__ explicit WeightBufs(const SkinnyArgs& a)
+        : codes(make_rsrc(a.codes, a.codes_bytes)),
+          scales(make_rsrc(a.scales, a.scales_bytes)),
+          zeros(make_rsrc(a.zeros, a.zeros_bytes)) {}
+};
+constexpr uint32_t kNoUnit = 0x80000000u;
+
 // Weight tile (nt, kt) (1 KB, one 16-byte word group per lane), streamed
 // once: nontemporal.
-__device__ __forceinline__ u32x4 load_tile(const SkinnyArgs& a, int64_t nt, int64_t kt, int lane, bool valid) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.codes + (valid ? nt : 0) * a.KTT * 64,
-                                                valid ? (uint32_t)(a.KTT * 1024) : 0u);
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((kt * 64 + lane) * 16), 0, 2));
+__device__ __forceinline__ u32x4 load_tile(const WeightBufs& wb, const SkinnyArgs& a, int64_t nt, int64_t kt,
+                                           int lane, bool valid) {
+    const uint32_t off = valid ? (uint32_t)(((nt * a.KTT + kt) * 64 + lane) * 16) : kNoUnit;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wb.codes, off, 0, 2));
 }
 
 // Scale (and zero) of row 16*nt + r for the fold block that starts at
@@ -356,16 +370,11 @@ __device__ __forceinline__ uint32_t group_of(const SkinnyArgs& a, int64_t kt, in
     return a.one_group ? 0u : (uint32_t)(k >> a.gshift);
 }
 template <int QT, int FW>
-__device__ __forceinline__ void load_scale_zero(const SkinnyArgs& a, int64_t nt, int64_t kt, int f, int r, bool valid,
-                                                uint16_t& sb, uint8_t& zb) {
-    const uint32_t g = group_of<FW>(a, kt, f);
-    const int64_t base = (valid ? nt : 0) * a.Kg * 16;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + base, valid ? (uint32_t)(a.Kg * 32) : 0u);
-    sb = __builtin_amdgcn_raw_buffer_load_b16(rs, (g * 16 + r) * 2, 0, 0);
-    if (QT) {
-        const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.zeros + base, valid ? (uint32_t)(a.Kg * 16) : 0u);
-        zb = __builtin_amdgcn_raw_buffer_load_b8(rz, g * 16 + r, 0, 0);
-    }
+__device__ __forceinline__ void load_scale_zero(const WeightBufs& wb, const SkinnyArgs& a, int64_t nt, int64_t kt,
+                                                int f, int r, bool valid, uint16_t& sb, uint8_t& zb) {
+    const uint32_t idx = (uint32_t)((nt * a.Kg + group_of<FW>(a, kt, f)) * 16 + r);
+    sb = __builtin_amdgcn_raw_buffer_load_b16(wb.scales, valid ? idx * 2 : kNoUnit, 0, 0);
+    if (QT) zb = __builtin_amdgcn_raw_buffer_load_b8(wb.zeros, valid ? idx : kNoUnit, 0, 0);
 }
 
 // B operand of exact magic values m + q for the 8 codes of word wv.
@@ -392,14 +401,15 @@ __device__ __forceinline__ void fold(floatx4& acc, const floatx4& P, const float
 // of the workgroup's nw waves sums them, in wave order, for n-tiles q,
 // q + nw, ..., adds the bias, rounds once and stores rows < M.
 template <int DT>
-__device__ __forceinline__ void finish_tiles(const SkinnyArgs& a, const floatx4* red, int nn, int nwa) {
+__device__ __forceinline__ void finish_tiles(const SkinnyArgs& a, const floatx4* red, int nn, int nwa, int64_t g,
+                                             int64_t groups) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g4 = lane >> 4;
     const int nw = blockDim.x >> 6;  // short K: fewer than 8 waves
     for (int i = wave; i < nn; i += nw) {
         floatx4 tot = red[(0 * nn + i) * 64 + lane];
         for (int q = 1; q < nwa; ++q) tot += red[(q * nn + i) * 64 + lane];
-        const int64_t n = (blockIdx.x + (int64_t)i * gridDim.x) * 16 + r;
+        const int64_t n = (g + (int64_t)i * groups) * 16 + r;
         const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -407,6 +417,73 @@ __device__ __forceinline__ void finish_tiles(const SkinnyArgs& a, const floatx4*
             if (m < a.M) a.C[(int64_t)m * a.ldc + n] = to_act_bits<DT>(tot[jj] + bv);
         }
     }
+}
+
+// Split K across ksplit workgroups per n-group g (chunk c of K each): the
+// workgroup's wave-summed tile of each of its n-tiles goes to the workspace
+// with write-through stores; the last workgroup of the n-group to arrive
+// (agent-scope counter, as in skinny_kernel) reads the ksplit partials back
+// with coherent loads and sums them in chunk order, so the result does not
+// depend on which one arrives last. Partial (g, c, i): 64 lanes x 16 bytes.
+template <int DT>
+__device__ __forceinline__ void finish_split(const SkinnyArgs& a, const floatx4* red, int* flag, int nn, int nwa,
+                                             int64_t g, int c) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g4 = lane >> 4;
+    const int nw = blockDim.x >> 6;
+    float* part = a.partials + g * a.ksplit * (int64_t)a.nn_max * 256;
+    for (int i = wave; i < nn; i += nw) {
+        floatx4 tot = red[(0 * nn + i) * 64 + lane];
+        for (int q = 1; q < nwa; ++q) tot += red[(q * nn + i) * 64 + lane];
+        store_coherent(part + (((int64_t)c * a.nn_max + i) * 64 + lane) * 4, tot);
+    }
+    wait_vector_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.counters + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = prev == (uint32_t)(a.ksplit - 1);
+    }
+    __syncthreads();
+    if (!*flag) return;
+    for (int i = wave; i < nn; i += nw) {
+        floatx4 tot = {0.f, 0.f, 0.f, 0.f};
+        for (int q0 = 0; q0 < a.ksplit; q0 += 4) {
+            const float* src[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int q = q0 + b < a.ksplit ? q0 + b : q0;
+                src[b] = part + (((int64_t)q * a.nn_max + i) * 64 + lane) * 4;
+            }
+            floatx4 v[4];
+            load_coherent4(src[0], src[1], src[2], src[3], v[0], v[1], v[2], v[3]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (q0 + b < a.ksplit) tot += v[b];
+        }
+        const int64_t n = (g + (int64_t)i * a.n_groups) * 16 + r;
+        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int m = 4 * g4 + jj;
+            if (m < a.M) a.C[(int64_t)m * a.ldc + n] = to_act_bits<DT>(tot[jj] + bv);
+        }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.counters + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS row stride (halves) of a wave's activation slice of KTW k-tiles: 16
+// bytes of padding per row spread the rows over the LDS banks.
+template <int KTW>
+constexpr int act_lds_ld() { return KTW * 128 + 8; }
+
+// Fold without the zero term: acc += s * P, for P accumulated on top of
+// -(m + z) * S (uint4b8: z = 8, the same for every n-tile, so that start
+// value is computed once per fold block and shared).
+template <int DT>
+__device__ __forceinline__ void fold_scaled(floatx4& acc, const floatx4& P, uint16_t sbits) {
+    const float sf = act_to_float<DT>(sbits);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(sf, P[jj], acc[jj]);
 }
 
 template <int DT, int QT, int FW, int NNM>
@@ -419,9 +496,15 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
     const int nwaves = blockDim.x >> 6;
     const int r = lane & 15, g4 = lane >> 4;
-    const int nn = (int)((a.NT - blockIdx.x + gridDim.x - 1) / gridDim.x);
-    const int64_t kt0 = (int64_t)wave * KTM;
-    const int kc = (int)(a.KTT - kt0 < KTM ? a.KTT - kt0 : KTM);  // >= 1
+    // Workgroup (K chunk c = blockIdx.x, n-group g = blockIdx.y): n-tiles
+    // g + i * n_groups, k-tiles [c * kc_tiles, +kc_tiles) (all of K when
+    // ksplit == 1).
+    const int c = blockIdx.x;
+    const int64_t g = blockIdx.y;
+    const int nn = (int)((a.NT - g + a.n_groups - 1) / a.n_groups);
+    const int64_t kt0 = (int64_t)c * a.kc_tiles + (int64_t)wave * KTM;
+    const int64_t kend = (int64_t)(c + 1) * a.kc_tiles < a.KTT ? (int64_t)(c + 1) * a.kc_tiles : a.KTT;
+    const int kc = kt0 >= kend ? 0 : (int)(kend - kt0 < KTM ? kend - kt0 : KTM);
 
     uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
@@ -429,6 +512,7 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
     // 1. Activation fragments: lane (r, g4) of word s of k-tile j holds
     //    A[r][128*(kt0+j) + 32*s + 8*g4 .. +7] (zeros for rows r >= M).
     const ActRows act(a, r, g4);
+    const WeightBufs wb(a);
     u32x4 af[KTM][4];
 #pragma unroll
     for (int j = 0; j < KTM; ++j) {
@@ -442,13 +526,13 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
     uint8_t zb[NNM][KTM][NB];
 #pragma unroll
     for (int i = 0; i < NNM; ++i) {
-        const int64_t nt = blockIdx.x + (int64_t)i * gridDim.x;
+        const int64_t nt = g + (int64_t)i * a.n_groups;
 #pragma unroll
         for (int j = 0; j < KTM; ++j) {
             const bool valid = i < nn && j < kc;
-            w[i][j] = load_tile(a, nt, kt0 + j, lane, valid);
+            w[i][j] = load_tile(wb, a, nt, kt0 + j, lane, valid);
 #pragma unroll
-            for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(a, nt, kt0 + j, f, r, valid, sb[i][j][f], zb[i][j][f]);
+            for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(wb, a, nt, kt0 + j, f, r, valid, sb[i][j][f], zb[i][j][f]);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -463,6 +547,7 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
             S[j][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ww = 0; ww < FW; ++ww) S[j][f] = mfma16x16x32<DT>(af[j][f * FW + ww], ones, S[j][f]);
+            if (!QT) S[j][f] *= -(magic_base<DT>() + 8.0f);  // uint4b8: the start value T = -(m + 8) * S
         }
     }
 
@@ -476,13 +561,14 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
                 if (j < kc) {
 #pragma unroll
                     for (int f = 0; f < NB; ++f) {
-                        floatx4 P = {0.f, 0.f, 0.f, 0.f};
+                        floatx4 P = QT ? floatx4{0.f, 0.f, 0.f, 0.f} : S[j][f];
 #pragma unroll
                         for (int ww = 0; ww < FW; ++ww) {
                             const int word = f * FW + ww;
                             P = mfma16x16x32<DT>(af[j][word], magic_operand(w[i][j][word], dq_mask, dq_magic), P);
                         }
-                        fold<DT, QT>(acc, P, S[j][f], sb[i][j][f], QT ? zb[i][j][f] : (uint8_t)8);
+                        if (QT) fold<DT, QT>(acc, P, S[j][f], sb[i][j][f], zb[i][j][f]);
+                        else fold_scaled<DT>(acc, P, sb[i][j][f]);
                     }
                 }
             }
@@ -490,13 +576,9 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
         }
     }
     __syncthreads();
-    finish_tiles<DT>(a, red, nn, nwaves);
+    if (a.ksplit == 1) finish_tiles<DT>(a, red, nn, nwaves, g, a.n_groups);
+    else finish_split<DT>(a, red, reinterpret_cast<int*>(red + kStreamWaves * a.nn_max * 64), nn, nwaves, g, c);
 }
-
-// LDS row stride (halves) of a wave's activation slice of KTW k-tiles: 16
-// bytes of padding per row spread the rows over the LDS banks.
-template <int KTW>
-constexpr int act_lds_ld() { return KTW * 128 + 8; }
 
 template <int DT, int QT, int FW, int NNM, int KTW>
 __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a) {
@@ -535,6 +617,7 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
         if (c < nch && col < ccols)
             ach[t] = *reinterpret_cast<const u32x4*>(a.A + (int64_t)m * a.lda + kt0 * 128 + 8 * col);
     }
+    const WeightBufs wb(a);
     // 2. Every weight tile, scale and zero of the wave, in consumption order
     //    (k-tile outer, n-tile inner). Units past the workgroup's n-tiles or
     //    the wave's k-tiles use zero-size descriptors (see make_rsrc).
@@ -547,9 +630,9 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
         for (int i = 0; i < NNM; ++i) {
             const int64_t nt = blockIdx.x + (int64_t)i * gridDim.x;
             const bool valid = i < nn && j < kc;
-            w[j][i] = load_tile(a, nt, kt0 + j, lane, valid);
+            w[j][i] = load_tile(wb, a, nt, kt0 + j, lane, valid);
 #pragma unroll
-            for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(a, nt, kt0 + j, f, r, valid, sb[j][i][f], zb[j][i][f]);
+            for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(wb, a, nt, kt0 + j, f, r, valid, sb[j][i][f], zb[j][i][f]);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -580,19 +663,21 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
                 S[f] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ww = 0; ww < FW; ++ww) S[f] = mfma16x16x32<DT>(af[f * FW + ww], ones, S[f]);
+                if (!QT) S[f] *= -(magic_base<DT>() + 8.0f);  // uint4b8: the start value T = -(m + 8) * S
             }
 #pragma unroll
             for (int i = 0; i < NNM; ++i) {
                 if (i < nn) {
 #pragma unroll
                     for (int f = 0; f < NB; ++f) {
-                        floatx4 P = {0.f, 0.f, 0.f, 0.f};
+                        floatx4 P = QT ? floatx4{0.f, 0.f, 0.f, 0.f} : S[f];
 #pragma unroll
                         for (int ww = 0; ww < FW; ++ww) {
                             const int word = f * FW + ww;
                             P = mfma16x16x32<DT>(af[word], magic_operand(w[j][i][word], dq_mask, dq_magic), P);
                         }
-                        fold<DT, QT>(acc[i], P, S[f], sb[j][i][f], QT ? zb[j][i][f] : (uint8_t)8);
+                        if (QT) fold<DT, QT>(acc[i], P, S[f], sb[j][i][f], zb[j][i][f]);
+                        else fold_scaled<DT>(acc[i], P, sb[j][i][f]);
                     }
                 }
             }
@@ -606,7 +691,7 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
     for (int i = 0; i < NNM; ++i)
         if (i < nn) red[(wave * nn + i) * 64 + lane] = acc[i];
     __syncthreads();
-    finish_tiles<DT>(a, red, nn, nwaves);
+    finish_tiles<DT>(a, red, nn, nwaves, blockIdx.x, gridDim.x);
 }
 
 template <int DT, int QT, int FW>
@@ -627,6 +712,7 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_str_kernel(SkinnyArgs a
     uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
     const ActRows act(a, r, g4);
+    const WeightBufs wb(a);
 
     struct Slot {
         u32x4 af[4];
@@ -645,9 +731,9 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_str_kernel(SkinnyArgs a
         const int64_t kt = kt0 + pj;
 #pragma unroll
         for (int s = 0; s < 4; ++s) sl.af[s] = act.load(kt, s, valid);
-        sl.w = load_tile(a, nt, kt, lane, valid);
+        sl.w = load_tile(wb, a, nt, kt, lane, valid);
 #pragma unroll
-        for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(a, nt, kt, f, r, valid, sl.sb[f], sl.zb[f]);
+        for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(wb, a, nt, kt, f, r, valid, sl.sb[f], sl.zb[f]);
         if (++pj >= kc) {
             pj = 0;
             ++pi;
@@ -691,13 +777,14 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_str_kernel(SkinnyArgs a
         }
     }
     __syncthreads();
-    finish_tiles<DT>(a, red, nn, nwa < kStreamWaves ? nwa : kStreamWaves);
+    finish_tiles<DT>(a, red, nn, nwa < kStreamWaves ? nwa : kStreamWaves, blockIdx.x, gridDim.x);
 }
 
 template <int DT, int QT, int FW, int NNM>
 hipError_t launch_reg(const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL((skinny_reg_kernel<DT, QT, FW, NNM>), grid, block, lds, stream, a);
-    return hipSuccess;
+    hipError_t e = allow_lds<skinny_reg_kernel<DT, QT, FW, NNM>>(lds);
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_reg_kernel<DT, QT, FW, NNM>), grid, block, lds, stream, a);
+    return e;
 }
 
 template <int DT, int QT, int FW, int NNM, int KTW>
@@ -712,26 +799,21 @@ hipError_t launch_stream_fw(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_
     const dim3 grid((unsigned)p.n_groups);
     const size_t lds = (size_t)kStreamWaves * p.nn_max * 64 * sizeof(floatx4);
     if (p.mode == SkinnyPlan::kRegisters) {
-        const dim3 block((unsigned)(64 * ((a.KTT + kResMaxKt - 1) / kResMaxKt)));
+        const dim3 rgrid((unsigned)p.ksplit, (unsigned)p.n_groups);
+        const dim3 block((unsigned)(64 * ((p.kc_tiles + kResMaxKt - 1) / kResMaxKt)));
+        const size_t rlds = lds + 16;  // + the last-arrival flag of a split
         hipError_t e = hipSuccess;
-        if (p.nn_max == 1) e = launch_reg<DT, QT, FW, 1>(a, grid, block, lds, stream);
-        else if (p.nn_max == 2 || FW == 1) e = launch_reg<DT, QT, FW, 2>(a, grid, block, lds, stream);
-        else e = launch_reg<DT, QT, FW, (FW == 1 ? 2 : 4)>(a, grid, block, lds, stream);
+        if (p.nn_max == 1) e = launch_reg<DT, QT, FW, 1>(a, rgrid, block, rlds, stream);
+        else if (p.nn_max == 2 || FW == 1) e = launch_reg<DT, QT, FW, 2>(a, rgrid, block, rlds, stream);
+        else e = launch_reg<DT, QT, FW, (FW == 1 ? 2 : 4)>(a, rgrid, block, rlds, stream);
         return e;
     }
     if (p.mode == SkinnyPlan::kResident) {
         const dim3 block((unsigned)(64 * ((a.KTT + p.ktw - 1) / p.ktw)));
         const size_t lds_a = (size_t)kStreamWaves * a.M * p.ktw * 128 * 2 + (size_t)kStreamWaves * a.M * 16;
         const size_t lds_r = lds > lds_a ? lds : lds_a;
-        hipError_t e = hipSuccess;
-        // Instantiated shapes (n-tiles per workgroup x k-tiles per wave); the
-        // planner only picks these.
-        // (FW == 1, a scale per word, only with up to 2 n-tiles.)
-        if (p.ktw == 4 && p.nn_max == 1) e = launch_res<DT, QT, FW, 1, 4>(a, grid, block, lds_r, stream);
-        else if (p.ktw == 4 && (p.nn_max == 2 || FW == 1)) e = launch_res<DT, QT, FW, 2, 4>(a, grid, block, lds_r, stream);
-        else if (p.ktw == 4) e = launch_res<DT, QT, FW, (FW == 1 ? 2 : 4), 4>(a, grid, block, lds_r, stream);
-        else e = launch_res<DT, QT, FW, 1, 14>(a, grid, block, lds_r, stream);
-        return e;
+        // The planner picks this variant for one n-tile per workgroup only.
+        return launch_res<DT, QT, FW, 1, 4>(a, grid, block, lds_r, stream);
     }
     hipError_t e = allow_lds<skinny_str_kernel<DT, QT, FW>>(lds);
     if (e == hipSuccess)
@@ -781,34 +863,54 @@ void launch_skinny_q(const SkinnyArgs& a, const SkinnyPlan& p, int spt, dim3 gri
 SkinnyPlan plan_skinny(int64_t M, const Geometry& g) {
     SkinnyPlan p;  // the workspace is sized for 16 rows, so one serves every M <= 16
     const int64_t NT = g.N / 16, KTT = g.K / 128;
-    if (NT >= kFullKMinTiles) {
-        // Full K: one workgroup per CU while N allows, n-tiles spread evenly.
+    // The wide-weight variants address each region of the packed weight with
+    // 32-bit offsets below 2^31 (codes N*K/2 bytes, the largest).
+    if (NT >= kFullKMinTiles && g.codes_bytes < ((size_t)1 << 31)) {
+        // Wide weights: one workgroup per CU while N allows, n-tiles spread
+        // evenly.
         p.full_k = true;
+        p.ksplit = 1;
         const int64_t per = (NT + kCUs - 1) / kCUs;
         p.nn_max = (int)(per < kMaxTilesPerWG ? per : kMaxTilesPerWG);
         p.n_groups = (NT + p.nn_max - 1) / p.nn_max;
-        // Every weight tile of a wave in registers (at most 16): with K <=
-        // 4096, 4 k-tiles per wave (ceil(KTT / 4) <= 8 waves) and up to 4
-        // n-tiles. The activation fragments either stay in registers for all
+        p.kc_tiles = (int)KTT;
+        // Every weight tile of a wave in registers (at most 16): 4 k-tiles
+        // per wave and up to 4 n-tiles per workgroup (2 with a scale per
+        // word). The activation fragments either stay in registers for all
         // of the wave's n-tiles (kRegisters: several n-tiles share them, or
         // few rows), or are staged per wave in LDS (kResident: one n-tile and
         // 8 or more rows, where registers would carry 16 rows of padding
-        // through the load path). With K = 14336: 14 k-tiles per wave, one
-        // n-tile, activations in LDS for up to 4 rows (the slices of the 8
-        // waves must fit the 160 KB of LDS). Otherwise the streamed variant.
+        // through the load path). With K > 4096, K is split into chunks of
+        // at most 32 k-tiles (8 waves) and the n-groups shrink so that the
+        // chunks of all n-groups still make about one workgroup per CU; the
+        // chunk partials meet in the workspace. Otherwise the streamed
+        // variant.
         const int64_t m = M < 1 ? 1 : (M > 16 ? 16 : M);
         const int nb = g.Kg == 1 || g.Ge >= 128 ? 1 : (int)(128 / g.Ge);  // fold blocks per k-tile
-        if (KTT <= 32 && p.nn_max <= (nb < 4 ? 4 : 2)) {
+        const int nn_cap = nb < 4 ? 4 : 2;
+        if (KTT <= 32 && p.nn_max <= nn_cap) {
             p.mode = (p.nn_max >= 2 || m < 8) ? SkinnyPlan::kRegisters : SkinnyPlan::kResident;
             p.ktw = kResMaxKt;
-        } else if (KTT == 112 && p.nn_max == 1 && m <= 4) {
-            p.mode = SkinnyPlan::kResident;
-            p.ktw = 14;
-        } else {
-            p.mode = SkinnyPlan::kStreamed;
-            p.ktw = (int)((KTT + kStreamWaves - 1) / kStreamWaves);
+            return p;
         }
-        p.ksplit = 1;
+        int64_t ks = (KTT + 31) / 32;
+        const int64_t kc = ((KTT + ks - 1) / ks + kResMaxKt - 1) / kResMaxKt * kResMaxKt;
+        ks = (KTT + kc - 1) / kc;
+        const int64_t groups = kCUs / ks > 1 ? kCUs / ks : 1;
+        const int64_t nnm = (NT + groups - 1) / groups;
+        if (nnm <= nn_cap) {
+            p.mode = SkinnyPlan::kRegisters;
+            p.ktw = kResMaxKt;
+            p.ksplit = (int)ks;
+            p.kc_tiles = (int)kc;
+            p.nn_max = (int)nnm;
+            p.n_groups = (NT + nnm - 1) / nnm;
+            p.partial_bytes = (size_t)p.n_groups * p.ksplit * p.nn_max * 64 * sizeof(floatx4);
+            p.counter_bytes = (size_t)p.n_groups * sizeof(uint32_t);
+            return p;
+        }
+        p.mode = SkinnyPlan::kStreamed;
+        p.ktw = (int)((KTT + kStreamWaves - 1) / kStreamWaves);
         return p;
     }
     // Few n-tiles: split K across workgroups so the grid still covers the
@@ -855,6 +957,11 @@ hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* pack
     const int64_t nblocks = p.n_groups * p.ksplit;
     a.xcd_map = !p.full_k && (nblocks % 8 == 0) && ((nblocks / 8) % p.ksplit == 0);
     a.a_bytes = (uint32_t)(((M - 1) * lda + g.K) * 2);
+    a.kc_tiles = p.kc_tiles;
+    a.nn_max = p.nn_max;
+    a.codes_bytes = (uint32_t)g.codes_bytes;  // the full-K paths need all three < 2^31
+    a.scales_bytes = (uint32_t)(g.N * g.Kg * 2);
+    a.zeros_bytes = g.qtype == 1 ? (uint32_t)(g.N * g.Kg) : 0u;
     a.mask = 0x000F000Fu;
     a.magic = dtype == 0 ? 0x64006400u : 0x43004300u;
     const int spt = g.Kg == 1 ? 1 : (g.Ge >= 128 ? 1 : 128 / g.Ge);
