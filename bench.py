@@ -352,7 +352,7 @@ def main():
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         },
         "roofline": {
-            "kernel": "skinny decode GEMM (skinny_persist_kernel at these shapes)",
+            "kernel": "skinny decode GEMM (wide-weight register, LDS and split-K variants)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
