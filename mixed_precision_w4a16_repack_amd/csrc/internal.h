@@ -48,8 +48,9 @@ struct SkinnyPlan {
 
 // Tiled MFMA launch plan.
 struct MfmaPlan {
-    int BM = 256;  // rows per workgroup
-    int BN = 256;  // columns per workgroup
+    bool lds = false;  // activation tile loaded straight into LDS (mfma_lds_kernel)
+    int BM = 256;      // rows per workgroup
+    int BN = 256;      // columns per workgroup
 };
 
 // Raises a kernel's dynamic-LDS limit (needed above 64 KB); cached per kernel

@@ -44,6 +44,7 @@ struct MfmaArgs {
     uint16_t* C;
     int64_t ldc;
     int64_t m_tiles, n_blocks;
+    uint32_t a_bytes, codes_bytes, scales_bytes, zeros_bytes;  // buffer extents (mfma_lds_kernel)
 };
 
 template <int DT, int QT, int BM, int WNT, int SPT>
@@ -189,6 +190,251 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
     }
 }
 
+// 16 bytes per lane from buffer `rs` (lane offset voff + scalar offset soff)
+// straight into LDS at dst + 16 * lane (dst wave-uniform). dst keeps its
+// __shared__ array identity so that the compiler knows which LDS object the
+// load writes (reads of the other buffer then need not wait for it).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, unsigned char* dst, uint32_t voff, uint32_t soff) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, soff, 0, 0);
+}
+
+// Waits until at most N vector memory operations of this wave are
+// outstanding (also the direct-to-LDS loads, which no register tracks).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Tiled variant with the activation tile loaded straight into LDS.
+// A workgroup of 8 waves computes a BM x BN tile of C, the waves in a
+// WM x (8/WM) grid; wave (wm, wn) owns MI = BM/(16*WM) row blocks and NJ
+// n-tiles (BN = (8/WM) * NJ * 16), so it holds MI*NJ accumulators of 16x16.
+// K advances in steps of KS k-tiles (128 k each). Per step, the BM x 128*KS
+// activation tile goes from HBM/L2 to LDS with direct 16-byte buffer loads
+// (no registers), in MFMA fragment order (1 KB per 16 x 32 block, lane l's
+// 16 bytes at 16*l: conflict-free ds_read_b128), double-buffered: step t+1
+// is in flight while step t is multiplied. Each wave streams its NJ x KS
+// weight tiles (one 16-byte load per lane each, already in B-operand
+// order), dequantises each word once, scale first as the pages do, and
+// reuses it for its MI row blocks. One barrier per step. Small tiles use
+// KS = 2 or 4 so that each step carries enough loads to cover the memory
+// latency.
+// All loads go through buffer descriptors whose per-wave part of the offset
+// is scalar, which keeps the vector registers for the accumulators (A, the
+// codes and the scales each below 2^31 bytes).
+template <int DT, int QT, int SPT, int BM, int WM, int NJ, int KS, bool OC>
+__global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
+    constexpr int WN = 8 / WM;
+    constexpr int MI = BM / (16 * WM);
+    constexpr int BN = WN * NJ * 16;
+    constexpr int NBLK = BM / 16 * 4 * KS;  // 1 KB fragment blocks per step
+    constexpr int BPW = NBLK / 8;           // blocks staged per wave
+    constexpr int BUF = NBLK * 1024;        // bytes of one LDS buffer
+    // Weight loads per wave per step (with OC the scales and zeros are
+    // loaded once, before the K loop).
+    constexpr int NB_LOADS = NJ * KS * (OC ? 1 : 1 + SPT * (1 + QT));
+    static_assert(BPW >= 1, "at least one block per wave");
+    // Two separate LDS objects (not one array) for the two activation
+    // buffers: the loads into one and the reads of the other then need not
+    // wait for each other.
+    __shared__ __attribute__((aligned(1024))) unsigned char abuf0[BUF];
+    __shared__ __attribute__((aligned(1024))) unsigned char abuf1[BUF];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave - wm * WN;
+    const int r = lane & 15, g4 = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int64_t NT = a.N / 16;
+    const int64_t steps = (a.KTT + KS - 1) / KS;
+
+    // Descriptors of A and of the packed weight; with live == false they
+    // have size 0, so loads past K or after the last step read zeros without
+    // a memory access and every step issues the same loads (a conditional
+    // load would make the compiler's counter waits pessimistic).
+    auto rsrc = [&](const void* base, uint32_t bytes, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
+    };
+
+    // Activation blocks this wave stages: block b = wave*BPW + t is row
+    // block rb = b / (4*KS), k-tile kk = (b / 4) % KS, word s = b % 4 of the
+    // step: rows m0 + 16*rb + (0..15), k 128*kk + 32*s + (0..31). Lane l
+    // loads row 16*rb + l%16 (clamped to M-1) at k offset 8*(l/16).
+    uint32_t a_off[BPW];
+#pragma unroll
+    for (int t = 0; t < BPW; ++t) {
+        const int b = wave * BPW + t;
+        int64_t row = m0 + 16 * (b / (4 * KS)) + r;
+        if (row > a.M - 1) row = a.M - 1;
+        a_off[t] = (uint32_t)((row * a.lda + 8 * g4) * 2);
+    }
+    auto stage_a = [&](int64_t st, int buf, bool live) {
+#pragma unroll
+        for (int t = 0; t < BPW; ++t) {
+            const int b = wave * BPW + t;
+            const int kk = (b / 4) % KS, s = b % 4;
+            const int64_t kt = st * KS + kk;
+            const __amdgpu_buffer_rsrc_t rs_a = rsrc(a.A, a.a_bytes, live && kt < a.KTT);
+            load_lds16(rs_a, (buf ? abuf1 : abuf0) + b * 1024, a_off[t], (uint32_t)((kt * 128 + 32 * s) * 2));
+        }
+    };
+
+    // This wave's n-tiles (clamped for loads past N; never stored).
+    const int64_t nt0 = (int64_t)blockIdx.x * (BN / 16) + wn * NJ;
+    auto nt_ld = [&](int j) { return nt0 + j < NT ? nt0 + j : NT - 1; };
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    // Scales and zeros stay one per 32-bit register: packing two freshly
+    // loaded 16-bit values would make the step wait for loads just issued.
+    u32x4 raw0[NJ][KS], raw1[NJ][KS];
+    uint32_t sb0[NJ][KS][SPT], sb1[NJ][KS][SPT];
+    uint32_t zb0[NJ][KS][SPT], zb1[NJ][KS][SPT];
+    auto load_b = [&](int64_t st, u32x4 (&raw)[NJ][KS], uint32_t (&sb)[NJ][KS][SPT], uint32_t (&zb)[NJ][KS][SPT],
+                      bool live) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int64_t kt = st * KS + kk;
+            const bool ok = live && kt < a.KTT;
+            const __amdgpu_buffer_rsrc_t rs_c = rsrc(a.codes, a.codes_bytes, ok);
+            const __amdgpu_buffer_rsrc_t rs_s = rsrc(a.scales, a.scales_bytes, ok);
+            const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.zeros, a.zeros_bytes, ok);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int64_t nt = nt_ld(j);
+                raw[j][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           rs_c, lane16, (uint32_t)((nt * a.KTT + kt) * 1024), 2));
+#pragma unroll
+                for (int u = 0; u < SPT && !OC; ++u) {
+                    const int64_t k = kt * 128 + u * (128 / SPT);
+                    const int64_t g = a.one_group ? 0 : (k >> a.gshift);
+                    const uint32_t so = (uint32_t)((nt * a.Kg + g) * 16);
+                    sb[j][kk][u] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)r * 2, so * 2, 0);
+                    if (QT) zb[j][kk][u] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, (uint32_t)r, so, 0);
+                }
+            }
+        }
+    };
+
+    uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
+    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
+
+    floatx4 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // OC (one group per row): offset-corrected dequantisation, as in the
+    // skinny kernels. The B operand is the exact magic value m + q (one
+    // v_and_or_b32 per pair of codes), acc sums A*(m + q) over all of K, S
+    // sums A over K (one MFMA against an all-ones B per activation
+    // fragment, shared by the NJ n-tiles), and the epilogue applies
+    // C = s * (acc - (m + z) * S): the scale multiplies an exact-integer-
+    // weight sum once instead of every weight.
+    floatx4 S[OC ? MI : 1];
+#pragma unroll
+    for (int i = 0; i < (OC ? MI : 1); ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
+    const u32x4 ones = {one2, one2, one2, one2};
+
+    // One step on LDS buffer `buf` with the weights in (raw, sb, zb); the
+    // next step's activation tile and weights are requested first.
+    auto step = [&](int64_t st, int buf, const u32x4 (&raw)[NJ][KS], const uint32_t (&sb)[NJ][KS][SPT],
+                    const uint32_t (&zb)[NJ][KS][SPT], u32x4 (&nraw)[NJ][KS], uint32_t (&nsb)[NJ][KS][SPT],
+                    uint32_t (&nzb)[NJ][KS][SPT]) {
+        const bool more = st + 1 < steps;
+        stage_a(st + 1, buf ^ 1, more);
+        load_b(st + 1, nraw, nsb, nzb, more);
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned char* abase = (buf ? abuf1 : abuf0) + lane * 16;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                u32x4 bq[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    if (OC) {
+                        const uint32_t w = raw[j][kk][s];
+                        bq[j] = u32x4{and_or(w, dq_mask, dq_magic), and_or(w >> 4, dq_mask, dq_magic),
+                                      and_or(w >> 8, dq_mask, dq_magic), and_or(w >> 12, dq_mask, dq_magic)};
+                    } else {
+                        const int u = s / (4 / SPT);
+                        bq[j] = Dequant<DT>::apply(
+                            raw[j][kk][s], Dequant<DT>::make((uint16_t)sb[j][kk][u], QT ? (int)zb[j][kk][u] : 8),
+                            dq_mask, dq_magic);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    const int blk = ((wm * MI + i) * KS + kk) * 4 + s;
+                    const u32x4 av = *reinterpret_cast<const u32x4*>(abase + blk * 1024);
+                    if (OC) S[i] = mfma16x16x32<DT>(av, ones, S[i]);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32<DT>(av, bq[j], acc[i][j]);
+                }
+            }
+        }
+        // The next activation tile has landed once only the weight loads
+        // issued after it may be outstanding; then every wave is done with
+        // this buffer and sees the next one.
+        wait_vmcnt<NB_LOADS>();
+        __syncthreads();
+    };
+
+    stage_a(0, 0, true);
+    load_b(0, raw0, sb0, zb0, true);
+    wait_vmcnt<NB_LOADS>();
+    __syncthreads();
+    int64_t st = 0;
+    for (; st + 1 < steps; st += 2) {
+        step(st, 0, raw0, sb0, zb0, raw1, sb1, zb1);
+        step(st + 1, 1, raw1, sb1, zb1, raw0, sb0, zb0);
+    }
+    if (st < steps) step(st, 0, raw0, sb0, zb0, raw1, sb1, zb1);
+
+    // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l%16 of each block.
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if (nt0 + j >= NT) continue;
+        const int64_t n = (nt0 + j) * 16 + r;
+        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+        float sf = 1.f, zf = 0.f;
+        if (OC) {  // the row's only scale and zero
+            sf = act_to_float<DT>(a.scales[n]);
+            zf = -((DT == 0 ? 1024.0f : 128.0f) + (QT ? (float)a.zeros[n] : 8.0f));
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int64_t m = m0 + wm * (BM / WM) + 16 * i + 4 * g4 + jj;
+                float v = acc[i][j][jj];
+                if (OC) v = sf * __builtin_fmaf(zf, S[OC ? i : 0][jj], v);
+                if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
+            }
+        }
+    }
+}
+
+template <int DT, int QT, int BM, int WM, int NJ, int KS>
+hipError_t launch_lds_t(const MfmaArgs& a, int spt, hipStream_t stream) {
+    constexpr int BN = (8 / WM) * NJ * 16;
+    const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
+    // Static LDS: two activation buffers of BM x 128*KS. One group per row:
+    // offset-corrected dequantisation; otherwise scale first.
+    if (a.one_group) {
+        hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, true>), grid, dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
+    switch (spt) {
+        case 1: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, false>), grid, dim3(512), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 2, BM, WM, NJ, KS, false>), grid, dim3(512), 0, stream, a); break;
+        default: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 4, BM, WM, NJ, KS, false>), grid, dim3(512), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+
 template <int DT, int QT, int BM, int WNT>
 hipError_t launch_mfma_t(const MfmaArgs& a, int spt, dim3 grid, hipStream_t stream) {
     const size_t lds = 2 * (size_t)BM * 128 * 2;
@@ -212,6 +458,14 @@ hipError_t launch_mfma_t(const MfmaArgs& a, int spt, dim3 grid, hipStream_t stre
 
 template <int DT, int QT>
 hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, dim3 grid, hipStream_t stream) {
+    if (p.lds && ((a.M - 1) * a.lda + a.KTT * 128) * 2 < ((int64_t)1 << 31)) {
+        if (p.BN == 256) return launch_lds_t<DT, QT, 128, 2, 4, 1>(a, spt, stream);
+        switch (p.BM) {  // BN = 64: one n-tile per wave, 2 or 4 k-tiles per step
+            case 32: return launch_lds_t<DT, QT, 32, 2, 1, 4>(a, spt, stream);
+            case 64: return launch_lds_t<DT, QT, 64, 2, 1, 2>(a, spt, stream);
+            default: return launch_lds_t<DT, QT, 128, 2, 1, 2>(a, spt, stream);
+        }
+    }
     if (p.BM == 256) {
         return p.BN == 256 ? launch_mfma_t<DT, QT, 256, 4>(a, spt, grid, stream)
                            : launch_mfma_t<DT, QT, 256, 2>(a, spt, grid, stream);
@@ -224,6 +478,24 @@ hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, dim3 gri
 
 MfmaPlan plan_mfma(int64_t M, const Geometry& g) {
     MfmaPlan p;
+    // The direct-to-LDS variant addresses A and the packed weight with
+    // 32-bit offsets; launch_mfma re-checks A, whose size depends on lda.
+    p.lds = g.codes_bytes < ((size_t)1 << 31);
+    if (p.lds) {
+        // 128 x 256 tiles while they give at least one workgroup per CU;
+        // otherwise 64-column tiles (four times the workgroups) with as few
+        // rows as M needs, so that the weight stream still spreads over the
+        // chip at small and medium M.
+        const int64_t wide = ((M + 127) / 128) * ((g.N + 255) / 256);
+        if (wide >= kCUs) {
+            p.BM = 128;
+            p.BN = 256;
+        } else {
+            p.BM = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+            p.BN = 64;
+        }
+        return p;
+    }
     p.BM = M > 128 ? 256 : 128;
     // Prefer the wider tile unless it leaves most of the 256 CUs idle.
     const int64_t mt = (M + p.BM - 1) / p.BM;
@@ -250,6 +522,10 @@ hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed
     a.bias = static_cast<const uint16_t*>(bias);
     a.C = static_cast<uint16_t*>(C);
     a.ldc = ldc;
+    a.a_bytes = (uint32_t)(((M - 1) * lda + g.K) * 2);
+    a.codes_bytes = (uint32_t)g.codes_bytes;
+    a.scales_bytes = (uint32_t)(g.N * g.Kg * 2);
+    a.zeros_bytes = g.qtype == 1 ? (uint32_t)(g.N * g.Kg) : 0u;
     a.m_tiles = (M + p.BM - 1) / p.BM;
     a.n_blocks = (g.N + p.BN - 1) / p.BN;
     const dim3 grid((unsigned)(a.m_tiles * a.n_blocks));
