@@ -223,8 +223,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // All loads go through buffer descriptors whose per-wave part of the offset
 // is scalar, which keeps the vector registers for the accumulators (A, the
 // codes and the scales each below 2^31 bytes).
-template <int DT, int QT, int SPT, int BM, int WM, int NJ, int KS, bool OC>
+// OCM: 0 scale-first dequantisation (groups of 32 or 64 k); 1 offset-corrected
+// with one group per row (scales applied in the epilogue); 2 offset-
+// corrected with groups of 128 k or more (KS == 1), folded at each group end.
+template <int DT, int QT, int SPT, int BM, int WM, int NJ, int KS, int OCM>
 __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
+    constexpr bool OC = OCM != 0;
+    static_assert(OCM != 2 || (KS == 1 && SPT == 1), "group folds at K-step ends");
     constexpr int WN = 8 / WM;
     constexpr int MI = BM / (16 * WM);
     constexpr int BN = WN * NJ * 16;
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
     constexpr int BUF = NBLK * 1024;        // bytes of one LDS buffer
     // Weight loads per wave per step (with OC the scales and zeros are
     // loaded once, before the K loop).
-    constexpr int NB_LOADS = NJ * KS * (OC ? 1 : 1 + SPT * (1 + QT));
+    constexpr int NB_LOADS = NJ * KS * (OCM == 1 ? 1 : 1 + SPT * (1 + QT));
     static_assert(BPW >= 1, "at least one block per wave");
     // Two separate LDS objects (not one array) for the two activation
     // buffers: the loads into one and the reads of the other then need not
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
                 raw[j][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                            rs_c, lane16, (uint32_t)((nt * a.KTT + kt) * 1024), 2));
 #pragma unroll
-                for (int u = 0; u < SPT && !OC; ++u) {
+                for (int u = 0; u < SPT && OCM != 1; ++u) {
                     const int64_t k = kt * 128 + u * (128 / SPT);
                     const int64_t g = a.one_group ? 0 : (k >> a.gshift);
                     const uint32_t so = (uint32_t)((nt * a.Kg + g) * 16);
@@ -333,6 +338,13 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
     floatx4 S[OC ? MI : 1];
 #pragma unroll
     for (int i = 0; i < (OC ? MI : 1); ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // OCM 2: P sums A*(m + q) and S sums A within the current group; at the
+    // group's last K step acc += s * (P - (m + z) * S) and both restart.
+    floatx4 P[OCM == 2 ? MI : 1][OCM == 2 ? NJ : 1];
+#pragma unroll
+    for (int i = 0; i < (OCM == 2 ? MI : 1); ++i)
+#pragma unroll
+        for (int j = 0; j < (OCM == 2 ? NJ : 1); ++j) P[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
     const u32x4 ones = {one2, one2, one2, one2};
 
@@ -370,9 +382,29 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
                     const u32x4 av = *reinterpret_cast<const u32x4*>(abase + blk * 1024);
                     if (OC) S[i] = mfma16x16x32<DT>(av, ones, S[i]);
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32<DT>(av, bq[j], acc[i][j]);
+                    for (int j = 0; j < NJ; ++j) {
+                        if (OCM == 2) P[OCM == 2 ? i : 0][OCM == 2 ? j : 0] = mfma16x16x32<DT>(av, bq[j], P[OCM == 2 ? i : 0][OCM == 2 ? j : 0]);
+                        else acc[i][j] = mfma16x16x32<DT>(av, bq[j], acc[i][j]);
+                    }
                 }
             }
+        }
+        if (OCM == 2 && (((st + 1) << 7) & ((1 << a.gshift) - 1)) == 0) {
+            // Last K step of a group (G = 2^gshift >= 128): fold and restart.
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float sf = act_to_float<DT>((uint16_t)sb[j][0][0]);
+                const float zf = -((DT == 0 ? 1024.0f : 128.0f) + (QT ? (float)zb[j][0][0] : 8.0f));
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    floatx4& p = P[OCM == 2 ? i : 0][OCM == 2 ? j : 0];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(sf, __builtin_fmaf(zf, S[OC ? i : 0][jj], p[jj]), acc[i][j][jj]);
+                    p = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < (OC ? MI : 1); ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
         // The next activation tile has landed once only the weight loads
         // issued after it may be outstanding; then every wave is done with
@@ -399,7 +431,7 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         const int64_t n = (nt0 + j) * 16 + r;
         const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
         float sf = 1.f, zf = 0.f;
-        if (OC) {  // the row's only scale and zero
+        if (OCM == 1) {  // the row's only scale and zero
             sf = act_to_float<DT>(a.scales[n]);
             zf = -((DT == 0 ? 1024.0f : 128.0f) + (QT ? (float)a.zeros[n] : 8.0f));
         }
@@ -409,7 +441,7 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
             for (int jj = 0; jj < 4; ++jj) {
                 const int64_t m = m0 + wm * (BM / WM) + 16 * i + 4 * g4 + jj;
                 float v = acc[i][j][jj];
-                if (OC) v = sf * __builtin_fmaf(zf, S[OC ? i : 0][jj], v);
+                if (OCM == 1) v = sf * __builtin_fmaf(zf, S[OC ? i : 0][jj], v);
                 if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
             }
         }
@@ -423,13 +455,16 @@ hipError_t launch_lds_t(const MfmaArgs& a, int spt, hipStream_t stream) {
     // Static LDS: two activation buffers of BM x 128*KS. One group per row:
     // offset-corrected dequantisation; otherwise scale first.
     if (a.one_group) {
-        hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, true>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, 1>), grid, dim3(512), 0, stream, a);
         return hipGetLastError();
     }
-    switch (spt) {
-        case 1: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, false>), grid, dim3(512), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 2, BM, WM, NJ, KS, false>), grid, dim3(512), 0, stream, a); break;
-        default: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 4, BM, WM, NJ, KS, false>), grid, dim3(512), 0, stream, a); break;
+    // Per-group offset correction needs KS == 1 and about 250 registers; the
+    // fp16 uint4 instance of it would spill, so that one stays scale first.
+    constexpr int OCG = (KS == 1 && !(DT == 0 && QT == 1)) ? 2 : 0;
+    switch (spt) {  // spt == 1: groups of 128 k or more
+        case 1: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, OCG>), grid, dim3(512), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 2, BM, WM, NJ, KS, 0>), grid, dim3(512), 0, stream, a); break;
+        default: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 4, BM, WM, NJ, KS, 0>), grid, dim3(512), 0, stream, a); break;
     }
     return hipGetLastError();
 }

@@ -102,6 +102,9 @@ IDENTITY = [
     (48, 128, 32, UINT4, "bf16", MFMA),
     (272, 256, 64, UINT4B8, "f16", MFMA),
     (64, 256, -1, UINT4, "f16", MFMA),
+    # wide tiles (at least one workgroup per CU): groups folded at K-step ends
+    (32768, 256, 128, UINT4, "bf16", MFMA),
+    (32768, 256, 256, UINT4B8, "f16", MFMA),
 ]
 
 
