@@ -206,6 +206,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier for the staged kernels. __syncthreads() carries a
+// workgroup-scope fence, which the compiler lowers to a wait for every
+// outstanding vector-memory operation, including the direct-to-LDS loads of
+// stages still in flight, and so serialises the pipeline. Here each wave
+// first waits for exactly the stage the next step reads (wait_vmcnt), and its
+// LDS reads of the current stage are complete (lgkmcnt(0)) before any wave
+// may overwrite that stage. The memory clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Tiled variant with the activation tile loaded straight into LDS.
 // A workgroup of 8 waves computes a BM x BN tile of C, the waves in a
 // WM x (8/WM) grid; wave (wm, wn) owns MI = BM/(16*WM) row blocks and NJ
@@ -410,13 +422,13 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         // issued after it may be outstanding; then every wave is done with
         // this buffer and sees the next one.
         wait_vmcnt<NB_LOADS>();
-        __syncthreads();
+        stage_barrier();
     };
 
     stage_a(0, 0, true);
     load_b(0, raw0, sb0, zb0, true);
     wait_vmcnt<NB_LOADS>();
-    __syncthreads();
+    stage_barrier();
     int64_t st = 0;
     for (; st + 1 < steps; st += 2) {
         step(st, 0, raw0, sb0, zb0, raw1, sb1, zb1);
@@ -446,6 +458,264 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
             }
         }
     }
+}
+
+// Ring variant of the tiled kernel for 128 x 256 tiles with offset-corrected
+// dequantisation (one group per row, or groups of 128 k or more).
+//  * Both operands go from HBM/L2 straight into LDS with direct 16-byte
+//    buffer loads: per K step of 128 the activation tile (32 fragment blocks
+//    of 1 KB) and the workgroup's 16 weight tiles (1 KB each, already in
+//    B-operand order), so every weight word is fetched once per workgroup.
+//  * Three LDS stages form a ring: step t computes on stage t % 3 while the
+//    loads of step t + 2 are in flight, which covers two steps of latency.
+//    One barrier per step.
+//  * The activation sums S (one MFMA per 16 x 32 block against an all-ones
+//    B) are split over the four waves that share a row half: wave wn takes
+//    the K slice s == wn of every step, and the partial sums meet in LDS.
+//  * OCM 1 (one group per row): P = sum A*(m+q) over all of K, and the
+//    epilogue applies C = s * (P - (m+z) * S). OCM 2 (groups of G >= 128):
+//    at each group end acc += s * P, and the correction -s * (m+z) * S_g is
+//    applied one step later, once the S partials of the group have passed
+//    the step's barrier.
+template <int DT, int QT, int OCM>
+__global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
+    static_assert(OCM == 1 || OCM == 2, "offset-corrected modes only");
+    constexpr int BM = 128, WN = 4, MI = 4, NJ = 4;
+    constexpr int ABLK = 32, BBLK = 16;             // 1 KB blocks per stage
+    constexpr int APW = ABLK / 8, BPW = BBLK / 8;   // blocks loaded per wave
+    constexpr int NSC = OCM == 2 ? NJ * (1 + QT) : 0;  // scale/zero loads per wave per step
+    constexpr int STAGE_LOADS = APW + BPW + NSC;
+    __shared__ __attribute__((aligned(1024))) unsigned char a0[ABLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char a1[ABLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char a2[ABLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b0[BBLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b1[BBLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b2[BBLK * 1024];
+    // Row sums: [group parity][wm][row block wn][4 row groups] of floatx4.
+    __shared__ floatx4 sx[2][2][WN][4];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave - wm * WN;
+    const int r = lane & 15, g4 = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int64_t NT = a.N / 16;
+    const int64_t steps = a.KTT;
+    const int64_t ntb = (int64_t)blockIdx.x * 16;  // first n-tile of the workgroup
+
+    auto rsrc = [&](const void* base, uint32_t bytes, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
+    };
+    // Activation block b = wave*APW + t: row block b/4, K slice s = b%4 of
+    // the step; lane l loads row 16*(b/4) + l%16 (clamped to M-1) at k
+    // offset 32*s + 8*(l/16).
+    uint32_t a_off[APW];
+#pragma unroll
+    for (int t = 0; t < APW; ++t) {
+        const int b = wave * APW + t;
+        int64_t row = m0 + 16 * (b >> 2) + r;
+        if (row > a.M - 1) row = a.M - 1;
+        a_off[t] = (uint32_t)((row * a.lda + 8 * g4) * 2);
+    }
+    // Weight block b = wave*BPW + t: n-tile ntb + b (clamped; never stored).
+    uint32_t b_tile[BPW];
+#pragma unroll
+    for (int t = 0; t < BPW; ++t) {
+        const int64_t nt = ntb + wave * BPW + t;
+        b_tile[t] = (uint32_t)(nt < NT ? nt : NT - 1);
+    }
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    auto nt_of = [&](int j) { return ntb + wn * NJ + j; };
+    auto nt_ld = [&](int j) { return nt_of(j) < NT ? nt_of(j) : NT - 1; };
+
+    uint32_t sb0[NJ], sb1[NJ], sb2[NJ], zb0[NJ], zb1[NJ], zb2[NJ];
+    // Requests part p (0..3) of step st: activation block p of the wave,
+    // weight block p (p < BPW), and with p == 2 the scales and zeros of the
+    // step's group. A step's loads are spread over its four K slices so that
+    // the waves do not all queue their requests at the barrier.
+    auto issue = [&](int64_t st, int p, unsigned char* abuf, unsigned char* bbuf, uint32_t (&sb)[NJ],
+                     uint32_t (&zb)[NJ]) {
+        const bool live = st < steps;
+        const int b = wave * APW + p;
+        load_lds16(rsrc(a.A, a.a_bytes, live), abuf + b * 1024, a_off[p], (uint32_t)((st * 128 + 32 * (b & 3)) * 2));
+        if (p < BPW)
+            load_lds16(rsrc(a.codes, a.codes_bytes, live), bbuf + (wave * BPW + p) * 1024, lane16,
+                       (uint32_t)((b_tile[p] * a.KTT + st) * 1024));
+        if (OCM == 2 && p == 2) {
+            const __amdgpu_buffer_rsrc_t rs_s = rsrc(a.scales, a.scales_bytes, live);
+            const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.zeros, a.zeros_bytes, live);
+            const int64_t g = (st * 128) >> a.gshift;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t so = (uint32_t)((nt_ld(j) * a.Kg + g) * 16);
+                sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)r * 2, so * 2, 0);
+                if (QT) zb[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, (uint32_t)r, so, 0);
+            }
+        }
+    };
+    static_assert(APW == 4 && BPW <= 2, "one activation block per K slice");
+
+    uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
+    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
+    const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
+    const u32x4 ones = {one2, one2, one2, one2};
+    constexpr float kM = DT == 0 ? 1024.0f : 128.0f;
+
+    floatx4 acc[MI][NJ], S = {0.f, 0.f, 0.f, 0.f};  // S: row block wn of the half
+    floatx4 P[OCM == 2 ? MI : 1][OCM == 2 ? NJ : 1];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < (OCM == 2 ? NJ : 1); ++j) P[OCM == 2 ? i : 0][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Pending group correction (OCM 2): -s*(m+z) per n column of the wave.
+    float cz[NJ];
+    int par = 0;          // parity of the group whose S partials are written next
+    bool pending = false; // a group ended in the previous step
+
+    // Writes this wave's row sums for parity p: lanes with l%16 == 0 hold
+    // the 16 distinct values (4 each) of the 16 x 16 result.
+    auto put_s = [&](int p) {
+        if (r == 0) sx[p][wm][wn][g4] = S;
+        S = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+    // Row sums of the wave's row blocks, in accumulator layout.
+    auto get_s = [&](int p, floatx4 (&Sf)[MI]) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) Sf[i] = sx[p][wm][i][g4];
+    };
+
+    auto step = [&](int64_t st, unsigned char* abuf, unsigned char* bbuf, const uint32_t (&sb)[NJ],
+                    const uint32_t (&zb)[NJ], unsigned char* nabuf, unsigned char* nbbuf, uint32_t (&nsb)[NJ],
+                    uint32_t (&nzb)[NJ]) {
+        if (OCM == 2 && pending) {
+            floatx4 Sf[MI];
+            get_s(par ^ 1, Sf);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j], Sf[i][jj], acc[i][j][jj]);
+            pending = false;
+        }
+        u32x4 raw[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) raw[j] = *reinterpret_cast<const u32x4*>(bbuf + (wn * NJ + j) * 1024 + lane16);
+        const unsigned char* abase = abuf + lane16;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue(st + 2, s, nabuf, nbbuf, nsb, nzb);
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4 bq[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t w = raw[j][s];
+                bq[j] = u32x4{and_or(w, dq_mask, dq_magic), and_or(w >> 4, dq_mask, dq_magic),
+                              and_or(w >> 8, dq_mask, dq_magic), and_or(w >> 12, dq_mask, dq_magic)};
+            }
+            const u32x4 as = *reinterpret_cast<const u32x4*>(abase + ((wm * MI + wn) * 4 + s) * 1024);
+            S = mfma16x16x32<DT>(as, ones, S);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const u32x4 av = *reinterpret_cast<const u32x4*>(abase + ((wm * MI + i) * 4 + s) * 1024);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    if (OCM == 2) P[OCM == 2 ? i : 0][OCM == 2 ? j : 0] = mfma16x16x32<DT>(av, bq[j], P[OCM == 2 ? i : 0][OCM == 2 ? j : 0]);
+                    else acc[i][j] = mfma16x16x32<DT>(av, bq[j], acc[i][j]);
+                }
+            }
+        }
+        if (OCM == 2 && (((st + 1) << 7) & ((1 << a.gshift) - 1)) == 0) {
+            // Last step of a group: acc += s * P now; the S part waits for
+            // the partials of the other waves (next step, after the barrier).
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float sf = act_to_float<DT>((uint16_t)sb[j]);
+                cz[j] = -sf * (kM + (QT ? (float)zb[j] : 8.0f));
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    floatx4& p = P[OCM == 2 ? i : 0][OCM == 2 ? j : 0];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(sf, p[jj], acc[i][j][jj]);
+                    p = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            put_s(par);
+            par ^= 1;
+            pending = true;
+        }
+        // Stage st + 1 has landed once only the loads of step st + 2 may be
+        // outstanding; the barrier then also frees stage st for step st + 3.
+        wait_vmcnt<STAGE_LOADS>();
+        stage_barrier();
+    };
+
+#pragma unroll
+    for (int p = 0; p < 4; ++p) issue(0, p, a0, b0, sb0, zb0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) issue(1, p, a1, b1, sb1, zb1);
+    wait_vmcnt<STAGE_LOADS>();
+    stage_barrier();
+    int64_t st = 0;
+    for (; st + 3 <= steps; st += 3) {
+        step(st, a0, b0, sb0, zb0, a2, b2, sb2, zb2);
+        step(st + 1, a1, b1, sb1, zb1, a0, b0, sb0, zb0);
+        step(st + 2, a2, b2, sb2, zb2, a1, b1, sb1, zb1);
+    }
+    if (st < steps) step(st, a0, b0, sb0, zb0, a2, b2, sb2, zb2);
+    if (st + 1 < steps) step(st + 1, a1, b1, sb1, zb1, a0, b0, sb0, zb0);
+    wait_vmcnt<0>();
+
+    floatx4 Sf[MI];
+    if (OCM == 1) {
+        put_s(0);
+        stage_barrier();
+        get_s(0, Sf);
+    } else {
+        // The last group's correction (its partials passed the last barrier).
+        get_s(par ^ 1, Sf);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j], Sf[i][jj], acc[i][j][jj]);
+    }
+
+    // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l%16 of each block.
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if (nt_of(j) >= NT) continue;
+        const int64_t n = nt_of(j) * 16 + r;
+        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+        float sf = 1.f, zf = 0.f;
+        if (OCM == 1) {  // the row's only scale and zero
+            sf = act_to_float<DT>(a.scales[n]);
+            zf = -(kM + (QT ? (float)a.zeros[n] : 8.0f));
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int64_t m = m0 + wm * 64 + 16 * i + 4 * g4 + jj;
+                float v = acc[i][j][jj];
+                if (OCM == 1) v = sf * __builtin_fmaf(zf, Sf[i][jj], v);
+                if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
+            }
+        }
+    }
+}
+
+template <int DT, int QT>
+hipError_t launch_ring_t(const MfmaArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)((a.M + 127) / 128));
+    if (a.one_group) hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, 1>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, 2>), grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
 }
 
 template <int DT, int QT, int BM, int WM, int NJ, int KS>
@@ -494,7 +764,10 @@ hipError_t launch_mfma_t(const MfmaArgs& a, int spt, dim3 grid, hipStream_t stre
 template <int DT, int QT>
 hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, dim3 grid, hipStream_t stream) {
     if (p.lds && ((a.M - 1) * a.lda + a.KTT * 128) * 2 < ((int64_t)1 << 31)) {
-        if (p.BN == 256) return launch_lds_t<DT, QT, 128, 2, 4, 1>(a, spt, stream);
+        if (p.BN == 256) {
+            // Offset-corrected modes run on the three-stage ring.
+            return spt == 1 ? launch_ring_t<DT, QT>(a, stream) : launch_lds_t<DT, QT, 128, 2, 4, 1>(a, spt, stream);
+        }
         switch (p.BM) {  // BN = 64: one n-tile per wave, 2 or 4 k-tiles per step
             case 32: return launch_lds_t<DT, QT, 32, 2, 1, 4>(a, spt, stream);
             case 64: return launch_lds_t<DT, QT, 64, 2, 1, 2>(a, spt, stream);

@@ -105,6 +105,7 @@ IDENTITY = [
     # wide tiles (at least one workgroup per CU): groups folded at K-step ends
     (32768, 256, 128, UINT4, "bf16", MFMA),
     (32768, 256, 256, UINT4B8, "f16", MFMA),
+    (32768, 512, 256, UINT4, "f16", MFMA),      # two K steps per group
 ]
 
 
@@ -290,6 +291,32 @@ def test_skinny_k_extremes(K):
     packed = repack(case)
     C = w4.gemm(case.A.to(DEV), packed, N, K, G, UINT4, path=SKINNY)
     assert oracle.rel_err(C.cpu(), oracle_ref(case)) <= oracle.TOLERANCE["bf16"]
+
+
+# 128 x 256 tiles on the three-stage ring (at least 256 workgroups, one group
+# per row or groups of 128 k or more). Each case names the edge it reaches.
+RING = [
+    # (M, N, K, G, qtype, dtype, bias)
+    (2048, 4096, 128, -1, UINT4B8, "bf16", False),  # one K step: only the loop tail runs
+    (2000, 4112, 1024, 256, UINT4, "f16", True),    # ragged M and N (257 n-tiles), 8 steps: tail of 2
+    (4096, 4096, 512, 128, UINT4B8, "f16", False),  # a group per step, tail of 1
+    (2048, 8192, 1536, 256, UINT4, "bf16", True),   # 2 steps per group, 12 steps: no tail
+    (1930, 8192, 896, -1, UINT4, "f16", False),     # 7 steps: tail of 1, ragged M
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,qtype,dtype,bias", RING,
+                         ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-G{c[3]}-q{c[4]}-{c[5]}" for c in RING])
+def test_ring_tiles(M, N, K, G, qtype, dtype, bias):
+    print(f"[case] ring M={M} N={N} K={K} G={G} qtype={qtype} {dtype} bias={bias}", flush=True)
+    case = _case(25, M, N, K, G, qtype, dtype, with_bias=bias)
+    packed = repack(case)
+    _, _, _, A, b = to_dev(case)
+    C = w4.gemm(A, packed, N, K, G, qtype, bias=b, path=MFMA)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    err = rel_err_rows(C, oracle_ref(case, rows=rows), rows)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
 
 
 # Full-K skinny kernels (N >= 3072): activations in registers or staged in
