@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """W4A16 GEMM benchmark on one MI355X (gfx950).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline] [--prefill-only]
 
 A step is one pass of the decode workload through the C ABI: the symmetric
 uint4b8 fp16 GEMMs with G = 128 for M in {1, 4, 8, 16} and (N, K) in
@@ -220,6 +220,30 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+def prefill_rates():
+    """Prefill workload on the MFMA kernel: TFLOP/s per shape and in total."""
+    wl = wi.WORKLOADS["prefill"]
+    rows, tot_flop, tot_us = [], 0.0, 0.0
+    for (G, qt) in wl["variants"]:
+        for (M, N, K) in wl["shapes"]:
+            g = Gemm(wl["cfg_id"], M, N, K, G, qt, wl["dtype"], wl["sigma"], 2)
+            us = per_case_rate(g, launches=2, reps=5)
+            tf = g.flops / us / 1e6
+            rows.append({"M": M, "N": N, "K": K, "G": G, "qtype": qt, "us": round(us, 1), "tflops": round(tf, 1),
+                         "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4)})
+            tot_flop += g.flops
+            tot_us += us
+            del g
+            torch.cuda.empty_cache()
+    return {
+        "workload": "M in {2048,8192} x (N,K) in {(14336,4096),(4096,14336)} x G in {-1,256} x {uint4b8, uint4+zp}, bf16",
+        "tflops": round(tot_flop / tot_us / 1e6, 1),
+        "frac_of_peak": round(tot_flop / tot_us / 1e6 / MFMA_PEAK_TFLOPS, 4),
+        "peak_tflops": MFMA_PEAK_TFLOPS,
+        "rows": rows,
+    }
+
+
 def extras(warmup):
     out = {}
     # Crossover workload: skinny (16-row slices) vs MFMA at M = 32..256.
@@ -236,27 +260,7 @@ def extras(warmup):
         cross.append(row)
     out["crossover"] = {"workload": "N=14336, K=4096, G=64, uint4b8, fp16", "rows": cross,
                         "crossover_M": next((r["M"] for r in cross if r["mfma_us"] < r["skinny_us"]), None)}
-    # Prefill workload on the MFMA kernel.
-    wl = wi.WORKLOADS["prefill"]
-    rows, tot_flop, tot_us = [], 0.0, 0.0
-    for (G, qt) in wl["variants"]:
-        for (M, N, K) in wl["shapes"]:
-            g = Gemm(wl["cfg_id"], M, N, K, G, qt, wl["dtype"], wl["sigma"], 2)
-            us = per_case_rate(g, launches=2, reps=5)
-            tf = g.flops / us / 1e6
-            rows.append({"M": M, "N": N, "K": K, "G": G, "qtype": qt, "us": round(us, 1), "tflops": round(tf, 1),
-                         "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4)})
-            tot_flop += g.flops
-            tot_us += us
-            del g
-            torch.cuda.empty_cache()
-    out["prefill"] = {
-        "workload": "M in {2048,8192} x (N,K) in {(14336,4096),(4096,14336)} x G in {-1,256} x {uint4b8, uint4+zp}, bf16",
-        "tflops": round(tot_flop / tot_us / 1e6, 1),
-        "frac_of_peak": round(tot_flop / tot_us / 1e6 / MFMA_PEAK_TFLOPS, 4),
-        "peak_tflops": MFMA_PEAK_TFLOPS,
-        "rows": rows,
-    }
+    out["prefill"] = prefill_rates()
     # Decode asymmetric bf16 workload and the tiny case.
     wl = wi.WORKLOADS["decode_asym"]
     asym = []
@@ -286,6 +290,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-shape decode timings")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time the prefill workload on the MFMA kernel and print its JSON")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer 10 times (a known-size workload that calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -308,6 +314,9 @@ def main():
         print(json.dumps({"calibration_copy_bytes": n, "copies": 10}), flush=True)
         return
     w4.load_library()
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_rates()}), flush=True)
+        return
 
     cases, copies = decode_cases()
     step_weight_bytes = sum(c.weight_bytes for c in cases)

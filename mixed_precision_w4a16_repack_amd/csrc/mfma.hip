@@ -1,27 +1,30 @@
 // mfma.hip -- W4A16 GEMM for large M (prefill), a dense contraction on the
-// gfx950 matrix cores.
+// gfx950 matrix cores (v_mfma_f32_16x16x32_{f16,bf16}).
 //
 // Prior art: the fused dequant-GEMM Triton kernels of the pages
 // (`_triton_w4a16_skinny_fmt_kernel` on the "rdna_hybrid_w4a16" pages,
 // `triton_w4a16_gemm_kernel` on the MI300 "triton_w4a16.py" page): per K step
 // they load an activation tile and a packed weight tile, unpack, subtract the
-// zero, scale, and accumulate a dot product in fp32. This kernel keeps that
-// arithmetic and lays the work out for CDNA4:
+// zero, scale, and accumulate a dot product in fp32. Three kernels keep that
+// arithmetic and lay the work out for CDNA4:
 //
-//  * A workgroup of 4 wavefronts computes a BM x (64*WNT) tile of C. All four
-//    waves share the BM activation rows; each wave owns WNT distinct 16-column
-//    n-tiles, so every weight word is loaded and dequantised exactly once per
-//    workgroup, in registers, straight from one 16-byte load per lane of the
-//    packed tile (which is already in MFMA B-operand order).
-//  * The activation tile (BM x 128 per K step) is staged in LDS in
-//    "fragment order": 1 KB per (16 rows x 32 k) block, lane l's 16 bytes at
-//    offset 16*l, so every A-operand read is one conflict-free ds_read_b128.
-//    Two LDS buffers alternate: the next tile is fetched while the current
-//    one feeds the MFMAs; one barrier per K step.
-//  * Each wave issues v_mfma_f32_16x16x32_{f16,bf16}; (BM/16) x WNT
-//    accumulators of 4 fp32 per lane (256 fp32 at BM = 256, WNT = 4) live in
-//    the accumulation registers.
-//  * Epilogue: + bias in fp32, one rounding to the act dtype, store.
+//  * mfma_ring_kernel: 128 x 256 tiles when they give at least one
+//    workgroup per CU, for one group per row or groups of 128 k or more.
+//    Activation and weight tiles go from HBM/L2 straight into a three-stage
+//    LDS ring (direct 16-byte buffer loads), and the weights are
+//    dequantised offset-corrected: exact magic values m + q into the MFMA,
+//    the scale applied once per group.
+//  * mfma_lds_kernel: the other tile shapes (64-column tiles at small and
+//    medium M) and groups of 32 or 64 k (scale first, per weight, as the
+//    pages do); activation tiles go straight into two LDS buffers, the
+//    weights into registers.
+//  * mfma_kernel: the fallback when an operand is too large for the 32-bit
+//    offsets of buffer loads.
+// Every kernel stages activations in LDS in "fragment order" (1 KB per
+// 16 rows x 32 k, lane l's 16 bytes at 16*l) so that each A-operand read is
+// one conflict-free ds_read_b128, reads the packed weight tiles, which are
+// already in B-operand order, and ends with bias in fp32, one rounding to
+// the act dtype, and the store.
 #include "device_common.h"
 #include "internal.h"
 
@@ -557,6 +560,18 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
 
     uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
+    // Magic values of two consecutive words: b0 from w0, b1 from w1.
+    auto dequant_pair = [&](uint32_t w0, uint32_t w1, u32x4& b0, u32x4& b1) {
+        const uint64_t x = ((uint64_t)w1 << 32) | w0;
+        uint64_t x4, x8, x12;
+        asm("v_lshrrev_b64 %0, 4, %1" : "=v"(x4) : "v"(x));
+        asm("v_lshrrev_b64 %0, 8, %1" : "=v"(x8) : "v"(x));
+        asm("v_lshrrev_b64 %0, 12, %1" : "=v"(x12) : "v"(x));
+        b0 = u32x4{and_or((uint32_t)x, dq_mask, dq_magic), and_or((uint32_t)x4, dq_mask, dq_magic),
+                   and_or((uint32_t)x8, dq_mask, dq_magic), and_or((uint32_t)x12, dq_mask, dq_magic)};
+        b1 = u32x4{and_or((uint32_t)(x >> 32), dq_mask, dq_magic), and_or((uint32_t)(x4 >> 32), dq_mask, dq_magic),
+                   and_or((uint32_t)(x8 >> 32), dq_mask, dq_magic), and_or((uint32_t)(x12 >> 32), dq_mask, dq_magic)};
+    };
     const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
     const u32x4 ones = {one2, one2, one2, one2};
     constexpr float kM = DT == 0 ? 1024.0f : 128.0f;
@@ -605,18 +620,19 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) raw[j] = *reinterpret_cast<const u32x4*>(bbuf + (wn * NJ + j) * 1024 + lane16);
         const unsigned char* abase = abuf + lane16;
+        u32x4 bq2[2][NJ];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             __builtin_amdgcn_sched_barrier(0);
             issue(st + 2, s, nabuf, nbbuf, nsb, nzb);
             __builtin_amdgcn_sched_barrier(0);
-            u32x4 bq[NJ];
+            if ((s & 1) == 0) {
+                // Slices s and s + 1 together: their words are adjacent
+                // registers, so one 64-bit shift serves both.
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const uint32_t w = raw[j][s];
-                bq[j] = u32x4{and_or(w, dq_mask, dq_magic), and_or(w >> 4, dq_mask, dq_magic),
-                              and_or(w >> 8, dq_mask, dq_magic), and_or(w >> 12, dq_mask, dq_magic)};
+                for (int j = 0; j < NJ; ++j) dequant_pair(raw[j][s], raw[j][s + 1], bq2[0][j], bq2[1][j]);
             }
+            const u32x4 (&bq)[NJ] = bq2[s & 1];
             const u32x4 as = *reinterpret_cast<const u32x4*>(abase + ((wm * MI + wn) * 4 + s) * 1024);
             S = mfma16x16x32<DT>(as, ones, S);
 #pragma unroll
