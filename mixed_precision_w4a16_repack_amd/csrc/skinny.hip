@@ -397,6 +397,20 @@ __device__ __forceinline__ void fold(floatx4& acc, const floatx4& P, const float
     for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(sf, __builtin_fmaf(zf, S[jj], P[jj]), acc[jj]);
 }
 
+// Sum over the first nwa waves of red[wave][i][lane], in wave order. The
+// LDS holds 8 waves' slots (launch size 8 * nn_max KB), so all 8 reads are
+// issued at once and only the additions depend on nwa.
+__device__ __forceinline__ floatx4 sum_waves(const floatx4* red, int nn, int i, int nwa, int lane) {
+    floatx4 v[kStreamWaves];
+#pragma unroll
+    for (int q = 0; q < kStreamWaves; ++q) v[q] = red[(q * nn + i) * 64 + lane];
+    floatx4 tot = v[0];
+#pragma unroll
+    for (int q = 1; q < kStreamWaves; ++q)
+        if (q < nwa) tot += v[q];
+    return tot;
+}
+
 // The first `nwa` waves have written red[wave][i][lane] for i < nn; wave q
 // of the workgroup's nw waves sums them, in wave order, for n-tiles q,
 // q + nw, ..., adds the bias, rounds once and stores rows < M.
@@ -407,8 +421,7 @@ __device__ __forceinline__ void finish_tiles(const SkinnyArgs& a, const floatx4*
     const int r = lane & 15, g4 = lane >> 4;
     const int nw = blockDim.x >> 6;  // short K: fewer than 8 waves
     for (int i = wave; i < nn; i += nw) {
-        floatx4 tot = red[(0 * nn + i) * 64 + lane];
-        for (int q = 1; q < nwa; ++q) tot += red[(q * nn + i) * 64 + lane];
+        const floatx4 tot = sum_waves(red, nn, i, nwa, lane);
         const int64_t n = (g + (int64_t)i * groups) * 16 + r;
         const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
 #pragma unroll
@@ -433,8 +446,7 @@ __device__ __forceinline__ void finish_split(const SkinnyArgs& a, const floatx4*
     const int nw = blockDim.x >> 6;
     float* part = a.partials + g * a.ksplit * (int64_t)a.nn_max * 256;
     for (int i = wave; i < nn; i += nw) {
-        floatx4 tot = red[(0 * nn + i) * 64 + lane];
-        for (int q = 1; q < nwa; ++q) tot += red[(q * nn + i) * 64 + lane];
+        const floatx4 tot = sum_waves(red, nn, i, nwa, lane);
         store_coherent(part + (((int64_t)c * a.nn_max + i) * 64 + lane) * 4, tot);
     }
     wait_vector_memory();
@@ -510,14 +522,26 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
 
     // 1. Activation fragments: lane (r, g4) of word s of k-tile j holds
-    //    A[r][128*(kt0+j) + 32*s + 8*g4 .. +7] (zeros for rows r >= M).
+    //    A[r][128*(kt0+j) + 32*s + 8*g4 .. +7]. The lanes of padding rows
+    //    (r >= M) issue no load at all: the texture unit's time per load
+    //    grows with the active lanes, and at small M most lanes are padding.
     const ActRows act(a, r, g4);
     const WeightBufs wb(a);
+    // Lanes of rows past M keep whatever their registers hold (an empty asm
+    // defines them without an instruction): row m of an MFMA result depends
+    // on row m of A only, and those rows are never stored.
     u32x4 af[KTM][4];
 #pragma unroll
     for (int j = 0; j < KTM; ++j) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) af[j][s] = act.load(kt0 + j, s, j < kc);
+        for (int s = 0; s < 4; ++s) asm volatile("" : "=v"(af[j][s]));
+    }
+    if (r < a.M) {
+#pragma unroll
+        for (int j = 0; j < KTM; ++j) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[j][s] = act.load(kt0 + j, s, j < kc);
+        }
     }
     // 2. Weight tiles, scales and zeros of every (n-tile, k-tile) unit, in
     //    consumption order.
@@ -580,11 +604,11 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
     else finish_split<DT>(a, red, reinterpret_cast<int*>(red + kStreamWaves * a.nn_max * 64), nn, nwaves, g, c);
 }
 
-template <int DT, int QT, int FW, int NNM, int KTW>
+template <int DT, int QT, int FW, int NNM, int KTW, int MR>
 __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a) {
-    constexpr int NB = 4 / FW;                   // fold blocks per k-tile
+    constexpr int NB = 4 / FW;  // fold blocks per k-tile
     constexpr int LD = act_lds_ld<KTW>();
-    constexpr int kMaxRows = KTW <= 4 ? 16 : 4;  // M this variant is launched for (LDS budget)
+    constexpr int kMaxRows = MR;  // largest M this instance is launched for
     constexpr int kMaxChunks = (kMaxRows * KTW * 16 + 63) / 64;  // 16-byte activation chunks per lane
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & 63;
@@ -787,10 +811,10 @@ hipError_t launch_reg(const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds, hi
     return e;
 }
 
-template <int DT, int QT, int FW, int NNM, int KTW>
+template <int DT, int QT, int FW, int NNM, int KTW, int MR>
 hipError_t launch_res(const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
-    hipError_t e = allow_lds<skinny_res_kernel<DT, QT, FW, NNM, KTW>>(lds);
-    if (e == hipSuccess) hipLaunchKernelGGL((skinny_res_kernel<DT, QT, FW, NNM, KTW>), grid, block, lds, stream, a);
+    hipError_t e = allow_lds<skinny_res_kernel<DT, QT, FW, NNM, KTW, MR>>(lds);
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_res_kernel<DT, QT, FW, NNM, KTW, MR>), grid, block, lds, stream, a);
     return e;
 }
 
@@ -812,8 +836,10 @@ hipError_t launch_stream_fw(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_
         const dim3 block((unsigned)(64 * ((a.KTT + p.ktw - 1) / p.ktw)));
         const size_t lds_a = (size_t)kStreamWaves * a.M * p.ktw * 128 * 2 + (size_t)kStreamWaves * a.M * 16;
         const size_t lds_r = lds > lds_a ? lds : lds_a;
-        // The planner picks this variant for one n-tile per workgroup only.
-        return launch_res<DT, QT, FW, 1, 4>(a, grid, block, lds_r, stream);
+        // The planner picks this variant for one n-tile per workgroup only;
+        // up to 8 rows need half the activation registers.
+        return a.M <= 8 ? launch_res<DT, QT, FW, 1, 4, 8>(a, grid, block, lds_r, stream)
+                        : launch_res<DT, QT, FW, 1, 4, 16>(a, grid, block, lds_r, stream);
     }
     hipError_t e = allow_lds<skinny_str_kernel<DT, QT, FW>>(lds);
     if (e == hipSuccess)
@@ -877,19 +903,18 @@ SkinnyPlan plan_skinny(int64_t M, const Geometry& g) {
         // Every weight tile of a wave in registers (at most 16): 4 k-tiles
         // per wave and up to 4 n-tiles per workgroup (2 with a scale per
         // word). The activation fragments either stay in registers for all
-        // of the wave's n-tiles (kRegisters: several n-tiles share them, or
-        // few rows), or are staged per wave in LDS (kResident: one n-tile and
-        // 8 or more rows, where registers would carry 16 rows of padding
-        // through the load path). With K > 4096, K is split into chunks of
-        // at most 32 k-tiles (8 waves) and the n-groups shrink so that the
-        // chunks of all n-groups still make about one workgroup per CU; the
-        // chunk partials meet in the workspace. Otherwise the streamed
-        // variant.
-        const int64_t m = M < 1 ? 1 : (M > 16 ? 16 : M);
+        // of the wave's n-tiles (kRegisters: several n-tiles share them), or
+        // the M real rows are loaded compactly and staged per wave in LDS
+        // (kResident: one n-tile per workgroup, where 16 fragment loads per
+        // wave would cost more texture-unit time than the weights). With
+        // K > 4096, K is split into chunks of at most 32 k-tiles (8 waves)
+        // and the n-groups shrink so that the chunks of all n-groups still
+        // make about one workgroup per CU; the chunk partials meet in the
+        // workspace. Otherwise the streamed variant.
         const int nb = g.Kg == 1 || g.Ge >= 128 ? 1 : (int)(128 / g.Ge);  // fold blocks per k-tile
         const int nn_cap = nb < 4 ? 4 : 2;
         if (KTT <= 32 && p.nn_max <= nn_cap) {
-            p.mode = (p.nn_max >= 2 || m < 8) ? SkinnyPlan::kRegisters : SkinnyPlan::kResident;
+            p.mode = p.nn_max >= 2 ? SkinnyPlan::kRegisters : SkinnyPlan::kResident;
             p.ktw = kResMaxKt;
             return p;
         }

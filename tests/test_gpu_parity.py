@@ -325,14 +325,15 @@ def test_ring_tiles(M, N, K, G, qtype, dtype, bias):
 FULL_K = [
     # (N, K, M, G, qtype, dtype, bias)
     (4096, 128, 16, 128, UINT4B8, "f16", True),   # one k-tile, one wave, LDS activations
-    (4096, 384, 3, 64, UINT4, "bf16", False),     # one wave with 3 k-tiles, register activations
+    (4096, 384, 3, 64, UINT4, "bf16", False),     # one wave with 3 k-tiles, LDS activations (up to 8 rows)
     (4096, 640, 9, 32, UINT4, "f16", True),       # two waves (4 and 1 k-tiles), a scale per word
     (4112, 1024, 5, 128, UINT4B8, "bf16", False), # 257 n-tiles: 2 per workgroup, the last has 1
     (14416, 512, 2, 64, UINT4, "f16", True),      # 901 n-tiles: 4 per workgroup, ragged last ones
     (14336, 4096, 2, 64, UINT4, "f16", False),    # 4 n-tiles per workgroup with zeros, 2 fold blocks
-    (4096, 4224, 16, 128, UINT4B8, "f16", False), # 33 k-tiles: streamed, a wave with no k-tile
-    (3072, 14336, 3, 128, UINT4, "bf16", True),   # 14 k-tiles per wave, LDS activations
-    (4096, 16384, 12, -1, UINT4B8, "f16", False), # streamed, one group per row
+    (4096, 4224, 16, 128, UINT4B8, "f16", False), # 33 k-tiles: K split in chunks of 20 and 13
+    (3072, 14336, 3, 128, UINT4, "bf16", True),   # K split in 4 chunks, 3 n-tiles per workgroup
+    (4096, 16384, 12, -1, UINT4B8, "f16", False), # K split in 4 chunks, one group per row
+    (14336, 4096, 7, 32, UINT4, "bf16", True),    # streamed: 4 n-tiles per workgroup, a scale per word
     (6144, 4096, 16, 32, UINT4, "bf16", True),    # 2 n-tiles per workgroup, a scale per word
 ]
 
