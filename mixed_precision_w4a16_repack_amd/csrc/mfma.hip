@@ -473,13 +473,15 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
 //    loads of step t + 2 are in flight, which covers two steps of latency.
 //    One barrier per step.
 //  * The activation sums S (one MFMA per 16 x 32 block against an all-ones
-//    B) are split over the four waves that share a row half: wave wn takes
-//    the K slice s == wn of every step, and the partial sums meet in LDS.
-//  * OCM 1 (one group per row): P = sum A*(m+q) over all of K, and the
+//    B) are split over the four waves that share a row half: wave wn sums
+//    row block wn of the half (one extra fragment read per K slice), and
+//    the sums meet in LDS.
+//  * P = sum A*(m+q) runs over all of K. OCM 1 (one group per row): the
 //    epilogue applies C = s * (P - (m+z) * S). OCM 2 (groups of G >= 128):
-//    at each group end acc += s * P, and the correction -s * (m+z) * S_g is
-//    applied one step later, once the S partials of the group have passed
-//    the step's barrier.
+//    each group end adds (s_g - s_{g+1}) * P to the result, which sums to
+//    sum_g s_g * P_g without ever clearing P, and the correction
+//    -s_g * (m+z_g) * S_g is applied one step later, once the row sums of
+//    the group have passed the step's barrier.
 template <int DT, int QT, int OCM>
 __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     static_assert(OCM == 1 || OCM == 2, "offset-corrected modes only");
@@ -602,9 +604,11 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
         for (int i = 0; i < MI; ++i) Sf[i] = sx[p][wm][i][g4];
     };
 
+    // sb, zb: scales and zeros of step st; sbn: scales of step st + 1 (0
+    // past the last step, whose loads use zero-size descriptors).
     auto step = [&](int64_t st, unsigned char* abuf, unsigned char* bbuf, const uint32_t (&sb)[NJ],
-                    const uint32_t (&zb)[NJ], unsigned char* nabuf, unsigned char* nbbuf, uint32_t (&nsb)[NJ],
-                    uint32_t (&nzb)[NJ]) {
+                    const uint32_t (&zb)[NJ], const uint32_t (&sbn)[NJ], unsigned char* nabuf, unsigned char* nbbuf,
+                    uint32_t (&nsb)[NJ], uint32_t (&nzb)[NJ]) {
         if (OCM == 2 && pending) {
             floatx4 Sf[MI];
             get_s(par ^ 1, Sf);
@@ -646,18 +650,20 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
             }
         }
         if (OCM == 2 && (((st + 1) << 7) & ((1 << a.gshift) - 1)) == 0) {
-            // Last step of a group: acc += s * P now; the S part waits for
-            // the partials of the other waves (next step, after the barrier).
+            // Last step of group g: P runs over all of K (never reset), so
+            // sum_g s_g * P_g = sum_g (s_g - s_{g+1}) * P(end of g), with
+            // s_{G+1} = 0 after the last group. The S part waits for the
+            // row sums of the other waves (next step, after the barrier).
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const float sf = act_to_float<DT>((uint16_t)sb[j]);
+                const float d = sf - act_to_float<DT>((uint16_t)sbn[j]);
                 cz[j] = -sf * (kM + (QT ? (float)zb[j] : 8.0f));
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
-                    floatx4& p = P[OCM == 2 ? i : 0][OCM == 2 ? j : 0];
+                    const floatx4& p = P[OCM == 2 ? i : 0][OCM == 2 ? j : 0];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(sf, p[jj], acc[i][j][jj]);
-                    p = floatx4{0.f, 0.f, 0.f, 0.f};
+                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(d, p[jj], acc[i][j][jj]);
                 }
             }
             put_s(par);
@@ -678,12 +684,12 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     stage_barrier();
     int64_t st = 0;
     for (; st + 3 <= steps; st += 3) {
-        step(st, a0, b0, sb0, zb0, a2, b2, sb2, zb2);
-        step(st + 1, a1, b1, sb1, zb1, a0, b0, sb0, zb0);
-        step(st + 2, a2, b2, sb2, zb2, a1, b1, sb1, zb1);
+        step(st, a0, b0, sb0, zb0, sb1, a2, b2, sb2, zb2);
+        step(st + 1, a1, b1, sb1, zb1, sb2, a0, b0, sb0, zb0);
+        step(st + 2, a2, b2, sb2, zb2, sb0, a1, b1, sb1, zb1);
     }
-    if (st < steps) step(st, a0, b0, sb0, zb0, a2, b2, sb2, zb2);
-    if (st + 1 < steps) step(st + 1, a1, b1, sb1, zb1, a0, b0, sb0, zb0);
+    if (st < steps) step(st, a0, b0, sb0, zb0, sb1, a2, b2, sb2, zb2);
+    if (st + 1 < steps) step(st + 1, a1, b1, sb1, zb1, sb2, a0, b0, sb0, zb0);
     wait_vmcnt<0>();
 
     floatx4 Sf[MI];
