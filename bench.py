@@ -244,6 +244,39 @@ def prefill_rates():
     }
 
 
+def prefill_dense_rates():
+    """The dense prefill variant on the prefill workload: the dequantisation of
+    each weight into a dense copy (w4a16_dequant) and hipBLASLt on that copy
+    (w4a16_gemm_dense), timed separately; TFLOP/s of the GEMM alone (the
+    cached-copy case of the pages) and of both together."""
+    wl = wi.WORKLOADS["prefill"]
+    rows, tot_flop, tot_gemm, tot_both = [], 0.0, 0.0, 0.0
+    for (G, qt) in wl["variants"]:
+        for (M, N, K) in wl["shapes"]:
+            g = Gemm(wl["cfg_id"], M, N, K, G, qt, wl["dtype"], wl["sigma"], 2)
+            dt = g.A.dtype
+            dense = [torch.empty((N, K), dtype=dt, device=DEV) for _ in range(2)]
+            deq = capture_graphs([[(lambda c=c: w4.dequant(g.packed[c], N, K, G, qt, dt, out=dense[c]))
+                                   for c in range(2)]])
+            us_deq = time_graphs(deq, 5, 2) * 1e3 / 10
+            mm = capture_graphs([[(lambda c=c: w4.gemm_dense(g.A, dense[c], out=g.C)) for c in range(2)]])
+            us_mm = time_graphs(mm, 5, 2) * 1e3 / 10
+            rows.append({"M": M, "N": N, "K": K, "G": G, "qtype": qt, "dequant_us": round(us_deq, 1),
+                         "gemm_us": round(us_mm, 1), "gemm_tflops": round(g.flops / us_mm / 1e6, 1),
+                         "total_tflops": round(g.flops / (us_mm + us_deq) / 1e6, 1)})
+            tot_flop += g.flops
+            tot_gemm += us_mm
+            tot_both += us_mm + us_deq
+            del g, dense, deq, mm
+            torch.cuda.empty_cache()
+    return {
+        "workload": "the prefill workload through w4a16_dequant + w4a16_gemm_dense (hipBLASLt), bf16",
+        "gemm_tflops": round(tot_flop / tot_gemm / 1e6, 1),
+        "total_tflops": round(tot_flop / tot_both / 1e6, 1),
+        "rows": rows,
+    }
+
+
 def extras(warmup):
     out = {}
     # Crossover workload: skinny (16-row slices) vs MFMA at M = 32..256.
@@ -261,6 +294,7 @@ def extras(warmup):
     out["crossover"] = {"workload": "N=14336, K=4096, G=64, uint4b8, fp16", "rows": cross,
                         "crossover_M": next((r["M"] for r in cross if r["mfma_us"] < r["skinny_us"]), None)}
     out["prefill"] = prefill_rates()
+    out["prefill_dense"] = prefill_dense_rates()
     # Decode asymmetric bf16 workload and the tiny case.
     wl = wi.WORKLOADS["decode_asym"]
     asym = []
@@ -291,7 +325,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-shape decode timings")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="only time the prefill workload on the MFMA kernel and print its JSON")
+                    help="only time the prefill workload (MFMA kernel, and the dense variant) and print its JSON")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer 10 times (a known-size workload that calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -315,7 +349,7 @@ def main():
         return
     w4.load_library()
     if args.prefill_only:
-        print(json.dumps({"prefill": prefill_rates()}), flush=True)
+        print(json.dumps({"prefill": prefill_rates(), "prefill_dense": prefill_dense_rates()}), flush=True)
         return
 
     cases, copies = decode_cases()

@@ -35,6 +35,7 @@
  *  - Pointers are device pointers unless a parameter says "host". All device
  *    memory is owned by the caller; the library never allocates, frees or
  *    synchronises (calls are asynchronous on `stream`, NULL = default stream).
+ *    The one exception is w4a16_gemm_dense (see there).
  *  - Every call validates its arguments before any HIP call. A failure
  *    returns a negative w4a16_status and sets a message readable with
  *    w4a16_last_error() on the same thread (e.g. "K=4100 must be divisible by
@@ -158,6 +159,40 @@ w4a16_status w4a16_gemm(const void *A, int64_t M, int64_t lda, const void *packe
                         int32_t group_size, int32_t qtype, int32_t dtype, const void *bias, void *C, int64_t ldc,
                         int32_t path, int32_t skinny_max_m, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/* Dense dequantisation of the packed buffer, the first half of the pages'
+ * second prefill strategy ("rdna_hybrid_w4a16" page, build 61746:
+ * `dequantize_w4a16` and `_cache_dequant_weight`, which keep a dense copy of
+ * each weight, four times its int4 bytes, for prefill):
+ *   dense[n, k] = RN_act((q - z) * s)   (one rounding, as `dequantize_w4a16`)
+ *   packed  the buffer written by w4a16_repack for the same N, K,
+ *           group_size and qtype (the call cannot check this)
+ *   dense   [N, ldw] act dtype, row-major, ldw >= K, 16-byte aligned with
+ *           ldw % 8 == 0 (W4A16_ERR_UNSUPPORTED otherwise); N * ldw * 2
+ *           bytes owned by the caller, who decides whether the memory budget
+ *           allows a dense copy
+ * Shapes and group sizes as for w4a16_repack. */
+w4a16_status w4a16_dequant(const void *packed, int64_t N, int64_t K, int32_t group_size, int32_t qtype,
+                           int32_t dtype, void *dense, int64_t ldw, hipStream_t stream);
+
+/* C[M, N] = A[M, K] @ W[N, K]^T (+ bias) for a dense act-dtype weight W
+ * (for example written by w4a16_dequant), the second half of that strategy:
+ * `_rdna_hybrid_w4a16_apply_impl` sends M >= MIN_DENSE_M to an unquantized
+ * GEMM on the dense copy. The product runs in hipBLASLt (fp32 accumulation,
+ * bias added before the single rounding of C):
+ *   A       [M, lda] act dtype, row-major, lda >= K
+ *   W       [N, ldw] act dtype, row-major, ldw >= K
+ *   bias    [N] act dtype, or NULL
+ *   C       [M, ldc] act dtype, ldc >= N; must not overlap A, W or bias
+ *   workspace, workspace_bytes  optional hipBLASLt workspace (NULL: none)
+ * Every pointer must be 2-byte aligned. M == 0 is a no-op. Unlike the other
+ * calls, this one relies on a library: on the first call on each device it
+ * creates a hipBLASLt handle, which holds host and device state until the
+ * process ends. A hipBLASLt failure returns W4A16_ERR_HIP with the
+ * hipblasStatus_t value in the message. */
+w4a16_status w4a16_gemm_dense(const void *A, int64_t M, int64_t lda, const void *W, int64_t N, int64_t K,
+                              int64_t ldw, int32_t dtype, const void *bias, void *C, int64_t ldc, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,8 @@ library's message on any non-zero status. It never falls back to another
 implementation: without the built library every call raises.
 
 Names follow the C ABI (include/w4a16.h): ``packed_size``, ``repack``,
-``unpack``, ``workspace_size``, ``select_path``, ``gemm``.
+``unpack``, ``workspace_size``, ``select_path``, ``gemm``, and the dense
+prefill variant ``dequant`` and ``gemm_dense``.
 """
 
 from __future__ import annotations
@@ -46,6 +47,11 @@ SIGNATURES = {
     "w4a16_gemm": (
         ctypes.c_int,
         [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _P, _SZ, _P],
+    ),
+    "w4a16_dequant": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _I32, _P, _I64, _P]),
+    "w4a16_gemm_dense": (
+        ctypes.c_int,
+        [_P, _I64, _I64, _P, _I64, _I64, _I64, _I32, _P, _P, _I64, _P, _SZ, _P],
     ),
 }
 
@@ -212,4 +218,45 @@ def gemm(A: torch.Tensor, packed: torch.Tensor, N: int, K: int, group_size: int,
         _ptr(A), M, A.stride(0), _ptr(packed), N, K, group_size, qtype, _DTYPE_CODE[A.dtype], _ptr(bias),
         _ptr(out), out.stride(0), path, skinny_max_m, _ptr(ws) if ws_bytes else None,
         ws.numel() if (ws is not None and ws_bytes) else 0, _stream(A)))
+    return out
+
+
+def dequant(packed: torch.Tensor, N: int, K: int, group_size: int, qtype: int, dtype: torch.dtype,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed buffer -> dense [N, K] weight RN((q - z) * s) in ``dtype`` (fp16 or bf16)."""
+    _need_cuda("packed", packed)
+    if dtype not in _DTYPE_CODE:
+        raise ValueError(f"dtype {dtype} is not fp16 or bf16")
+    if out is None:
+        out = torch.empty((N, K), dtype=dtype, device=packed.device)
+    _need_cuda("out", out, dtype)
+    if out.dim() != 2 or tuple(out.shape) != (N, K) or out.stride(1) != 1:
+        raise ValueError(f"out must be [N={N}, K={K}] with unit column stride")
+    _check(load_library().w4a16_dequant(_ptr(packed), N, K, group_size, qtype, _DTYPE_CODE[dtype], _ptr(out),
+                                        out.stride(0), _stream(packed)))
+    return out
+
+
+def gemm_dense(A: torch.Tensor, W: torch.Tensor, bias: torch.Tensor | None = None,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] = A[M, K] @ W[N, K]^T (+ bias) for a dense weight (e.g. from ``dequant``), via hipBLASLt."""
+    _need_cuda("A", A, (torch.float16, torch.bfloat16))
+    _need_cuda("W", W, A.dtype)
+    _need_cuda("bias", bias, A.dtype)
+    if A.dim() != 2 or A.stride(1) != 1 or W.dim() != 2 or W.stride(1) != 1 or W.shape[1] != A.shape[1]:
+        raise ValueError(f"A [M, K] and W [N, K] need unit column strides and equal K, got {tuple(A.shape)}, {tuple(W.shape)}")
+    M, K = A.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    _need_cuda("out", out, A.dtype)
+    if out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError(f"out must be [M={M}, N={N}] with unit column stride")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != N or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous [N={N}] tensor")
+    _need_cuda("workspace", workspace)
+    _check(load_library().w4a16_gemm_dense(
+        _ptr(A), M, A.stride(0), _ptr(W), N, K, W.stride(0), _DTYPE_CODE[A.dtype], _ptr(bias), _ptr(out),
+        out.stride(0), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(A)))
     return out

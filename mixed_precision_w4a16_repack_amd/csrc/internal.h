@@ -87,5 +87,12 @@ hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* pack
                          hipStream_t stream);
 hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed, const Geometry& g, int dtype,
                        const void* bias, void* C, int64_t ldc, const MfmaPlan& p, hipStream_t stream);
+hipError_t launch_dequant(const void* packed, const Geometry& g, int dtype, void* dense, int64_t ldw,
+                          hipStream_t stream);
+// hipBLASLt GEMM on a dense weight; returns a hipblasStatus_t value (0 on
+// success) and names the failing step in *what.
+int dense_gemm(const void* A, int64_t M, int64_t lda, const void* W, int64_t N, int64_t K, int64_t ldw, int dtype,
+               const void* bias, void* C, int64_t ldc, void* workspace, size_t workspace_bytes, hipStream_t stream,
+               const char** what);
 
 }  // namespace w4a16

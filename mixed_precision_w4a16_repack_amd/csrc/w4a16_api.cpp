@@ -241,4 +241,46 @@ w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packe
     return W4A16_OK;
 }
 
+
+w4a16_status w4a16_dequant(const void* packed, int64_t N, int64_t K, int32_t group_size, int32_t qtype, int32_t dtype,
+                           void* dense, int64_t ldw, hipStream_t stream) {
+    clear_error();
+    Geometry g;
+    w4a16_status st = make_geometry(N, K, group_size, qtype, &g);
+    if (st != W4A16_OK) return st;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+        return fail(W4A16_ERR_INVALID_ARG, "dtype=%d is not a w4a16_dtype (0 fp16, 1 bf16)", dtype);
+    if (packed == nullptr || dense == nullptr) return fail(W4A16_ERR_INVALID_ARG, "packed and dense must not be NULL");
+    if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
+    if (ldw < K) return fail(W4A16_ERR_INVALID_ARG, "ldw=%lld must be >= K=%lld", (long long)ldw, (long long)K);
+    if (!aligned16(dense) || ldw % 8 != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "dense must be 16-byte aligned with ldw %% 8 == 0 (ldw=%lld)", (long long)ldw);
+    hipError_t e = launch_dequant(packed, g, dtype, dense, ldw, stream);
+    if (e != hipSuccess) return hip_fail("dequant kernel launch", e);
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_gemm_dense(const void* A, int64_t M, int64_t lda, const void* dense, int64_t N, int64_t K,
+                              int64_t ldw, int32_t dtype, const void* bias, void* C, int64_t ldc, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    clear_error();
+    if (N <= 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "N=%lld and K=%lld must be positive", (long long)N, (long long)K);
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+        return fail(W4A16_ERR_INVALID_ARG, "dtype=%d is not a w4a16_dtype (0 fp16, 1 bf16)", dtype);
+    if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M=%lld must be >= 0", (long long)M);
+    if (M == 0) return W4A16_OK;
+    if (A == nullptr || dense == nullptr || C == nullptr)
+        return fail(W4A16_ERR_INVALID_ARG, "A, dense and C must not be NULL");
+    if (lda < K) return fail(W4A16_ERR_INVALID_ARG, "lda=%lld must be >= K=%lld", (long long)lda, (long long)K);
+    if (ldw < K) return fail(W4A16_ERR_INVALID_ARG, "ldw=%lld must be >= K=%lld", (long long)ldw, (long long)K);
+    if (ldc < N) return fail(W4A16_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc, (long long)N);
+    if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(dense) | reinterpret_cast<uintptr_t>(C) |
+         reinterpret_cast<uintptr_t>(bias)) & 1u)
+        return fail(W4A16_ERR_INVALID_ARG, "A, dense, C and bias must be 2-byte aligned");
+    const char* what = "";
+    const int bst = dense_gemm(A, M, lda, dense, N, K, ldw, dtype, bias, C, ldc, workspace, workspace_bytes, stream, &what);
+    if (bst != 0) return fail(W4A16_ERR_HIP, "%s failed: hipblasStatus %d", what, bst);
+    return W4A16_OK;
+}
+
 }  // extern "C"

@@ -160,3 +160,62 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(w4, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         w4.load_library(str(tmp_path / "libw4a16.so"))
+
+
+def _dequant(lib, **kw):
+    args = dict(packed=ctypes.c_void_p(4096), N=4096, K=4096, G=128, qtype=0, dtype=1, dense=ctypes.c_void_p(8192),
+                ldw=4096)
+    args.update(kw)
+    return lib.w4a16_dequant(args["packed"], args["N"], args["K"], args["G"], args["qtype"], args["dtype"],
+                             args["dense"], args["ldw"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,needle",
+    [
+        (dict(dtype=2), INVALID, "dtype=2"),
+        (dict(K=4000, ldw=4000), UNSUPPORTED, "K=4000 must be divisible by 128"),
+        (dict(packed=None), INVALID, "must not be NULL"),
+        (dict(dense=None), INVALID, "must not be NULL"),
+        (dict(packed=ctypes.c_void_p(4100)), INVALID, "256-byte aligned"),
+        (dict(ldw=4000), INVALID, "ldw=4000 must be >= K=4096"),
+        (dict(ldw=4100), UNSUPPORTED, "ldw % 8 == 0"),
+        (dict(dense=ctypes.c_void_p(8200)), UNSUPPORTED, "16-byte aligned"),
+    ],
+)
+def test_dequant_rejects_before_any_hip_call(lib, kw, status, needle):
+    assert _dequant(lib, **kw) == status
+    assert needle in w4.last_error()
+
+
+def _gemm_dense(lib, **kw):
+    args = dict(A=ctypes.c_void_p(4096), M=2048, lda=4096, W=ctypes.c_void_p(8192), N=4096, K=4096, ldw=4096,
+                dtype=1, bias=None, C=ctypes.c_void_p(16384), ldc=4096, ws=None, wsb=0)
+    args.update(kw)
+    return lib.w4a16_gemm_dense(args["A"], args["M"], args["lda"], args["W"], args["N"], args["K"], args["ldw"],
+                                args["dtype"], args["bias"], args["C"], args["ldc"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,needle",
+    [
+        (dict(dtype=3), INVALID, "dtype=3"),
+        (dict(M=-2), INVALID, "M=-2"),
+        (dict(N=0), INVALID, "must be positive"),
+        (dict(A=None), INVALID, "must not be NULL"),
+        (dict(W=None), INVALID, "must not be NULL"),
+        (dict(C=None), INVALID, "must not be NULL"),
+        (dict(lda=100), INVALID, "lda=100 must be >= K=4096"),
+        (dict(ldw=100), INVALID, "ldw=100 must be >= K=4096"),
+        (dict(ldc=100), INVALID, "ldc=100 must be >= N=4096"),
+        (dict(bias=ctypes.c_void_p(4097)), INVALID, "2-byte aligned"),
+    ],
+)
+def test_gemm_dense_rejects_before_any_hip_call(lib, kw, status, needle):
+    assert _gemm_dense(lib, **kw) == status
+    assert needle in w4.last_error()
+
+
+def test_gemm_dense_m_zero_is_a_noop(lib):
+    assert _gemm_dense(lib, M=0) == OK
+    assert w4.last_error() == ""

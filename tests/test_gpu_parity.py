@@ -365,3 +365,76 @@ def test_identity_through_full_k(N, dtype, qtype, G):
     expect = torch.from_numpy(W.T.copy()).to(case.torch_dtype)
     bad = (C.cpu().view(torch.int16) != expect.view(torch.int16)).sum().item()
     assert bad == 0, f"{bad} of {C.numel()} values differ from RN((q - z) * s)"
+
+
+# ------------------------------------------------------------------ dense prefill variant
+# (dequantise once into a dense weight, then a library GEMM on it)
+
+
+DEQUANT = [
+    # (N, K, G, qtype, dtype, pad): pad = extra columns of the dense rows (ldw = K + pad)
+    (16, 128, 128, UINT4B8, "f16", 0),
+    (48, 256, 32, UINT4, "bf16", 8),
+    (272, 512, 64, UINT4B8, "bf16", 0),
+    (4096, 1024, -1, UINT4, "f16", 64),
+    (14336, 4096, 256, UINT4B8, "bf16", 0),
+    (6144, 4096, 32, UINT4, "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("N,K,G,qtype,dtype,pad", DEQUANT,
+                         ids=[f"{c[0]}x{c[1]}g{c[2]}q{c[3]}-{c[4]}-pad{c[5]}" for c in DEQUANT])
+def test_dequant_bit_exact(N, K, G, qtype, dtype, pad):
+    # Every dense value must be RN_act((q - z) * s) bit for bit (q - z is a
+    # small integer, so the product is exact before its one rounding).
+    print(f"[case] dequant N={N} K={K} G={G} qtype={qtype} {dtype} pad={pad}", flush=True)
+    case = _case(26, 1, N, K, G, qtype, dtype)
+    packed = repack(case)
+    big = torch.full((N, K + pad), 3.0, dtype=case.torch_dtype, device=DEV)
+    w4.dequant(packed, N, K, G, qtype, case.torch_dtype, out=big[:, :K])
+    W = oracle.dequant(case.weight_packed, case.weight_scale, case.weight_zero_point, qtype, G)
+    expect = torch.from_numpy(W).to(case.torch_dtype)
+    got = big[:, :K].cpu()
+    bad = (got.view(torch.int16) != expect.view(torch.int16)).sum().item()
+    assert bad == 0, f"{bad} of {got.numel()} values differ from RN((q - z) * s)"
+    if pad:
+        assert torch.all(big[:, K:] == 3.0), "wrote outside [N, K]"
+
+
+DENSE_GEMM = [
+    # (M, N, K, G, qtype, dtype, bias)
+    (300, 400, 640, 64, UINT4, "f16", True),
+    (2048, 14336, 4096, 256, UINT4B8, "bf16", False),
+    (2048, 4096, 14336, -1, UINT4, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,qtype,dtype,bias", DENSE_GEMM,
+                         ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-G{c[3]}-q{c[4]}-{c[5]}" for c in DENSE_GEMM])
+def test_dense_prefill_parity(M, N, K, G, qtype, dtype, bias):
+    print(f"[case] dense M={M} N={N} K={K} G={G} qtype={qtype} {dtype} bias={bias}", flush=True)
+    case = _case(27, M, N, K, G, qtype, dtype, with_bias=bias)
+    packed = repack(case)
+    _, _, _, A, b = to_dev(case)
+    Wd = w4.dequant(packed, N, K, G, qtype, case.torch_dtype)
+    C = w4.gemm_dense(A, Wd, bias=b)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    err = rel_err_rows(C, oracle_ref(case, rows=rows), rows)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
+
+
+def test_dense_gemm_strides():
+    # A, W and C with row strides beyond their widths; C's padding untouched.
+    M, N, K, G = 64, 256, 512, 128
+    case = _case(28, M, N, K, G, UINT4B8, "bf16", with_bias=True)
+    packed = repack(case)
+    _, _, _, A, b = to_dev(case)
+    A_big = torch.zeros((M, K + 32), dtype=torch.bfloat16, device=DEV)
+    A_big[:, :K] = A
+    W_big = torch.zeros((N, K + 16), dtype=torch.bfloat16, device=DEV)
+    w4.dequant(packed, N, K, G, UINT4B8, torch.bfloat16, out=W_big[:, :K])
+    C_big = torch.full((M, N + 24), 7.0, dtype=torch.bfloat16, device=DEV)
+    w4.gemm_dense(A_big[:, :K], W_big[:, :K], bias=b, out=C_big[:, :N])
+    assert oracle.rel_err(C_big[:, :N].cpu(), oracle_ref(case)) <= oracle.TOLERANCE["bf16"]
+    assert torch.all(C_big[:, N:] == 7.0), "wrote outside [M, N]"
