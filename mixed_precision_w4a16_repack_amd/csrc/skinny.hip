@@ -575,29 +575,29 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
         }
     }
 
-    // 4. Multiply and fold, n-tile by n-tile.
+    // 4. Multiply and fold, n-tile by n-tile. k-tiles past the wave's kc are
+    //    computed too, without a branch (their activations and scales read as
+    //    zeros, so they add exactly 0 to rows < M), so the chains of a wave's
+    //    k-tiles can interleave.
 #pragma unroll
     for (int i = 0; i < NNM; ++i) {
-        if (i < nn) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (i >= nn) continue;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < KTM; ++j) {
-                if (j < kc) {
+        for (int j = 0; j < KTM; ++j) {
 #pragma unroll
-                    for (int f = 0; f < NB; ++f) {
-                        floatx4 P = QT ? floatx4{0.f, 0.f, 0.f, 0.f} : S[j][f];
+            for (int f = 0; f < NB; ++f) {
+                floatx4 P = QT ? floatx4{0.f, 0.f, 0.f, 0.f} : S[j][f];
 #pragma unroll
-                        for (int ww = 0; ww < FW; ++ww) {
-                            const int word = f * FW + ww;
-                            P = mfma16x16x32<DT>(af[j][word], magic_operand(w[i][j][word], dq_mask, dq_magic), P);
-                        }
-                        if (QT) fold<DT, QT>(acc, P, S[j][f], sb[i][j][f], zb[i][j][f]);
-                        else fold_scaled<DT>(acc, P, sb[i][j][f]);
-                    }
+                for (int ww = 0; ww < FW; ++ww) {
+                    const int word = f * FW + ww;
+                    P = mfma16x16x32<DT>(af[j][word], magic_operand(w[i][j][word], dq_mask, dq_magic), P);
                 }
+                if (QT) fold<DT, QT>(acc, P, S[j][f], sb[i][j][f], zb[i][j][f]);
+                else fold_scaled<DT>(acc, P, sb[i][j][f]);
             }
-            red[(wave * nn + i) * 64 + lane] = acc;
         }
+        red[(wave * nn + i) * 64 + lane] = acc;
     }
     __syncthreads();
     if (a.ksplit == 1) finish_tiles<DT>(a, red, nn, nwaves, g, a.n_groups);
@@ -670,7 +670,8 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
     }
 
     // 4. k-tile by k-tile: the activation fragments (padding rows read row
-    //    M-1) and S once, then every n-tile.
+    //    M-1) and S once, then every n-tile. P starts from zero, so the S
+    //    and P chains of a k-tile do not wait for each other.
     const u32x4 ones = ones_operand<DT>();
     floatx4 acc[NNM];
 #pragma unroll
@@ -687,21 +688,19 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
                 S[f] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ww = 0; ww < FW; ++ww) S[f] = mfma16x16x32<DT>(af[f * FW + ww], ones, S[f]);
-                if (!QT) S[f] *= -(magic_base<DT>() + 8.0f);  // uint4b8: the start value T = -(m + 8) * S
             }
 #pragma unroll
             for (int i = 0; i < NNM; ++i) {
                 if (i < nn) {
 #pragma unroll
                     for (int f = 0; f < NB; ++f) {
-                        floatx4 P = QT ? floatx4{0.f, 0.f, 0.f, 0.f} : S[f];
+                        floatx4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int ww = 0; ww < FW; ++ww) {
                             const int word = f * FW + ww;
                             P = mfma16x16x32<DT>(af[word], magic_operand(w[j][i][word], dq_mask, dq_magic), P);
                         }
-                        if (QT) fold<DT, QT>(acc[i], P, S[f], sb[j][i][f], zb[j][i][f]);
-                        else fold_scaled<DT>(acc[i], P, sb[j][i][f]);
+                        fold<DT, QT>(acc[i], P, S[f], sb[j][i][f], zb[j][i][f]);
                     }
                 }
             }
