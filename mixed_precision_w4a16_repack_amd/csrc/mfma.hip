@@ -48,6 +48,7 @@ struct MfmaArgs {
     int64_t ldc;
     int64_t m_tiles, n_blocks;
     uint32_t a_bytes, codes_bytes, scales_bytes, zeros_bytes;  // buffer extents (mfma_lds_kernel)
+    int64_t tile0;  // mfma_ring_kernel: first 128 x 256 tile (row-major over m-tiles x n-blocks)
 };
 
 template <int DT, int QT, int BM, int WNT, int SPT>
@@ -482,11 +483,12 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
 //    sum_g s_g * P_g without ever clearing P, and the correction
 //    -s_g * (m+z_g) * S_g is applied one step later, once the row sums of
 //    the group have passed the step's barrier.
-template <int DT, int QT, int OCM>
+template <int DT, int QT, int OCM, int BM>
 __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     static_assert(OCM == 1 || OCM == 2, "offset-corrected modes only");
-    constexpr int BM = 128, WN = 4, MI = 4, NJ = 4;
-    constexpr int ABLK = 32, BBLK = 16;             // 1 KB blocks per stage
+    static_assert(BM == 128 || BM == 64, "whole or half tiles");
+    constexpr int WN = 4, MI = BM / 32, NJ = 4;
+    constexpr int ABLK = BM / 4, BBLK = 16;         // 1 KB blocks per stage
     constexpr int APW = ABLK / 8, BPW = BBLK / 8;   // blocks loaded per wave
     constexpr int NSC = OCM == 2 ? NJ * (1 + QT) : 0;  // scale/zero loads per wave per step
     constexpr int STAGE_LOADS = APW + BPW + NSC;
@@ -503,10 +505,14 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave - wm * WN;
     const int r = lane & 15, g4 = lane >> 4;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    // Tile of the workgroup: 128 x 256 tile a.tile0 + blockIdx.x, or with
+    // BM = 64 half (blockIdx.x & 1) of tile a.tile0 + blockIdx.x / 2.
+    const int64_t lin = a.tile0 + (BM == 128 ? (int64_t)blockIdx.x : (int64_t)(blockIdx.x >> 1));
+    const int64_t ty = lin / a.n_blocks, tx = lin - ty * a.n_blocks;
+    const int64_t m0 = ty * 128 + (BM == 64 ? (int64_t)(blockIdx.x & 1) * 64 : 0);
     const int64_t NT = a.N / 16;
     const int64_t steps = a.KTT;
-    const int64_t ntb = (int64_t)blockIdx.x * 16;  // first n-tile of the workgroup
+    const int64_t ntb = tx * 16;  // first n-tile of the workgroup
 
     auto rsrc = [&](const void* base, uint32_t bytes, bool live) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
@@ -542,7 +548,8 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
                      uint32_t (&zb)[NJ]) {
         const bool live = st < steps;
         const int b = wave * APW + p;
-        load_lds16(rsrc(a.A, a.a_bytes, live), abuf + b * 1024, a_off[p], (uint32_t)((st * 128 + 32 * (b & 3)) * 2));
+        if (p < APW)
+            load_lds16(rsrc(a.A, a.a_bytes, live), abuf + b * 1024, a_off[p], (uint32_t)((st * 128 + 32 * (b & 3)) * 2));
         if (p < BPW)
             load_lds16(rsrc(a.codes, a.codes_bytes, live), bbuf + (wave * BPW + p) * 1024, lane16,
                        (uint32_t)((b_tile[p] * a.KTT + st) * 1024));
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
             }
         }
     };
-    static_assert(APW == 4 && BPW <= 2, "one activation block per K slice");
+    static_assert(APW <= 4 && BPW <= 2, "at most one activation block per K slice");
 
     uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
@@ -578,7 +585,9 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     const u32x4 ones = {one2, one2, one2, one2};
     constexpr float kM = DT == 0 ? 1024.0f : 128.0f;
 
-    floatx4 acc[MI][NJ], S = {0.f, 0.f, 0.f, 0.f};  // S: row block wn of the half
+    // S: row block wn % MI of the wave's half (with half tiles two waves
+    // sum each row block; the sums read back are those of waves 0..MI-1).
+    floatx4 acc[MI][NJ], S = {0.f, 0.f, 0.f, 0.f};
     floatx4 P[OCM == 2 ? MI : 1][OCM == 2 ? NJ : 1];
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -637,7 +646,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
                 for (int j = 0; j < NJ; ++j) dequant_pair(raw[j][s], raw[j][s + 1], bq2[0][j], bq2[1][j]);
             }
             const u32x4 (&bq)[NJ] = bq2[s & 1];
-            const u32x4 as = *reinterpret_cast<const u32x4*>(abase + ((wm * MI + wn) * 4 + s) * 1024);
+            const u32x4 as = *reinterpret_cast<const u32x4*>(abase + ((wm * MI + wn % MI) * 4 + s) * 1024);
             S = mfma16x16x32<DT>(as, ones, S);
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
@@ -723,7 +732,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
         for (int i = 0; i < MI; ++i) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int64_t m = m0 + wm * 64 + 16 * i + 4 * g4 + jj;
+                const int64_t m = m0 + wm * (BM / 2) + 16 * i + 4 * g4 + jj;
                 float v = acc[i][j][jj];
                 if (OCM == 1) v = sf * __builtin_fmaf(zf, Sf[i][jj], v);
                 if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
@@ -732,12 +741,32 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     }
 }
 
-template <int DT, int QT>
-hipError_t launch_ring_t(const MfmaArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)((a.M + 127) / 128));
-    if (a.one_group) hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, 1>), grid, dim3(512), 0, stream, a);
-    else hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, 2>), grid, dim3(512), 0, stream, a);
+template <int DT, int QT, int OCM>
+hipError_t launch_ring_ocm(MfmaArgs a, hipStream_t stream) {
+    // 128 x 256 tiles, row-major over m-tiles x n-blocks, one workgroup per
+    // CU at a time. When the last round of workgroups would be at most half
+    // full, its tiles run as 64-row halves in a second launch: twice the
+    // workgroups at half the work each, so the last round takes half as long.
+    const int64_t tiles = a.m_tiles * a.n_blocks;
+    const int64_t tail = tiles % kCUs;
+    const int64_t full = tiles > kCUs && tail > 0 && 2 * tail <= kCUs ? tiles - tail : tiles;
+    a.tile0 = 0;
+    hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, OCM, 128>), dim3((unsigned)full), dim3(512), 0, stream, a);
+    if (full < tiles) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        a.tile0 = full;
+        hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, OCM, 64>), dim3((unsigned)(2 * (tiles - full))), dim3(512), 0,
+                           stream, a);
+    }
     return hipGetLastError();
+}
+
+template <int DT, int QT>
+hipError_t launch_ring_t(MfmaArgs a, hipStream_t stream) {
+    a.m_tiles = (a.M + 127) / 128;
+    a.n_blocks = (a.N + 255) / 256;
+    return a.one_group ? launch_ring_ocm<DT, QT, 1>(a, stream) : launch_ring_ocm<DT, QT, 2>(a, stream);
 }
 
 template <int DT, int QT, int BM, int WM, int NJ, int KS>

@@ -294,7 +294,8 @@ def test_skinny_k_extremes(K):
 
 
 # 128 x 256 tiles on the three-stage ring (at least 256 workgroups, one group
-# per row or groups of 128 k or more). Each case names the edge it reaches.
+# per row or groups of 128 k or more; a last round at most half full runs as
+# 64-row halves). Each case names the edge it reaches.
 RING = [
     # (M, N, K, G, qtype, dtype, bias)
     (2048, 4096, 128, -1, UINT4B8, "bf16", False),  # one K step: only the loop tail runs
@@ -302,6 +303,8 @@ RING = [
     (4096, 4096, 512, 128, UINT4B8, "f16", False),  # a group per step, tail of 1
     (2048, 8192, 1536, 256, UINT4, "bf16", True),   # 2 steps per group, 12 steps: no tail
     (1930, 8192, 896, -1, UINT4, "f16", False),     # 7 steps: tail of 1, ragged M
+    (2048, 14336, 512, 256, UINT4, "bf16", True),   # 896 tiles: the last 128 as 64-row halves
+    (1990, 14336, 256, -1, UINT4B8, "f16", False),  # halves over m-tiles 13-15, ragged M
 ]
 
 
