@@ -154,7 +154,9 @@ int32_t w4a16_select_path(int64_t M, int32_t path, int32_t skinny_max_m);
  * on earlier calls (no float atomics: the order of every sum is fixed).
  * The skinny kernel addresses the (at most 16) rows of one launch with 32-bit
  * byte offsets: it returns W4A16_ERR_UNSUPPORTED when
- * ((min(M, 16) - 1) * lda + K) * 2 >= 2^31. */
+ * ((min(M, 16) - 1) * lda + K) * 2 >= 2^31. The tiled kernel does the same
+ * per workgroup tile (A and the weight may be of any size): it returns
+ * W4A16_ERR_UNSUPPORTED when (128 * lda + K) * 2 >= 2^31. */
 w4a16_status w4a16_gemm(const void *A, int64_t M, int64_t lda, const void *packed, int64_t N, int64_t K,
                         int32_t group_size, int32_t qtype, int32_t dtype, const void *bias, void *C, int64_t ldc,
                         int32_t path, int32_t skinny_max_m, void *workspace, size_t workspace_bytes,

@@ -48,9 +48,8 @@ struct SkinnyPlan {
 
 // Tiled MFMA launch plan.
 struct MfmaPlan {
-    bool lds = false;  // activation tile loaded straight into LDS (mfma_lds_kernel)
-    int BM = 256;      // rows per workgroup
-    int BN = 256;      // columns per workgroup
+    int BM = 128;  // rows per workgroup
+    int BN = 256;  // columns per workgroup
 };
 
 // Raises a kernel's dynamic-LDS limit (needed above 64 KB); cached per kernel

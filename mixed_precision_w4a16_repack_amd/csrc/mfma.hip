@@ -18,8 +18,8 @@
 //    medium M) and groups of 32 or 64 k (scale first, per weight, as the
 //    pages do); activation tiles go straight into two LDS buffers, the
 //    weights into registers.
-//  * mfma_kernel: the fallback when an operand is too large for the 32-bit
-//    offsets of buffer loads.
+// Both address a workgroup's operands through buffer descriptors based at
+// its own tile, so A and the packed weight may be of any size.
 // Every kernel stages activations in LDS in "fragment order" (1 KB per
 // 16 rows x 32 k, lane l's 16 bytes at 16*l) so that each A-operand read is
 // one conflict-free ds_read_b128, reads the packed weight tiles, which are
@@ -47,152 +47,8 @@ struct MfmaArgs {
     uint16_t* C;
     int64_t ldc;
     int64_t m_tiles, n_blocks;
-    uint32_t a_bytes, codes_bytes, scales_bytes, zeros_bytes;  // buffer extents (mfma_lds_kernel)
     int64_t tile0;  // mfma_ring_kernel: first 128 x 256 tile (row-major over m-tiles x n-blocks)
 };
-
-template <int DT, int QT, int BM, int WNT, int SPT>
-__global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
-    constexpr int MB = BM / 16;            // 16-row blocks per tile
-    constexpr int CHUNKS = MB * 4;         // 1 KB A chunks per K step
-    constexpr int CPW = CHUNKS / 4;        // chunks loaded per wave
-    constexpr int BUF_BYTES = BM * 128 * 2;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int r = lane & 15, g4 = lane >> 4;
-
-    const int64_t b = blockIdx.x;
-    const int64_t nb_idx = b % a.n_blocks;
-    const int64_t mt = b / a.n_blocks;
-    const int64_t m0 = mt * BM;
-    const int64_t NT = a.N / 16;
-
-    // This wave's n-tiles (clamped for loads when N is not a multiple of the
-    // workgroup width; clamped tiles are never stored).
-    int64_t nt_of[WNT];
-    int64_t nt_ld[WNT];
-#pragma unroll
-    for (int nb = 0; nb < WNT; ++nb) {
-        nt_of[nb] = nb_idx * (4 * WNT) + wave * WNT + nb;
-        nt_ld[nb] = nt_of[nb] < NT ? nt_of[nb] : NT - 1;
-    }
-
-    // A chunk c = wave * CPW + i covers rows 16*(c/4) .. +15, k 32*(c%4) .. +31
-    // of the current K step; lane l loads row 16*(c/4) + l%16 (clamped to
-    // M - 1) at k offset 32*(c%4) + 8*(l/16).
-    const uint16_t* a_src[CPW];
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int c = wave * CPW + i;
-        int64_t row = m0 + 16 * (c >> 2) + r;
-        if (row > a.M - 1) row = a.M - 1;
-        a_src[i] = a.A + row * a.lda + 32 * (c & 3) + 8 * g4;
-    }
-
-    auto load_a = [&](int64_t kt, u32x4 (&regs)[CPW]) {
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) regs[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * 128);
-    };
-    auto store_a = [&](int buf, const u32x4 (&regs)[CPW]) {
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int c = wave * CPW + i;
-            *reinterpret_cast<u32x4*>(smem + buf * BUF_BYTES + (c * 64 + lane) * 16) = regs[i];
-        }
-    };
-    auto load_b = [&](int64_t kt, u32x4 (&raw)[WNT], uint16_t (&sb)[WNT][SPT], uint8_t (&zb)[WNT][SPT]) {
-#pragma unroll
-        for (int nb = 0; nb < WNT; ++nb) {
-            raw[nb] = __builtin_nontemporal_load(a.codes + (nt_ld[nb] * a.KTT + kt) * 64 + lane);
-#pragma unroll
-            for (int u = 0; u < SPT; ++u) {
-                const int64_t k = kt * 128 + u * (128 / SPT);
-                const int64_t g = a.one_group ? 0 : (k >> a.gshift);
-                const int64_t idx = (nt_ld[nb] * a.Kg + g) * 16 + r;
-                sb[nb][u] = a.scales[idx];
-                zb[nb][u] = QT ? a.zeros[idx] : (uint8_t)8;
-            }
-        }
-    };
-
-    // Dequant operands in registers (see and_or).
-    uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
-    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
-
-    floatx4 acc[MB][WNT];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < WNT; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 areg[CPW];
-    u32x4 braw[WNT];
-    uint16_t sb[WNT][SPT];
-    uint8_t zb[WNT][SPT];
-    load_a(0, areg);
-    load_b(0, braw, sb, zb);
-    store_a(0, areg);
-    __syncthreads();
-
-    for (int64_t kt = 0; kt < a.KTT; ++kt) {
-        const int buf = (int)(kt & 1);
-        const bool more = kt + 1 < a.KTT;
-        u32x4 braw_n[WNT];
-        uint16_t sb_n[WNT][SPT];
-        uint8_t zb_n[WNT][SPT];
-        if (more) {
-            load_a(kt + 1, areg);
-            load_b(kt + 1, braw_n, sb_n, zb_n);
-        }
-        const unsigned char* abase = smem + buf * BUF_BYTES + lane * 16;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            u32x4 bq[WNT];
-#pragma unroll
-            for (int nb = 0; nb < WNT; ++nb) {
-                const int u = s / (4 / SPT);
-                bq[nb] = Dequant<DT>::apply(braw[nb][s], Dequant<DT>::make(sb[nb][u], zb[nb][u]), dq_mask, dq_magic);
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const u32x4 av = *reinterpret_cast<const u32x4*>(abase + (mb * 4 + s) * 1024);
-#pragma unroll
-                for (int nb = 0; nb < WNT; ++nb) acc[mb][nb] = mfma16x16x32<DT>(av, bq[nb], acc[mb][nb]);
-            }
-        }
-        if (more) {
-            store_a(buf ^ 1, areg);
-#pragma unroll
-            for (int nb = 0; nb < WNT; ++nb) {
-                braw[nb] = braw_n[nb];
-#pragma unroll
-                for (int u = 0; u < SPT; ++u) {
-                    sb[nb][u] = sb_n[nb][u];
-                    zb[nb][u] = zb_n[nb][u];
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l%16 of each block.
-#pragma unroll
-    for (int nb = 0; nb < WNT; ++nb) {
-        if (nt_of[nb] >= NT) continue;
-        const int64_t n = nt_of[nb] * 16 + r;
-        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int64_t m = m0 + 16 * mb + 4 * g4 + jj;
-                if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(acc[mb][nb][jj] + bv);
-            }
-        }
-    }
-}
 
 // 16 bytes per lane from buffer `rs` (lane offset voff + scalar offset soff)
 // straight into LDS at dst + 16 * lane (dst wave-uniform). dst keeps its
@@ -220,6 +76,40 @@ __device__ __forceinline__ void wait_vmcnt() {
 // moving memory operations across it.
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One workgroup's operands as buffer bases and byte extents: rows
+// [mb, mb + rows) of A with mb = min(m0, M - 1) (a half tile may start past
+// a ragged M; its rows then all clamp to M - 1 >= mb), and n-tiles
+// [nt0, nt0 + ntn) of the packed weight (nt0 < N/16).
+// The kernels form 32-bit offsets from these per-workgroup bases, which stay
+// below 2^31 whatever the sizes of A and of the weight (the host checks
+// (128 * lda + K) * 2 < 2^31, which with lda >= K also bounds the 128*K bytes
+// of codes of 16 n-tiles).
+struct TileBufs {
+    int64_t mb;  // row of A at the base
+    const uint16_t* A;
+    const u32x4* codes;
+    const uint16_t* scales;
+    const uint8_t* zeros;
+    uint32_t a_bytes, codes_bytes, scales_bytes, zeros_bytes;
+};
+
+__device__ __forceinline__ TileBufs tile_bufs(const MfmaArgs& a, int64_t m0, int64_t rows, int64_t nt0, int64_t ntn) {
+    const int64_t NT = a.N / 16;
+    TileBufs t;
+    t.mb = m0 < a.M - 1 ? m0 : a.M - 1;
+    const int64_t mr = a.M - t.mb < rows ? a.M - t.mb : rows;  // >= 1 rows of A
+    const int64_t nn = NT - nt0 < ntn ? NT - nt0 : ntn;        // >= 1 n-tiles
+    t.A = a.A + t.mb * a.lda;
+    t.a_bytes = (uint32_t)(((mr - 1) * a.lda + a.KTT * 128) * 2);
+    t.codes = a.codes + nt0 * a.KTT * 64;
+    t.codes_bytes = (uint32_t)(nn * a.KTT * 1024);
+    t.scales = a.scales + nt0 * a.Kg * 16;
+    t.scales_bytes = (uint32_t)(nn * a.Kg * 32);
+    t.zeros = a.zeros != nullptr ? a.zeros + nt0 * a.Kg * 16 : nullptr;
+    t.zeros_bytes = a.zeros != nullptr ? (uint32_t)(nn * a.Kg * 16) : 0u;
+    return t;
 }
 
 // Tiled variant with the activation tile loaded straight into LDS.
@@ -278,6 +168,10 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
     };
 
+    // The workgroup's operands, based at its tile (offsets below 2^31).
+    const int64_t ntw = (int64_t)blockIdx.x * (BN / 16);  // first n-tile of the workgroup
+    const TileBufs tb = tile_bufs(a, m0, BM, ntw, BN / 16);
+
     // Activation blocks this wave stages: block b = wave*BPW + t is row
     // block rb = b / (4*KS), k-tile kk = (b / 4) % KS, word s = b % 4 of the
     // step: rows m0 + 16*rb + (0..15), k 128*kk + 32*s + (0..31). Lane l
@@ -288,7 +182,7 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         const int b = wave * BPW + t;
         int64_t row = m0 + 16 * (b / (4 * KS)) + r;
         if (row > a.M - 1) row = a.M - 1;
-        a_off[t] = (uint32_t)((row * a.lda + 8 * g4) * 2);
+        a_off[t] = (uint32_t)(((row - tb.mb) * a.lda + 8 * g4) * 2);
     }
     auto stage_a = [&](int64_t st, int buf, bool live) {
 #pragma unroll
@@ -296,13 +190,13 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
             const int b = wave * BPW + t;
             const int kk = (b / 4) % KS, s = b % 4;
             const int64_t kt = st * KS + kk;
-            const __amdgpu_buffer_rsrc_t rs_a = rsrc(a.A, a.a_bytes, live && kt < a.KTT);
+            const __amdgpu_buffer_rsrc_t rs_a = rsrc(tb.A, tb.a_bytes, live && kt < a.KTT);
             load_lds16(rs_a, (buf ? abuf1 : abuf0) + b * 1024, a_off[t], (uint32_t)((kt * 128 + 32 * s) * 2));
         }
     };
 
     // This wave's n-tiles (clamped for loads past N; never stored).
-    const int64_t nt0 = (int64_t)blockIdx.x * (BN / 16) + wn * NJ;
+    const int64_t nt0 = ntw + wn * NJ;
     auto nt_ld = [&](int j) { return nt0 + j < NT ? nt0 + j : NT - 1; };
     const uint32_t lane16 = (uint32_t)lane * 16;
     // Scales and zeros stay one per 32-bit register: packing two freshly
@@ -316,12 +210,12 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         for (int kk = 0; kk < KS; ++kk) {
             const int64_t kt = st * KS + kk;
             const bool ok = live && kt < a.KTT;
-            const __amdgpu_buffer_rsrc_t rs_c = rsrc(a.codes, a.codes_bytes, ok);
-            const __amdgpu_buffer_rsrc_t rs_s = rsrc(a.scales, a.scales_bytes, ok);
-            const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.zeros, a.zeros_bytes, ok);
+            const __amdgpu_buffer_rsrc_t rs_c = rsrc(tb.codes, tb.codes_bytes, ok);
+            const __amdgpu_buffer_rsrc_t rs_s = rsrc(tb.scales, tb.scales_bytes, ok);
+            const __amdgpu_buffer_rsrc_t rs_z = rsrc(tb.zeros, tb.zeros_bytes, ok);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int64_t nt = nt_ld(j);
+                const int64_t nt = nt_ld(j) - ntw;  // relative to the workgroup's first n-tile
                 raw[j][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                            rs_c, lane16, (uint32_t)((nt * a.KTT + kt) * 1024), 2));
 #pragma unroll
@@ -513,6 +407,8 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     const int64_t NT = a.N / 16;
     const int64_t steps = a.KTT;
     const int64_t ntb = tx * 16;  // first n-tile of the workgroup
+    // The workgroup's operands, based at its tile (offsets below 2^31).
+    const TileBufs tb = tile_bufs(a, m0, BM, ntb, 16);
 
     auto rsrc = [&](const void* base, uint32_t bytes, bool live) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
@@ -526,14 +422,15 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
         const int b = wave * APW + t;
         int64_t row = m0 + 16 * (b >> 2) + r;
         if (row > a.M - 1) row = a.M - 1;
-        a_off[t] = (uint32_t)((row * a.lda + 8 * g4) * 2);
+        a_off[t] = (uint32_t)(((row - tb.mb) * a.lda + 8 * g4) * 2);
     }
-    // Weight block b = wave*BPW + t: n-tile ntb + b (clamped; never stored).
+    // Weight block b = wave*BPW + t: n-tile ntb + b (clamped; never stored),
+    // as an index relative to ntb.
     uint32_t b_tile[BPW];
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
         const int64_t nt = ntb + wave * BPW + t;
-        b_tile[t] = (uint32_t)(nt < NT ? nt : NT - 1);
+        b_tile[t] = (uint32_t)((nt < NT ? nt : NT - 1) - ntb);
     }
     const uint32_t lane16 = (uint32_t)lane * 16;
     auto nt_of = [&](int j) { return ntb + wn * NJ + j; };
@@ -549,17 +446,17 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
         const bool live = st < steps;
         const int b = wave * APW + p;
         if (p < APW)
-            load_lds16(rsrc(a.A, a.a_bytes, live), abuf + b * 1024, a_off[p], (uint32_t)((st * 128 + 32 * (b & 3)) * 2));
+            load_lds16(rsrc(tb.A, tb.a_bytes, live), abuf + b * 1024, a_off[p], (uint32_t)((st * 128 + 32 * (b & 3)) * 2));
         if (p < BPW)
-            load_lds16(rsrc(a.codes, a.codes_bytes, live), bbuf + (wave * BPW + p) * 1024, lane16,
+            load_lds16(rsrc(tb.codes, tb.codes_bytes, live), bbuf + (wave * BPW + p) * 1024, lane16,
                        (uint32_t)((b_tile[p] * a.KTT + st) * 1024));
         if (OCM == 2 && p == 2) {
-            const __amdgpu_buffer_rsrc_t rs_s = rsrc(a.scales, a.scales_bytes, live);
-            const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.zeros, a.zeros_bytes, live);
+            const __amdgpu_buffer_rsrc_t rs_s = rsrc(tb.scales, tb.scales_bytes, live);
+            const __amdgpu_buffer_rsrc_t rs_z = rsrc(tb.zeros, tb.zeros_bytes, live);
             const int64_t g = (st * 128) >> a.gshift;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const uint32_t so = (uint32_t)((nt_ld(j) * a.Kg + g) * 16);
+                const uint32_t so = (uint32_t)(((nt_ld(j) - ntb) * a.Kg + g) * 16);
                 sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)r * 2, so * 2, 0);
                 if (QT) zb[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, (uint32_t)r, so, 0);
             }
@@ -791,75 +688,35 @@ hipError_t launch_lds_t(const MfmaArgs& a, int spt, hipStream_t stream) {
 }
 
 
-template <int DT, int QT, int BM, int WNT>
-hipError_t launch_mfma_t(const MfmaArgs& a, int spt, dim3 grid, hipStream_t stream) {
-    const size_t lds = 2 * (size_t)BM * 128 * 2;
-    hipError_t e = hipSuccess;
-    switch (spt) {
-        case 1:
-            e = allow_lds<mfma_kernel<DT, QT, BM, WNT, 1>>(lds);
-            if (e == hipSuccess) hipLaunchKernelGGL((mfma_kernel<DT, QT, BM, WNT, 1>), grid, dim3(256), lds, stream, a);
-            break;
-        case 2:
-            e = allow_lds<mfma_kernel<DT, QT, BM, WNT, 2>>(lds);
-            if (e == hipSuccess) hipLaunchKernelGGL((mfma_kernel<DT, QT, BM, WNT, 2>), grid, dim3(256), lds, stream, a);
-            break;
-        default:
-            e = allow_lds<mfma_kernel<DT, QT, BM, WNT, 4>>(lds);
-            if (e == hipSuccess) hipLaunchKernelGGL((mfma_kernel<DT, QT, BM, WNT, 4>), grid, dim3(256), lds, stream, a);
-            break;
-    }
-    return e != hipSuccess ? e : hipGetLastError();
-}
-
 template <int DT, int QT>
-hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, dim3 grid, hipStream_t stream) {
-    if (p.lds && ((a.M - 1) * a.lda + a.KTT * 128) * 2 < ((int64_t)1 << 31)) {
-        if (p.BN == 256) {
-            // Offset-corrected modes run on the three-stage ring.
-            return spt == 1 ? launch_ring_t<DT, QT>(a, stream) : launch_lds_t<DT, QT, 128, 2, 4, 1>(a, spt, stream);
-        }
-        switch (p.BM) {  // BN = 64: one n-tile per wave, 2 or 4 k-tiles per step
-            case 32: return launch_lds_t<DT, QT, 32, 2, 1, 4>(a, spt, stream);
-            case 64: return launch_lds_t<DT, QT, 64, 2, 1, 2>(a, spt, stream);
-            default: return launch_lds_t<DT, QT, 128, 2, 1, 2>(a, spt, stream);
-        }
+hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, hipStream_t stream) {
+    if (p.BN == 256) {
+        // Offset-corrected modes run on the three-stage ring.
+        return spt == 1 ? launch_ring_t<DT, QT>(a, stream) : launch_lds_t<DT, QT, 128, 2, 4, 1>(a, spt, stream);
     }
-    if (p.BM == 256) {
-        return p.BN == 256 ? launch_mfma_t<DT, QT, 256, 4>(a, spt, grid, stream)
-                           : launch_mfma_t<DT, QT, 256, 2>(a, spt, grid, stream);
+    switch (p.BM) {  // BN = 64: one n-tile per wave, 2 or 4 k-tiles per step
+        case 32: return launch_lds_t<DT, QT, 32, 2, 1, 4>(a, spt, stream);
+        case 64: return launch_lds_t<DT, QT, 64, 2, 1, 2>(a, spt, stream);
+        default: return launch_lds_t<DT, QT, 128, 2, 1, 2>(a, spt, stream);
     }
-    return p.BN == 256 ? launch_mfma_t<DT, QT, 128, 4>(a, spt, grid, stream)
-                       : launch_mfma_t<DT, QT, 128, 2>(a, spt, grid, stream);
 }
 
 }  // namespace
 
 MfmaPlan plan_mfma(int64_t M, const Geometry& g) {
     MfmaPlan p;
-    // The direct-to-LDS variant addresses A and the packed weight with
-    // 32-bit offsets; launch_mfma re-checks A, whose size depends on lda.
-    p.lds = g.codes_bytes < ((size_t)1 << 31);
-    if (p.lds) {
-        // 128 x 256 tiles while they give at least one workgroup per CU;
-        // otherwise 64-column tiles (four times the workgroups) with as few
-        // rows as M needs, so that the weight stream still spreads over the
-        // chip at small and medium M.
-        const int64_t wide = ((M + 127) / 128) * ((g.N + 255) / 256);
-        if (wide >= kCUs) {
-            p.BM = 128;
-            p.BN = 256;
-        } else {
-            p.BM = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
-            p.BN = 64;
-        }
-        return p;
+    // 128 x 256 tiles while they give at least one workgroup per CU;
+    // otherwise 64-column tiles (four times the workgroups) with as few rows
+    // as M needs, so that the weight stream still spreads over the chip at
+    // small and medium M.
+    const int64_t wide = ((M + 127) / 128) * ((g.N + 255) / 256);
+    if (wide >= kCUs) {
+        p.BM = 128;
+        p.BN = 256;
+    } else {
+        p.BM = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+        p.BN = 64;
     }
-    p.BM = M > 128 ? 256 : 128;
-    // Prefer the wider tile unless it leaves most of the 256 CUs idle.
-    const int64_t mt = (M + p.BM - 1) / p.BM;
-    const int64_t wide = mt * ((g.N + 255) / 256);
-    p.BN = wide >= 256 ? 256 : 128;
     return p;
 }
 
@@ -881,16 +738,12 @@ hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed
     a.bias = static_cast<const uint16_t*>(bias);
     a.C = static_cast<uint16_t*>(C);
     a.ldc = ldc;
-    a.a_bytes = (uint32_t)(((M - 1) * lda + g.K) * 2);
-    a.codes_bytes = (uint32_t)g.codes_bytes;
-    a.scales_bytes = (uint32_t)(g.N * g.Kg * 2);
-    a.zeros_bytes = g.qtype == 1 ? (uint32_t)(g.N * g.Kg) : 0u;
     a.m_tiles = (M + p.BM - 1) / p.BM;
     a.n_blocks = (g.N + p.BN - 1) / p.BN;
-    const dim3 grid((unsigned)(a.m_tiles * a.n_blocks));
+    a.tile0 = 0;
     const int spt = g.Kg == 1 ? 1 : (g.Ge >= 128 ? 1 : 128 / g.Ge);
-    if (dtype == 0) return g.qtype ? launch_mfma_q<0, 1>(a, p, spt, grid, stream) : launch_mfma_q<0, 0>(a, p, spt, grid, stream);
-    return g.qtype ? launch_mfma_q<1, 1>(a, p, spt, grid, stream) : launch_mfma_q<1, 0>(a, p, spt, grid, stream);
+    if (dtype == 0) return g.qtype ? launch_mfma_q<0, 1>(a, p, spt, stream) : launch_mfma_q<0, 0>(a, p, spt, stream);
+    return g.qtype ? launch_mfma_q<1, 1>(a, p, spt, stream) : launch_mfma_q<1, 0>(a, p, spt, stream);
 }
 
 }  // namespace w4a16

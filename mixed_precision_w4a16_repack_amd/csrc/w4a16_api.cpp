@@ -206,6 +206,12 @@ w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packe
 
     const int32_t which = resolve_path(M, path, skinny_max_m);
     if (which == W4A16_PATH_MFMA) {
+        // The tiled kernels address one workgroup's tile (at most 128 rows
+        // of A, 16 n-tiles = 128*K bytes of codes) with 32-bit byte offsets;
+        // lda >= K makes this bound cover both.
+        if ((128 * lda + K) * 2 >= (int64_t)1 << 31)
+            return fail(W4A16_ERR_UNSUPPORTED, "lda=%lld is too large for the tiled path: need (128*lda + K)*2 < 2^31",
+                        (long long)lda);
         const MfmaPlan p = plan_mfma(M, g);
         hipError_t e = launch_mfma(A, M, lda, packed, g, dtype, bias, C, ldc, p, stream);
         if (e != hipSuccess) return hip_fail("mfma kernel launch", e);

@@ -109,6 +109,8 @@ def _gemm(lib, **kw):
         (dict(packed=ctypes.c_void_p(4100)), INVALID, "256-byte aligned"),
         (dict(K=4000, lda=4000), UNSUPPORTED, "K=4000 must be divisible by 128"),
         (dict(bias=ctypes.c_void_p(4097)), INVALID, "2-byte aligned"),
+        # the tiled path addresses one workgroup's tile with 32-bit offsets
+        (dict(M=256, lda=1 << 23), UNSUPPORTED, "too large for the tiled path"),
         # a narrow weight (64 n-tiles) splits K on the skinny path and needs a workspace
         (dict(M=1, N=1024, ldc=1024), SIZE, "workspace of 0 bytes is smaller"),
         (dict(M=1, N=1024, ldc=1024, ws=ctypes.c_void_p(4096), wsb=16), SIZE, "workspace of 16 bytes is smaller"),

@@ -305,6 +305,7 @@ RING = [
     (1930, 8192, 896, -1, UINT4, "f16", False),     # 7 steps: tail of 1, ragged M
     (2048, 14336, 512, 256, UINT4, "bf16", True),   # 896 tiles: the last 128 as 64-row halves
     (1990, 14336, 256, -1, UINT4B8, "f16", False),  # halves over m-tiles 13-15, ragged M
+    (1930, 14336, 256, 128, UINT4, "f16", True),    # a half tile lies wholly past M
 ]
 
 
@@ -441,3 +442,45 @@ def test_dense_gemm_strides():
     w4.gemm_dense(A_big[:, :K], W_big[:, :K], bias=b, out=C_big[:, :N])
     assert oracle.rel_err(C_big[:, :N].cpu(), oracle_ref(case)) <= oracle.TOLERANCE["bf16"]
     assert torch.all(C_big[:, N:] == 7.0), "wrote outside [M, N]"
+
+
+# ------------------------------------------------------------------ operands beyond 2 GiB
+# The kernels address buffers with 32-bit offsets from per-launch or
+# per-workgroup bases. These cases put A, or the packed weight, past 2^31
+# bytes. Inputs are drawn on the GPU (seeded); the oracle checks sampled rows
+# and column blocks at both ends of the weight.
+
+
+def test_activations_beyond_2gib():
+    M, N, K, G = 65600, 256, 16384, 128  # A is 2.15 GB; 513 tiles, the last as halves
+    print(f"[case] A beyond 2 GiB M={M} N={N} K={K}", flush=True)
+    case = _case(29, 1, N, K, G, UINT4B8, "bf16")  # the weight (its 1-row A is unused)
+    packed = repack(case)
+    gen = torch.Generator(device=DEV).manual_seed(29)
+    A = torch.randn((M, K), device=DEV, generator=gen).to(torch.bfloat16)
+    assert A.numel() * 2 > 2**31
+    C = w4.gemm(A, packed, N, K, G, UINT4B8, path=MFMA)
+    torch.cuda.synchronize()
+    rows = torch.as_tensor(sample_rows(M), device=DEV)
+    ref, _ = oracle.gemm(A[rows].cpu(), case.weight_packed, case.weight_scale, None, UINT4B8, G)
+    assert oracle.rel_err(C[rows].cpu(), ref) <= oracle.TOLERANCE["bf16"]
+
+
+@pytest.mark.parametrize("M,path", [(256, MFMA), (16, SKINNY)])
+def test_weights_beyond_2gib(M, path):
+    N, K, G = 65552, 65536, 128  # 2.15 GB of codes; 4097 n-tiles
+    print(f"[case] weight beyond 2 GiB M={M} N={N} K={K} path={path}", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(30)
+    wq = torch.randint(-2**31, 2**31, (N, K // 8), dtype=torch.int32, device=DEV, generator=gen)
+    ws = torch.empty((N, K // G), dtype=torch.bfloat16, device=DEV).uniform_(0.005, 0.02, generator=gen)
+    packed = w4.repack(wq, ws, None, G, UINT4B8)
+    assert N * K // 2 > 2**31
+    A = torch.randn((M, K), device=DEV, generator=gen).to(torch.bfloat16)
+    C = w4.gemm(A, packed, N, K, G, UINT4B8, path=path, workspace=w4.Workspace(DEV))
+    torch.cuda.synchronize()
+    rows = torch.as_tensor(sample_rows(M))
+    A_rows = A.cpu()[rows]
+    for n0 in (0, N - 48):  # the last n-tiles sit past 2 GiB in the packed buffer
+        ref, _ = oracle.gemm(A_rows, wq[n0:n0 + 48].cpu().numpy(), ws[n0:n0 + 48].cpu(), None, UINT4B8, G)
+        err = oracle.rel_err(C[:, n0:n0 + 48].cpu()[rows], ref)
+        assert err <= oracle.TOLERANCE["bf16"], f"columns {n0}..: rel err {err:.3e}"
