@@ -126,16 +126,15 @@ __device__ __forceinline__ TileBufs tile_bufs(const MfmaArgs& a, int64_t m0, int
 // reuses it for its MI row blocks. One barrier per step. Small tiles use
 // KS = 2 or 4 so that each step carries enough loads to cover the memory
 // latency.
-// All loads go through buffer descriptors whose per-wave part of the offset
-// is scalar, which keeps the vector registers for the accumulators (A, the
-// codes and the scales each below 2^31 bytes).
-// OCM: 0 scale-first dequantisation (groups of 32 or 64 k); 1 offset-corrected
-// with one group per row (scales applied in the epilogue); 2 offset-
-// corrected with groups of 128 k or more (KS == 1), folded at each group end.
+// All loads go through buffer descriptors based at the workgroup's tile
+// whose per-wave part of the offset is scalar, which keeps the vector
+// registers for the accumulators.
+// OCM: 0 scale-first dequantisation; 1 offset-corrected with one group per
+// row (scales applied in the epilogue).
 template <int DT, int QT, int SPT, int BM, int WM, int NJ, int KS, int OCM>
 __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
+    static_assert(OCM == 0 || OCM == 1, "scale first, or one group per row");
     constexpr bool OC = OCM != 0;
-    static_assert(OCM != 2 || (KS == 1 && SPT == 1), "group folds at K-step ends");
     constexpr int WN = 8 / WM;
     constexpr int MI = BM / (16 * WM);
     constexpr int BN = WN * NJ * 16;
@@ -248,13 +247,6 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
     floatx4 S[OC ? MI : 1];
 #pragma unroll
     for (int i = 0; i < (OC ? MI : 1); ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // OCM 2: P sums A*(m + q) and S sums A within the current group; at the
-    // group's last K step acc += s * (P - (m + z) * S) and both restart.
-    floatx4 P[OCM == 2 ? MI : 1][OCM == 2 ? NJ : 1];
-#pragma unroll
-    for (int i = 0; i < (OCM == 2 ? MI : 1); ++i)
-#pragma unroll
-        for (int j = 0; j < (OCM == 2 ? NJ : 1); ++j) P[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
     const u32x4 ones = {one2, one2, one2, one2};
 
@@ -292,29 +284,9 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
                     const u32x4 av = *reinterpret_cast<const u32x4*>(abase + blk * 1024);
                     if (OC) S[i] = mfma16x16x32<DT>(av, ones, S[i]);
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        if (OCM == 2) P[OCM == 2 ? i : 0][OCM == 2 ? j : 0] = mfma16x16x32<DT>(av, bq[j], P[OCM == 2 ? i : 0][OCM == 2 ? j : 0]);
-                        else acc[i][j] = mfma16x16x32<DT>(av, bq[j], acc[i][j]);
-                    }
+                    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32<DT>(av, bq[j], acc[i][j]);
                 }
             }
-        }
-        if (OCM == 2 && (((st + 1) << 7) & ((1 << a.gshift) - 1)) == 0) {
-            // Last K step of a group (G = 2^gshift >= 128): fold and restart.
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const float sf = act_to_float<DT>((uint16_t)sb[j][0][0]);
-                const float zf = -((DT == 0 ? 1024.0f : 128.0f) + (QT ? (float)zb[j][0][0] : 8.0f));
-#pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    floatx4& p = P[OCM == 2 ? i : 0][OCM == 2 ? j : 0];
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(sf, __builtin_fmaf(zf, S[OC ? i : 0][jj], p[jj]), acc[i][j][jj]);
-                    p = floatx4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < (OC ? MI : 1); ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
         // The next activation tile has landed once only the weight loads
         // issued after it may be outstanding; then every wave is done with
@@ -676,11 +648,8 @@ hipError_t launch_lds_t(const MfmaArgs& a, int spt, hipStream_t stream) {
         hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, 1>), grid, dim3(512), 0, stream, a);
         return hipGetLastError();
     }
-    // Per-group offset correction needs KS == 1 and about 250 registers; the
-    // fp16 uint4 instance of it would spill, so that one stays scale first.
-    constexpr int OCG = (KS == 1 && !(DT == 0 && QT == 1)) ? 2 : 0;
     switch (spt) {  // spt == 1: groups of 128 k or more
-        case 1: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, OCG>), grid, dim3(512), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, 0>), grid, dim3(512), 0, stream, a); break;
         case 2: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 2, BM, WM, NJ, KS, 0>), grid, dim3(512), 0, stream, a); break;
         default: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 4, BM, WM, NJ, KS, 0>), grid, dim3(512), 0, stream, a); break;
     }
@@ -688,11 +657,21 @@ hipError_t launch_lds_t(const MfmaArgs& a, int spt, hipStream_t stream) {
 }
 
 
+// 128 x 256 staged tiles for groups of 32 or 64 k (scale first); every
+// other G at this tile size runs on the ring.
+template <int DT, int QT>
+hipError_t launch_lds_wide(const MfmaArgs& a, int spt, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)((a.M + 127) / 128));
+    if (spt == 2) hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 2, 128, 2, 4, 1, 0>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 4, 128, 2, 4, 1, 0>), grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int DT, int QT>
 hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, hipStream_t stream) {
     if (p.BN == 256) {
         // Offset-corrected modes run on the three-stage ring.
-        return spt == 1 ? launch_ring_t<DT, QT>(a, stream) : launch_lds_t<DT, QT, 128, 2, 4, 1>(a, spt, stream);
+        return spt == 1 ? launch_ring_t<DT, QT>(a, stream) : launch_lds_wide<DT, QT>(a, spt, stream);
     }
     switch (p.BM) {  // BN = 64: one n-tile per wave, 2 or 4 k-tiles per step
         case 32: return launch_lds_t<DT, QT, 32, 2, 1, 4>(a, spt, stream);

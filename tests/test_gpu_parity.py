@@ -293,9 +293,10 @@ def test_skinny_k_extremes(K):
     assert oracle.rel_err(C.cpu(), oracle_ref(case)) <= oracle.TOLERANCE["bf16"]
 
 
-# 128 x 256 tiles on the three-stage ring (at least 256 workgroups, one group
-# per row or groups of 128 k or more; a last round at most half full runs as
-# 64-row halves). Each case names the edge it reaches.
+# 128 x 256 tiles (at least 256 workgroups): the three-stage ring for one
+# group per row or groups of 128 k or more (a last round at most half full
+# runs as 64-row halves), the staged kernel with scale-first dequantisation
+# for groups of 32 or 64 k. Each case names the edge it reaches.
 RING = [
     # (M, N, K, G, qtype, dtype, bias)
     (2048, 4096, 128, -1, UINT4B8, "bf16", False),  # one K step: only the loop tail runs
@@ -306,6 +307,8 @@ RING = [
     (2048, 14336, 512, 256, UINT4, "bf16", True),   # 896 tiles: the last 128 as 64-row halves
     (1990, 14336, 256, -1, UINT4B8, "f16", False),  # halves over m-tiles 13-15, ragged M
     (1930, 14336, 256, 128, UINT4, "f16", True),    # a half tile lies wholly past M
+    (2048, 4096, 1024, 64, UINT4, "bf16", True),    # G = 64: staged tiles, scale first
+    (1000, 8192, 512, 32, UINT4B8, "f16", False),   # G = 32: staged tiles, scale first, ragged M
 ]
 
 
