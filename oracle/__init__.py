@@ -6,7 +6,9 @@ never import it, and it imports nothing from them.
 
 The arithmetic lives in ``w4a16_oracle.c`` (plain C, fp64, OpenMP over output
 rows); this file compiles it with gcc and marshals numpy/torch arrays. See the
-C file's header for the passages each function follows.
+C file's header for the passages each function follows. The readers of the
+other checkpoint orientations (``unpack_int4``, ``weight_codes_nk``,
+``scales_nk``, ``zeros_nk``) are index work only and are plain numpy here.
 
 Parity: every function here is pinned by ``tests/test_oracle.py`` against hand
 words derived from the stated bit positions, the little-endian byte view,
@@ -154,6 +156,68 @@ def pack_zeros(zeros) -> np.ndarray:
     out = np.empty((N // 8, Kg), dtype=np.uint32)
     _load().w4o_pack_zeros(_ptr(z), N, Kg, _ptr(out))
     return out.view(np.int32)
+
+
+def unpack_int4(words, dim: int) -> np.ndarray:
+    """Eight 4-bit values per int32 word along tensor dimension ``dim``.
+
+    The step the MI300 Triton W4A16 page's ``process_weights_after_loading``
+    takes first on any checkpoint (``unpack_quantized_values_into_int32`` with
+    ``packed_dim``): dimension ``dim`` grows eightfold, word ``j`` of it giving
+    entries ``8j .. 8j+7``, entry ``8j + i`` from bits ``[4i, 4i+4)`` (the nibble
+    order the compressed-tensors layout states for its words). Plain numpy, no
+    C; shared by no product code.
+    """
+    w = _words(words)
+    if w.ndim != 2 or dim not in (0, 1):
+        raise ValueError("words must be 2-D and dim 0 or 1")
+    w = np.moveaxis(w, dim, -1)
+    shifts = np.arange(8, dtype=np.uint32) * 4
+    v = (w[..., None] >> shifts) & np.uint32(0xF)
+    v = v.reshape(w.shape[0], w.shape[1] * 8)
+    return np.ascontiguousarray(np.moveaxis(v, -1, dim).astype(np.uint8))
+
+
+def weight_codes_nk(weight, output_dim: int, packed_dim: int) -> np.ndarray:
+    """A packed weight in any orientation the pages name -> codes [N, K].
+
+    The MI300 Triton W4A16 page (``process_weights_after_loading``) unpacks
+    the weight along its ``packed_dim`` and then transposes it when its
+    ``output_dim`` (the dimension over the N output features) is not 0: AWQ
+    weights arrive as (K, N) with ``output_dim=1``, compressed-tensors ones as
+    (N, K) with ``output_dim=0``.
+    """
+    if output_dim not in (0, 1) or packed_dim not in (0, 1):
+        raise ValueError("output_dim and packed_dim must be 0 or 1")
+    codes = unpack_int4(weight, packed_dim)
+    return np.ascontiguousarray(codes.T) if output_dim != 0 else codes
+
+
+def scales_nk(scale, output_dim: int) -> torch.Tensor:
+    """Scales [N, Kg] (output_dim 0) or [Kg, N] (output_dim 1) -> [N, Kg],
+    the page's ``permute_param_layout_(w_s, input_dim=1, output_dim=0)``."""
+    if output_dim not in (0, 1):
+        raise ValueError("output_dim must be 0 or 1")
+    if not isinstance(scale, torch.Tensor):
+        raise TypeError("scale must be a torch tensor")
+    s = scale.detach().cpu()
+    return (s.t() if output_dim != 0 else s).contiguous()
+
+
+def zeros_nk(zero_point, output_dim: int) -> np.ndarray:
+    """Zero points, eight per int32 word along N, -> zeros [N, Kg].
+
+    The MI300 kernel section of the same page: with ``output_dim=1`` the
+    tensor is already [K/G, N/8] (AutoGPTQ), with ``output_dim=0`` it is
+    [N/8, K/G] (compressed-tensors); either way the words are permuted to
+    [N/8, K/G] and unpacked along that first dimension.
+    """
+    if output_dim not in (0, 1):
+        raise ValueError("output_dim must be 0 or 1")
+    zw = _words(zero_point)
+    if output_dim != 0:
+        zw = np.ascontiguousarray(zw.T)
+    return unpack_int4(zw, 0)
 
 
 def dequant(words, scales, zp_words, qtype: int, G: int) -> np.ndarray:

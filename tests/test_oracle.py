@@ -129,6 +129,100 @@ def test_zero_point_byte_view(oracle_mod):
     np.testing.assert_array_equal(oracle_mod.pack_zeros(expect).view(np.uint32), words)
 
 
+# ------------------------------------------------- checkpoint orientations
+
+
+def _load_layout_blocks():
+    blocks, cur = [], None
+    with open(os.path.join(GOLDEN, "layout_words.txt")) as f:
+        for ln in f:
+            ln = ln.split("#")[0].split()
+            if not ln:
+                continue
+            if ln[0] in ("weight", "zero"):
+                od, pd, r, c = (int(x) for x in ln[1:5])
+                cur = dict(kind=ln[0], od=od, pd=pd, words=np.zeros((r, c), dtype=np.uint32), expect=[])
+            elif ln[0] == "word":
+                cur["words"][int(ln[1]), int(ln[2])] = int(ln[3], 16)
+            elif ln[0] == "expect":
+                cur["expect"].append(tuple(int(x) for x in ln[1:4]))
+            elif ln[0] == "end":
+                blocks.append(cur)
+    return blocks
+
+
+def _nk_shape(b):
+    r, c = b["words"].shape
+    n_dim = b["od"]  # the tensor dimension over N
+    dims = [r, c]
+    dims[b["pd"]] *= 8
+    return (dims[n_dim], dims[1 - n_dim])
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_layout_hand_words(oracle_mod, idx):
+    b = _load_layout_blocks()[idx]
+    if b["kind"] == "weight":
+        got = oracle_mod.weight_codes_nk(b["words"], b["od"], b["pd"])
+    else:
+        assert b["pd"] == b["od"]  # zero points are packed along N
+        got = oracle_mod.zeros_nk(b["words"], b["od"])
+    expect = np.zeros(_nk_shape(b), dtype=np.uint8)
+    for n, k, v in b["expect"]:
+        expect[n, k] = v
+    assert got.shape == expect.shape
+    np.testing.assert_array_equal(got, expect)
+
+
+def test_layout_blocks_cover_every_orientation():
+    seen = {(b["kind"], b["od"], b["pd"]) for b in _load_layout_blocks()}
+    assert seen == {("weight", 0, 0), ("weight", 0, 1), ("weight", 1, 0), ("weight", 1, 1),
+                    ("zero", 0, 0), ("zero", 1, 1)}
+
+
+def test_layout_canonical_matches_c_unpack(oracle_mod):
+    # Two independent readers of the compressed-tensors words (numpy here, C
+    # for the GEMM oracle) agree, and the transposed (K/8, N) tensor with
+    # output_dim=1, packed_dim=0 holds the same codes.
+    rng = np.random.default_rng(21)
+    words = rng.integers(0, 2**32, size=(24, 40), dtype=np.uint64).astype(np.uint32)
+    ref = oracle_mod.unpack_codes(words)
+    np.testing.assert_array_equal(oracle_mod.weight_codes_nk(words, 0, 1), ref)
+    np.testing.assert_array_equal(oracle_mod.weight_codes_nk(np.ascontiguousarray(words.T), 1, 0), ref)
+    # (N/8, K) and its transpose (K, N/8) with the packed dimension along N.
+    wn = rng.integers(0, 2**32, size=(5, 72), dtype=np.uint64).astype(np.uint32)
+    a = oracle_mod.weight_codes_nk(wn, 0, 0)
+    np.testing.assert_array_equal(oracle_mod.weight_codes_nk(np.ascontiguousarray(wn.T), 1, 1), a)
+    # Packed along N, column k of the codes is the C zero-point reader applied
+    # to column k of the words (the same "eight rows per word" rule).
+    np.testing.assert_array_equal(a, oracle_mod.unpack_zeros(wn, 40))
+
+
+def test_layout_zero_points_match_c_unpack(oracle_mod):
+    rng = np.random.default_rng(22)
+    zw = rng.integers(0, 2**32, size=(6, 9), dtype=np.uint64).astype(np.uint32)
+    ref = oracle_mod.unpack_zeros(zw, 48)
+    np.testing.assert_array_equal(oracle_mod.zeros_nk(zw, 0), ref)
+    np.testing.assert_array_equal(oracle_mod.zeros_nk(np.ascontiguousarray(zw.T), 1), ref)
+
+
+def test_layout_scales_orientation(oracle_mod):
+    t = torch.tensor([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]], dtype=torch.bfloat16)  # [Kg=2, N=3]
+    got = oracle_mod.scales_nk(t, 1)
+    assert got.dtype == torch.bfloat16 and got.is_contiguous()
+    assert got.tolist() == [[1.0, 4.0], [2.0, 5.0], [3.0, 6.0]]
+    assert torch.equal(oracle_mod.scales_nk(t, 0), t)
+
+
+def test_layout_rejects_bad_dims(oracle_mod):
+    w = np.zeros((2, 2), dtype=np.uint32)
+    for od, pd in ((2, 0), (0, 2), (-1, 1)):
+        with pytest.raises(ValueError):
+            oracle_mod.weight_codes_nk(w, od, pd)
+    with pytest.raises(ValueError):
+        oracle_mod.zeros_nk(w, 2)
+
+
 # ---------------------------------------------------------------- dequant
 
 

@@ -3,20 +3,26 @@
 Each mutant is a one-line textual change to a copy of ``oracle/w4a16_oracle.c``
 (a dropped term, a wrong sign, index or shift, a transposed operand), built
 with gcc into a temporary library. The pins of ``tests/test_oracle.py`` run
-against it; at least one must fail. The real oracle is never modified.
+against it; at least one must fail. The numpy readers of the other checkpoint
+orientations get the same treatment from a mutated copy of
+``oracle/__init__.py`` loaded as a separate module. The real oracle is never
+modified.
 """
 
 from __future__ import annotations
 
 import os
 import subprocess
+import types
 
 import pytest
 import torch
 
 import tests.test_oracle as pins
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "w4a16_oracle.c")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "w4a16_oracle.c")
+PY_SRC = os.path.join(ORACLE_DIR, "__init__.py")
 
 # (name, original text, planted text). Each original must occur exactly once.
 MUTANTS = [
@@ -99,3 +105,50 @@ def test_planted_mistake_is_caught(oracle_mod, tmp_path, name, orig, planted):
 
 def test_unmutated_oracle_passes_the_same_pins(oracle_mod):
     assert _run_pins(oracle_mod) == []
+
+
+# Mutants of the numpy orientation readers in oracle/__init__.py.
+PY_MUTANTS = [
+    ("int4_reversed_nibbles", "shifts = np.arange(8, dtype=np.uint32) * 4", "shifts = (7 - np.arange(8, dtype=np.uint32)) * 4"),
+    ("int4_interleave", "v = v.reshape(w.shape[0], w.shape[1] * 8)",
+     "v = np.swapaxes(v, -1, -2).reshape(w.shape[0], w.shape[1] * 8)"),
+    ("weight_no_transpose", "return np.ascontiguousarray(codes.T) if output_dim != 0 else codes", "return codes"),
+    ("weight_packed_dim_ignored", "codes = unpack_int4(weight, packed_dim)", "codes = unpack_int4(weight, 1 - output_dim)"),
+    ("zeros_no_transpose", "        zw = np.ascontiguousarray(zw.T)\n    return unpack_int4(zw, 0)",
+     "        pass\n    return unpack_int4(zw, 0)"),
+    ("zeros_wrong_dim", "return unpack_int4(zw, 0)", "return np.ascontiguousarray(unpack_int4(zw, 1).T)"),
+    ("scales_no_transpose", "return (s.t() if output_dim != 0 else s).contiguous()", "return s.contiguous()"),
+]
+
+PY_PIN_CALLS = [(pins.test_layout_hand_words, {"idx": i}) for i in range(6)] + [
+    (pins.test_layout_canonical_matches_c_unpack, {}),
+    (pins.test_layout_zero_points_match_c_unpack, {}),
+    (pins.test_layout_scales_orientation, {}),
+]
+
+
+def _mutated_module(src: str):
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = PY_SRC  # so it finds (and shares) the built C library
+    exec(compile(src, PY_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,orig,planted", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_planted_reader_mistake_is_caught(oracle_mod, name, orig, planted):
+    src = open(PY_SRC).read()
+    assert src.count(orig) == 1, f"mutant {name}: anchor text not found exactly once"
+    mod = _mutated_module(src.replace(orig, planted))
+    failed = []
+    for fn, kw in PY_PIN_CALLS:
+        try:
+            fn(mod, **kw)
+        except (AssertionError, ValueError):
+            failed.append(fn.__name__)
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_unmutated_readers_pass_the_same_pins(oracle_mod):
+    mod = _mutated_module(open(PY_SRC).read())
+    for fn, kw in PY_PIN_CALLS:
+        fn(mod, **kw)
