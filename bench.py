@@ -313,7 +313,32 @@ def extras(warmup):
     us = g.time_repack()
     out["repack"] = {"N": 14336, "K": 4096, "us": round(us, 1),
                      "GBps_read_plus_write": round(2 * g.weight_bytes / us / 1e3, 1)}
+    out["repack_layout"] = time_repack_layouts(14336, 4096, 128)
     return out
+
+
+def time_repack_layouts(N, K, G, reps=5):
+    """One-time repack from the AWQ (K, N/8) and AutoGPTQ (K/8, N) weight
+    orientations, (K/G, N) scales and (K/G, N/8) zero points, uint4."""
+    rows = []
+    for name, od, pd in (("awq", 1, 1), ("autogptq", 1, 0)):
+        L = wi.make_layout_weights(6, N, K, G, wi.UINT4, "bf16", od, pd, 1, 1)
+        w = torch.from_numpy(L.weight).to(DEV)
+        s_ = L.weight_scale.to(DEV)
+        z = torch.from_numpy(L.weight_zero_point).to(DEV)
+        out = w4.repack_layout(w, od, pd, s_, 1, z, 1, G, wi.UINT4)
+        torch.cuda.synchronize()
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        for _ in range(reps):
+            w4.repack_layout(w, od, pd, s_, 1, z, 1, G, wi.UINT4, out=out)
+        e.record()
+        torch.cuda.synchronize()
+        us = b.elapsed_time(e) / reps * 1e3
+        moved = 2 * (w.numel() * 4 + s_.numel() * 2 + z.numel() * 4)
+        rows.append({"orientation": name, "N": N, "K": K, "G": G, "us": round(us, 1),
+                     "GBps_read_plus_write": round(moved / us / 1e3, 1)})
+    return rows
 
 
 def main():

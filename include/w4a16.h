@@ -114,6 +114,33 @@ w4a16_status w4a16_repack(const int32_t *weight_packed, const void *weight_scale
                           int64_t N, int64_t K, int32_t group_size, int32_t qtype, void *packed, size_t packed_bytes,
                           hipStream_t stream);
 
+/* w4a16_repack for checkpoints in the other orientations the MI300 Triton
+ * W4A16 page accepts ("triton_w4a16.py": process_weights_after_loading, and
+ * the zero-point handling of its MI300 kernel section). Each packed tensor is
+ * described as the page describes a parameter: output_dim is its dimension
+ * that runs over the N output features, packed_dim the dimension whose eight
+ * consecutive entries share one int32 word (entry 8j + i of that dimension in
+ * bits [4i, 4i+4) of word j). All tensors row-major and contiguous:
+ *   weight             output_dim 0, packed_dim 1: [N, K/8]  (compressed-tensors)
+ *                      output_dim 0, packed_dim 0: [N/8, K]
+ *                      output_dim 1, packed_dim 1: [K, N/8]  (AWQ)
+ *                      output_dim 1, packed_dim 0: [K/8, N]  (AutoGPTQ)
+ *   weight_scale       scale_output_dim 0: [N, Kg]; 1: [Kg, N] (raw 16-bit values)
+ *   weight_zero_point  eight zeros per word along N; zero_output_dim 0:
+ *                      [N/8, Kg]; 1: [Kg, N/8] (AutoGPTQ); NULL and qtype
+ *                      rules as for w4a16_repack
+ * The packed buffer is byte-identical to what w4a16_repack writes for the
+ * same codes, scales and zeros; with dims (0, 1, 0, 0) this is w4a16_repack.
+ * Nibble orders other than the sequential one above (for instance an
+ * interleaved order some AWQ exporters use) must be undone by the caller.
+ * W4A16_ERR_INVALID_ARG if a dim is not 0 or 1; otherwise fails like
+ * w4a16_repack. */
+w4a16_status w4a16_repack_layout(const int32_t *weight, int32_t weight_output_dim, int32_t weight_packed_dim,
+                                 const void *weight_scale, int32_t scale_output_dim,
+                                 const int32_t *weight_zero_point, int32_t zero_output_dim, int64_t N, int64_t K,
+                                 int32_t group_size, int32_t qtype, void *packed, size_t packed_bytes,
+                                 hipStream_t stream);
+
 /* Test support: the inverse of w4a16_repack. Reads the packed buffer and
  * writes codes [N, K] (one code per byte, row-major), scale_bits [N, Kg]
  * (raw 16-bit values) and, for uint4, zeros [N, Kg] bytes. Any output may be

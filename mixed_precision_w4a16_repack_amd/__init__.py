@@ -40,6 +40,7 @@ SIGNATURES = {
     "w4a16_last_error": (ctypes.c_char_p, []),
     "w4a16_packed_size": (ctypes.c_int, [_I64, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "w4a16_repack": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _SZ, _P]),
+    "w4a16_repack_layout": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _P, _I32, _I64, _I64, _I32, _I32, _P, _SZ, _P]),
     "w4a16_unpack": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _P, _P, _P, _P]),
     "w4a16_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "w4a16_workspace_counter_bytes": (_SZ, []),
@@ -132,6 +133,48 @@ def repack(weight_packed: torch.Tensor, weight_scale: torch.Tensor, weight_zero_
     _check(load_library().w4a16_repack(
         _ptr(weight_packed), _ptr(weight_scale), _ptr(weight_zero_point), N, K, group_size, qtype,
         _ptr(out), out.numel() * out.element_size(), _stream(weight_packed)))
+    return out
+
+
+def repack_layout(weight: torch.Tensor, weight_output_dim: int, weight_packed_dim: int, weight_scale: torch.Tensor,
+                  scale_output_dim: int, weight_zero_point: torch.Tensor | None, zero_output_dim: int,
+                  group_size: int, qtype: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Checkpoint tensors in any orientation w4a16_repack_layout accepts -> packed buffer.
+
+    N and K follow from the weight's shape and dims (the packed dimension holds
+    a word per eight entries); the scale and zero-point shapes are checked
+    against them before the call.
+    """
+    _need_cuda("weight", weight, torch.int32)
+    _need_cuda("weight_scale", weight_scale, (torch.float16, torch.bfloat16))
+    _need_cuda("weight_zero_point", weight_zero_point, torch.int32)
+    for name, d in (("weight_output_dim", weight_output_dim), ("weight_packed_dim", weight_packed_dim),
+                    ("scale_output_dim", scale_output_dim), ("zero_output_dim", zero_output_dim)):
+        if d not in (0, 1):
+            raise ValueError(f"{name} must be 0 or 1")
+    if weight.dim() != 2:
+        raise ValueError("weight must be 2-D")
+    dims = list(weight.shape)
+    dims[weight_packed_dim] *= 8
+    N, K = dims[weight_output_dim], dims[1 - weight_output_dim]
+    Kg = 1 if group_size == -1 else (K // group_size if group_size > 0 else 0)
+    want_s = (N, Kg) if scale_output_dim == 0 else (Kg, N)
+    if tuple(weight_scale.shape) != want_s:
+        raise ValueError(f"weight_scale must be {list(want_s)}, got {list(weight_scale.shape)}")
+    if weight_zero_point is not None:
+        want_z = (N // 8, Kg) if zero_output_dim == 0 else (Kg, N // 8)
+        if tuple(weight_zero_point.shape) != want_z:
+            raise ValueError(f"weight_zero_point must be {list(want_z)}, got {list(weight_zero_point.shape)}")
+    for name, t in (("weight", weight), ("weight_scale", weight_scale), ("weight_zero_point", weight_zero_point)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    nbytes = packed_size(N, K, group_size, qtype)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=weight.device)
+    _check(load_library().w4a16_repack_layout(
+        _ptr(weight), weight_output_dim, weight_packed_dim, _ptr(weight_scale), scale_output_dim,
+        _ptr(weight_zero_point), zero_output_dim, N, K, group_size, qtype,
+        _ptr(out), out.numel() * out.element_size(), _stream(weight)))
     return out
 
 

@@ -77,8 +77,16 @@ MfmaPlan plan_mfma(int64_t M, const Geometry& g);
 
 // Launchers; each returns hipSuccess or the launch error. Shapes are already
 // validated by the caller.
-hipError_t launch_repack(const int32_t* wq, const uint16_t* ws, const int32_t* wzp, const Geometry& g, void* packed,
-                         hipStream_t stream);
+// Orientation of the checkpoint tensors read by launch_repack.
+struct CheckpointLayout {
+    bool weight_n_first = true;   // weight words [Nw][Kw] (else [Kw][Nw])
+    bool weight_k_packed = true;  // eight consecutive k per word (else eight n)
+    bool scale_n_first = true;    // scales [N][Kg] (else [Kg][N])
+    bool zero_n_first = true;     // zero-point words [N/8][Kg] (else [Kg][N/8])
+};
+
+hipError_t launch_repack(const int32_t* wq, const uint16_t* ws, const int32_t* wzp, const CheckpointLayout& lay,
+                         const Geometry& g, void* packed, hipStream_t stream);
 hipError_t launch_unpack(const void* packed, const Geometry& g, uint8_t* codes, uint16_t* scale_bits, uint8_t* zeros,
                          hipStream_t stream);
 hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* packed, const Geometry& g, int dtype,

@@ -7,6 +7,13 @@
 // weight_zero_point [N/8, K/G] int32 with row n at bits 4*(n%8) of word n/8.
 // The pages repack on the host at load time (`process_weights_after_loading`,
 // `repack_w_q`); here it is one pass of three small GPU kernels, bit-exact.
+//
+// The same kernels read the other orientations the page's
+// `process_weights_after_loading` and zero-point handling accept: a packed
+// tensor is described by the dimension over N (output_dim) and the dimension
+// whose eight consecutive entries share a word (packed_dim), value i of a
+// word at bits 4i. AWQ weights arrive as (K, N/8) (packed along N), AutoGPTQ
+// ones as (K/8, N), scales as (K/G, N), AutoGPTQ zero points as (K/G, N/8).
 #include "internal.h"
 
 namespace w4a16 {
@@ -35,11 +42,22 @@ __device__ __forceinline__ uint32_t pair_to_gptq_order(uint32_t w) {
     return out;
 }
 
-// One thread per (tile, lane): gathers the four checkpoint words that feed
-// lane l of tile (nt, kt) and writes them as one 16-byte store.
+// Index of checkpoint word (nw, kw) in a tensor of Nw x Kw words stored with
+// N first ([Nw][Kw]) or K first ([Kw][Nw]).
+template <bool NFIRST>
+__device__ __forceinline__ int64_t word_index(int64_t nw, int64_t kw, int64_t Nw, int64_t Kw) {
+    return NFIRST ? nw * Kw + kw : kw * Nw + nw;
+}
+
+// One thread per (tile, lane): builds the four words that lane l of tile
+// (nt, kt) holds (codes of row n at k0 .. k0+7, k0 = 128kt + 32s + 8(l/16))
+// and writes them as one 16-byte store. Packed along K, each is one
+// checkpoint word with its nibbles reordered; packed along N, its eight codes
+// come from nibble n%8 of eight words, one per k.
+template <bool NFIRST, bool KPACKED>
 __global__ __launch_bounds__(256) void repack_codes_kernel(const uint32_t* __restrict__ wq, uint4* __restrict__ out,
                                                            int64_t N, int64_t K) {
-    const int64_t KT = K / 128, K8 = K / 8;
+    const int64_t KT = K / 128;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = (N / 16) * KT * 64;
     if (t >= total) return;
@@ -47,16 +65,29 @@ __global__ __launch_bounds__(256) void repack_codes_kernel(const uint32_t* __res
     const int l = (int)(t & 63);
     const int64_t nt = tile / KT, kt = tile - nt * KT;
     const int64_t n = 16 * nt + (l & 15);
-    const uint32_t* row = wq + n * K8 + 16 * kt + (l >> 4);  // word of k = 128kt + 8(l/16)
-    uint4 v;
-    v.x = gptq_to_pair_order(row[0]);   // s = 0: k + 0
-    v.y = gptq_to_pair_order(row[4]);   // s = 1: k + 32
-    v.z = gptq_to_pair_order(row[8]);   // s = 2: k + 64
-    v.w = gptq_to_pair_order(row[12]);  // s = 3: k + 96
-    out[t] = v;
+    const int64_t k = 128 * kt + 8 * (l >> 4);
+    uint32_t w[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int64_t k0 = k + 32 * s;
+        if constexpr (KPACKED) {
+            w[s] = gptq_to_pair_order(wq[word_index<NFIRST>(n, k0 / 8, N, K / 8)]);
+        } else {
+            const int shift = 4 * (int)(n & 7);
+            uint32_t v = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t q = (wq[word_index<NFIRST>(n >> 3, k0 + i, N / 8, K)] >> shift) & 0xFu;
+                v |= q << (4 * (i >> 1) + 16 * (i & 1));
+            }
+            w[s] = v;
+        }
+    }
+    out[t] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // One thread per (row, group): scales to [N/16][Kg][16], zeros likewise.
+template <bool SNFIRST, bool ZNFIRST>
 __global__ __launch_bounds__(256) void repack_scales_kernel(const uint16_t* __restrict__ ws,
                                                             const uint32_t* __restrict__ wzp,
                                                             uint16_t* __restrict__ s_out, uint8_t* __restrict__ z_out,
@@ -68,10 +99,11 @@ __global__ __launch_bounds__(256) void repack_scales_kernel(const uint16_t* __re
     const int64_t ng = t >> 4;  // nt * Kg + g
     const int64_t nt = ng / Kg, g = ng - nt * Kg;
     const int64_t n = 16 * nt + r;
-    s_out[t] = ws[n * Kg + g];
+    s_out[t] = ws[SNFIRST ? n * Kg + g : g * N + n];
     if (z_out != nullptr) {
         uint8_t z = 0;
-        if (wzp != nullptr) z = (uint8_t)((wzp[(n >> 3) * Kg + g] >> (4 * (n & 7))) & 0xFu);
+        if (wzp != nullptr)
+            z = (uint8_t)((wzp[word_index<ZNFIRST>(n >> 3, g, N / 8, Kg)] >> (4 * (n & 7))) & 0xFu);
         z_out[t] = z;
     }
 }
@@ -122,18 +154,35 @@ inline unsigned blocks_for(int64_t threads, int per_block) { return (unsigned)((
 
 }  // namespace
 
-hipError_t launch_repack(const int32_t* wq, const uint16_t* ws, const int32_t* wzp, const Geometry& g, void* packed,
-                         hipStream_t stream) {
+hipError_t launch_repack(const int32_t* wq, const uint16_t* ws, const int32_t* wzp, const CheckpointLayout& lay,
+                         const Geometry& g, void* packed, hipStream_t stream) {
     uint8_t* base = static_cast<uint8_t*>(packed);
     const int64_t code_threads = (g.N / 16) * (g.K / 128) * 64;
-    hipLaunchKernelGGL(repack_codes_kernel, dim3(blocks_for(code_threads, 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const uint32_t*>(wq), reinterpret_cast<uint4*>(base), g.N, g.K);
+    const dim3 cgrid(blocks_for(code_threads, 256));
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(wq);
+    uint4* dst = reinterpret_cast<uint4*>(base);
+    if (lay.weight_n_first && lay.weight_k_packed)
+        hipLaunchKernelGGL((repack_codes_kernel<true, true>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.K);
+    else if (lay.weight_n_first)
+        hipLaunchKernelGGL((repack_codes_kernel<true, false>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.K);
+    else if (lay.weight_k_packed)
+        hipLaunchKernelGGL((repack_codes_kernel<false, true>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.K);
+    else
+        hipLaunchKernelGGL((repack_codes_kernel<false, false>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint8_t* z_out = g.qtype == 1 ? base + g.zeros_off : nullptr;
     const uint32_t* zp = g.qtype == 1 ? reinterpret_cast<const uint32_t*>(wzp) : nullptr;
-    hipLaunchKernelGGL(repack_scales_kernel, dim3(blocks_for(g.N * g.Kg, 256)), dim3(256), 0, stream, ws, zp,
-                       reinterpret_cast<uint16_t*>(base + g.scales_off), z_out, g.N, g.Kg);
+    uint16_t* s_out = reinterpret_cast<uint16_t*>(base + g.scales_off);
+    const dim3 sgrid(blocks_for(g.N * g.Kg, 256));
+    if (lay.scale_n_first && lay.zero_n_first)
+        hipLaunchKernelGGL((repack_scales_kernel<true, true>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Kg);
+    else if (lay.scale_n_first)
+        hipLaunchKernelGGL((repack_scales_kernel<true, false>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Kg);
+    else if (lay.zero_n_first)
+        hipLaunchKernelGGL((repack_scales_kernel<false, true>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Kg);
+    else
+        hipLaunchKernelGGL((repack_scales_kernel<false, false>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Kg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Padding bytes between and after the regions are part of the contract

@@ -91,6 +91,28 @@ size_t skinny_workspace(const SkinnyPlan& p) {
     return p.ksplit > 1 ? kCounterRegionBytes + p.partial_bytes : 0;
 }
 
+w4a16_status repack_impl(const int32_t* weight, const void* weight_scale, const int32_t* weight_zero_point,
+                         const CheckpointLayout& lay, int64_t N, int64_t K, int32_t group_size, int32_t qtype,
+                         void* packed, size_t packed_bytes, hipStream_t stream) {
+    Geometry g;
+    w4a16_status st = make_geometry(N, K, group_size, qtype, &g);
+    if (st != W4A16_OK) return st;
+    if (weight == nullptr) return fail(W4A16_ERR_INVALID_ARG, "weight_packed is NULL");
+    if (weight_scale == nullptr) return fail(W4A16_ERR_INVALID_ARG, "weight_scale is NULL");
+    if (packed == nullptr) return fail(W4A16_ERR_INVALID_ARG, "packed is NULL");
+    if ((reinterpret_cast<uintptr_t>(weight) & 3u) || (reinterpret_cast<uintptr_t>(weight_scale) & 1u) ||
+        (reinterpret_cast<uintptr_t>(weight_zero_point) & 3u))
+        return fail(W4A16_ERR_INVALID_ARG, "checkpoint tensors must be aligned to their element size");
+    if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
+    if (packed_bytes < g.total_bytes)
+        return fail(W4A16_ERR_SIZE, "packed_bytes=%zu is smaller than the %zu bytes the layout needs", packed_bytes,
+                    g.total_bytes);
+    hipError_t e = launch_repack(weight, static_cast<const uint16_t*>(weight_scale),
+                                 qtype == W4A16_UINT4 ? weight_zero_point : nullptr, lay, g, packed, stream);
+    if (e != hipSuccess) return hip_fail("repack launch", e);
+    return W4A16_OK;
+}
+
 }  // namespace
 }  // namespace w4a16
 
@@ -114,27 +136,31 @@ w4a16_status w4a16_packed_size(int64_t N, int64_t K, int32_t group_size, int32_t
     return W4A16_OK;
 }
 
+
 w4a16_status w4a16_repack(const int32_t* weight_packed, const void* weight_scale, const int32_t* weight_zero_point,
                           int64_t N, int64_t K, int32_t group_size, int32_t qtype, void* packed, size_t packed_bytes,
                           hipStream_t stream) {
     clear_error();
-    Geometry g;
-    w4a16_status st = make_geometry(N, K, group_size, qtype, &g);
-    if (st != W4A16_OK) return st;
-    if (weight_packed == nullptr) return fail(W4A16_ERR_INVALID_ARG, "weight_packed is NULL");
-    if (weight_scale == nullptr) return fail(W4A16_ERR_INVALID_ARG, "weight_scale is NULL");
-    if (packed == nullptr) return fail(W4A16_ERR_INVALID_ARG, "packed is NULL");
-    if ((reinterpret_cast<uintptr_t>(weight_packed) & 3u) || (reinterpret_cast<uintptr_t>(weight_scale) & 1u) ||
-        (reinterpret_cast<uintptr_t>(weight_zero_point) & 3u))
-        return fail(W4A16_ERR_INVALID_ARG, "checkpoint tensors must be aligned to their element size");
-    if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
-    if (packed_bytes < g.total_bytes)
-        return fail(W4A16_ERR_SIZE, "packed_bytes=%zu is smaller than the %zu bytes the layout needs", packed_bytes,
-                    g.total_bytes);
-    hipError_t e = launch_repack(weight_packed, static_cast<const uint16_t*>(weight_scale),
-                                 qtype == W4A16_UINT4 ? weight_zero_point : nullptr, g, packed, stream);
-    if (e != hipSuccess) return hip_fail("repack launch", e);
-    return W4A16_OK;
+    return repack_impl(weight_packed, weight_scale, weight_zero_point, CheckpointLayout{}, N, K, group_size, qtype,
+                       packed, packed_bytes, stream);
+}
+
+w4a16_status w4a16_repack_layout(const int32_t* weight, int32_t weight_output_dim, int32_t weight_packed_dim,
+                                 const void* weight_scale, int32_t scale_output_dim, const int32_t* weight_zero_point,
+                                 int32_t zero_output_dim, int64_t N, int64_t K, int32_t group_size, int32_t qtype,
+                                 void* packed, size_t packed_bytes, hipStream_t stream) {
+    clear_error();
+    const int32_t dims[4] = {weight_output_dim, weight_packed_dim, scale_output_dim, zero_output_dim};
+    const char* names[4] = {"weight_output_dim", "weight_packed_dim", "scale_output_dim", "zero_output_dim"};
+    for (int i = 0; i < 4; ++i)
+        if (dims[i] != 0 && dims[i] != 1) return fail(W4A16_ERR_INVALID_ARG, "%s=%d must be 0 or 1", names[i], dims[i]);
+    CheckpointLayout lay;
+    lay.weight_n_first = weight_output_dim == 0;
+    lay.weight_k_packed = weight_packed_dim != weight_output_dim;
+    lay.scale_n_first = scale_output_dim == 0;
+    lay.zero_n_first = zero_output_dim == 0;
+    return repack_impl(weight, weight_scale, weight_zero_point, lay, N, K, group_size, qtype, packed, packed_bytes,
+                       stream);
 }
 
 w4a16_status w4a16_unpack(const void* packed, int64_t N, int64_t K, int32_t group_size, int32_t qtype,

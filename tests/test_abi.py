@@ -137,6 +137,29 @@ def test_repack_rejects(lib):
     assert "256-byte aligned" in w4.last_error()
 
 
+@pytest.mark.parametrize("dims,needle", [
+    ((2, 1, 0, 0), "weight_output_dim=2"),
+    ((0, -1, 0, 0), "weight_packed_dim=-1"),
+    ((0, 1, 3, 0), "scale_output_dim=3"),
+    ((0, 1, 0, 2), "zero_output_dim=2"),
+])
+def test_repack_layout_rejects_bad_dims(lib, dims, needle):
+    p = ctypes.c_void_p(4096)
+    od, pd, sd, zd = dims
+    assert lib.w4a16_repack_layout(p, od, pd, p, sd, None, zd, 16, 128, 128, 0, p, 1 << 20, None) == INVALID
+    assert needle in w4.last_error()
+
+
+def test_repack_layout_rejects_like_repack(lib):
+    p = ctypes.c_void_p(4096)
+    for od in (0, 1):
+        for pd in (0, 1):
+            assert lib.w4a16_repack_layout(None, od, pd, p, 1, None, 1, 16, 128, 128, 0, p, 1 << 20, None) == INVALID
+            assert "weight_packed is NULL" in w4.last_error()
+            assert lib.w4a16_repack_layout(p, od, pd, p, 1, None, 1, 16, 128, 128, 0, p, 1000, None) == SIZE
+            assert lib.w4a16_repack_layout(p, od, pd, p, 1, None, 1, 24, 128, 128, 0, p, 1 << 20, None) == UNSUPPORTED
+
+
 def test_select_path(lib):
     assert w4.select_path(1) == w4.PATH_SKINNY
     assert w4.select_path(16) == w4.PATH_SKINNY

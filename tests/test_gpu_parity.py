@@ -91,6 +91,96 @@ def test_repack_symmetric_ignores_zero_points():
     assert torch.equal(w4.repack(wq, ws, zp, 32, UINT4B8), w4.repack(wq, ws, None, 32, UINT4B8))
 
 
+# ------------------------------------------- repack from other orientations
+
+
+LAYOUTS = [
+    # (N, K, G, qtype, weight_output_dim, weight_packed_dim, scale_output_dim, zero_output_dim, zero points)
+    (16, 128, 128, UINT4B8, 1, 1, 1, 1, False),  # AWQ orientation, one tile
+    (48, 384, 32, UINT4, 1, 1, 1, 1, True),  # AWQ weight, AutoGPTQ zeros, several tiles
+    (48, 384, 64, UINT4, 1, 0, 1, 1, True),  # AutoGPTQ weight
+    (32, 256, -1, UINT4, 0, 0, 0, 0, True),  # packed along N, N first
+    (64, 512, 128, UINT4, 0, 1, 1, 0, True),  # compressed-tensors weight, (K/G, N) scales
+    (80, 640, 128, UINT4, 1, 1, 0, 1, False),  # uint4 without zero points
+    (4096, 4096, 128, UINT4, 1, 1, 1, 1, True),
+    (14336, 4096, 128, UINT4B8, 1, 0, 1, 1, False),
+    (4096, 14336, 32, UINT4, 0, 0, 0, 1, True),
+    (6144, 4096, -1, UINT4, 1, 1, 1, 1, True),
+]
+
+
+def _layout_dev(L):
+    w = torch.from_numpy(L.weight).to(DEV)
+    s = L.weight_scale.to(DEV)
+    z = None if L.weight_zero_point is None else torch.from_numpy(L.weight_zero_point).to(DEV)
+    return w, s, z
+
+
+def _layout_expect(L):
+    codes = oracle.weight_codes_nk(L.weight, L.weight_output_dim, L.weight_packed_dim)
+    scales = oracle.scales_nk(L.weight_scale, L.scale_output_dim)
+    zeros = None
+    if L.qtype == UINT4:
+        Kg = scales.shape[1]
+        zeros = (oracle.zeros_nk(L.weight_zero_point, L.zero_output_dim) if L.weight_zero_point is not None
+                 else np.zeros((L.N, Kg), dtype=np.uint8))
+    return codes, scales, zeros
+
+
+@pytest.mark.parametrize("N,K,G,qtype,od,pd,sd,zd,zp", LAYOUTS,
+                         ids=[f"{c[0]}x{c[1]}g{c[2]}q{c[3]}w{c[4]}{c[5]}s{c[6]}z{c[7]}{int(c[8])}" for c in LAYOUTS])
+def test_repack_layout_bit_exact(N, K, G, qtype, od, pd, sd, zd, zp):
+    L = wi.make_layout_weights(14, N, K, G, qtype, "bf16" if qtype == UINT4 else "f16", od, pd, sd, zd,
+                               with_zero_point=zp)
+    w, s, z = _layout_dev(L)
+    packed = w4.repack_layout(w, od, pd, s, sd, z, zd, G, qtype)
+    codes, scales, zeros = _layout_expect(L)
+    expect = oracle.encode_device(codes, scales, zeros, qtype, G)
+    got = packed.cpu().numpy()
+    assert got.shape == expect.shape
+    mism = np.flatnonzero(got != expect)
+    assert mism.size == 0, f"{mism.size} bytes differ, first at {mism[:8]}"
+
+
+def test_repack_layout_canonical_is_repack():
+    case = _case(15, 1, 96, 768, 64, UINT4, "bf16")
+    wq, ws, zp, _, _ = to_dev(case)
+    a = w4.repack(wq, ws, zp, 64, UINT4)
+    b = w4.repack_layout(wq, 0, 1, ws, 0, zp, 0, 64, UINT4)
+    assert torch.equal(a, b)
+    # Every orientation of the same checkpoint gives the same buffer.
+    N, K = 96, 768
+    wt = wq.t().contiguous()  # (K/8, N): output_dim 1, packed_dim 0
+    st = ws.t().contiguous()
+    zt = zp.t().contiguous()
+    assert torch.equal(w4.repack_layout(wt, 1, 0, st, 1, zt, 1, 64, UINT4), a)
+    assert a.numel() == w4.packed_size(N, K, 64, UINT4)
+
+
+@pytest.mark.parametrize("path", [w4.PATH_SKINNY, w4.PATH_MFMA])
+def test_gemm_from_awq_orientation(path):
+    # End to end: an AWQ-oriented checkpoint, repacked, multiplied; the
+    # oracle multiplies the same codes re-packed into its own input layout.
+    N, K, G, M = 256, 1024, 128, 16 if path == w4.PATH_SKINNY else 200
+    L = wi.make_layout_weights(16, N, K, G, UINT4, "bf16", 1, 1, 1, 1)
+    w, s, z = _layout_dev(L)
+    packed = w4.repack_layout(w, 1, 1, s, 1, z, 1, G, UINT4)
+    codes, scales, zeros = _layout_expect(L)
+    A = wi.random_activations(16, M, K, "bf16")
+    C = w4.gemm(A.to(DEV), packed, N, K, G, UINT4, path=path)
+    ref, _ = oracle.gemm(A, oracle.pack_codes(codes), scales, oracle.pack_zeros(zeros), UINT4, G)
+    assert oracle.rel_err(C.cpu(), ref) <= oracle.TOLERANCE["bf16"]
+
+
+def test_repack_layout_binding_rejects_shapes():
+    L = wi.make_layout_weights(17, 32, 256, 32, UINT4, "f16", 1, 1, 1, 1)  # Kg = 8, N/8 = 4
+    w, s, z = _layout_dev(L)
+    with pytest.raises(ValueError, match="weight_scale must be"):
+        w4.repack_layout(w, 1, 1, s.t().contiguous(), 1, z, 1, 32, UINT4)
+    with pytest.raises(ValueError, match="weight_zero_point must be"):
+        w4.repack_layout(w, 1, 1, s, 1, z.t().contiguous(), 1, 32, UINT4)
+
+
 # ------------------------------------------------------------------ dequant
 
 

@@ -111,6 +111,55 @@ def make_case(
     return Case(M, N, K, G, qtype, dtype, words.view(np.int32), scales, zp, A, bias)
 
 
+@dataclasses.dataclass
+class LayoutWeights:
+    """A checkpoint drawn directly in one of the other orientations: the
+    weight words ``[N, K/8]``, ``[N/8, K]``, ``[K, N/8]`` or ``[K/8, N]`` by
+    (output_dim, packed_dim), scales ``[N, Kg]`` or ``[Kg, N]``, zero-point words
+    ``[N/8, Kg]`` or ``[Kg, N/8]``."""
+
+    N: int
+    K: int
+    G: int
+    qtype: int
+    dtype: str
+    weight_output_dim: int
+    weight_packed_dim: int
+    scale_output_dim: int
+    zero_output_dim: int
+    weight: np.ndarray  # int32
+    weight_scale: torch.Tensor  # act dtype (CPU)
+    weight_zero_point: np.ndarray | None  # int32
+
+
+def make_layout_weights(cfg_id: int, N: int, K: int, G: int, qtype: int, dtype: str, weight_output_dim: int,
+                        weight_packed_dim: int, scale_output_dim: int, zero_output_dim: int,
+                        with_zero_point: bool | None = None) -> LayoutWeights:
+    """Draw a weight, scales and zero points in the given orientation: uniform
+    32-bit words (eight independent uniform nibbles each), scales as in
+    ``make_case``. Same draw order as ``make_case``, without activations."""
+    if with_zero_point is None:
+        with_zero_point = qtype == UINT4
+    Ge = effective_group(K, G)
+    if K % 8 or N % 8 or Ge <= 0 or K % Ge:
+        raise ValueError(f"cannot draw N={N}, K={K}, G={G}")
+    Kg = K // Ge
+    wdims = [N, K] if weight_output_dim == 0 else [K, N]
+    wdims[weight_packed_dim] //= 8
+    rng = np.random.default_rng(case_seed(cfg_id, 0, N, K, G, qtype, dtype,
+                                          1000 + 8 * weight_output_dim + 4 * weight_packed_dim
+                                          + 2 * scale_output_dim + zero_output_dim))
+    words = rng.integers(0, 2**32, size=tuple(wdims), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    sdims = (N, Kg) if scale_output_dim == 0 else (Kg, N)
+    scales = _to_act(rng.uniform(0.005, 0.02, size=sdims), dtype)
+    zp = None
+    if with_zero_point:
+        zdims = (N // 8, Kg) if zero_output_dim == 0 else (Kg, N // 8)
+        zp = rng.integers(0, 2**32, size=zdims, dtype=np.uint64).astype(np.uint32).view(np.int32)
+    return LayoutWeights(N, K, G, qtype, dtype, weight_output_dim, weight_packed_dim, scale_output_dim,
+                         zero_output_dim, words, scales, zp)
+
+
 def random_activations(cfg_id: int, M: int, K: int, dtype: str, sigma: float = 1.0, extra: int = 0) -> torch.Tensor:
     """Activations alone, for benchmarks that rotate several activation buffers."""
     rng = np.random.default_rng([cfg_id, M, K, DTYPE_CODES[dtype], 7919, extra])
