@@ -10,9 +10,10 @@ M to the skinny kernel. Inputs are synthetic (seeded, w4a16_inputs) and
 already repacked in HBM before timing (the repack is a one-time load step,
 timed separately). Every launch reads a different copy of its weights from a
 rotation pool larger than 1 GB, so neither L2 nor the 256 MB MALL can serve
-them. Steps are captured into HIP graphs (one per weight-copy set) and
-replayed; W untimed steps, then K timed steps between a device
-synchronisation and HIP events on the launch stream.
+them. Steps are captured into HIP graphs of eight steps each (step j of a
+graph uses weight copy j mod 4), as a serving loop captures a forward pass,
+plus one-step graphs for a remainder; W untimed steps, then exactly K timed
+steps between a device synchronisation and HIP events on the launch stream.
 
 Prints one JSON line: value = weight-stream GB/s of the whole step
 (codes + scales [+ zeros] bytes per GEMM, summed, over the step time), the
@@ -46,6 +47,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2516.6  # dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 DEV = "cuda:0"
 ROTATE_BYTES = 1 << 30
+ROUND_STEPS = 8  # decode steps per captured graph
 
 
 def weight_stream_bytes(N, K, G, qtype, with_zero_point):
@@ -146,6 +148,26 @@ def time_graphs(graphs, reps, warmup):
     return s.elapsed_time(e)
 
 
+def time_steps(round_graph, round_steps, step_graphs, steps, warmup):
+    """Elapsed ms of exactly `steps` steps: whole rounds from round_graph,
+    then the remainder from the one-step graphs (after `warmup` untimed
+    steps the same way)."""
+    def run(k):
+        for _ in range(k // round_steps):
+            round_graph.replay()
+        for i in range(k % round_steps):
+            step_graphs[i % len(step_graphs)].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    run(steps)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e)
+
+
 def copies_for(total_bytes_per_round, minimum=2):
     return max(minimum, -(-ROTATE_BYTES // max(1, total_bytes_per_round)))
 
@@ -166,6 +188,26 @@ def per_case_rate(g: Gemm, launches=None, reps=20):
     graphs = capture_graphs([[(lambda c=c: g.launch(c)) for c in range(n)]])
     ms = time_graphs(graphs, reps, 3)
     return ms * 1e3 / (reps * n)  # us per launch
+
+
+def per_case_spread(g: Gemm, reps=30, min_launches=64):
+    """p10 / p50 / p90 of the per-launch time over `reps` replays of one graph
+    of back-to-back launches (cycling through the rotating copies, at least
+    `min_launches` per graph so the replay's own overhead is spread thin), each
+    replay bracketed by its own pair of events."""
+    n = max(len(g.packed), min_launches)
+    graph = capture_graphs([[(lambda c=c: g.launch(c)) for c in range(n)]])[0]
+    for _ in range(3):
+        graph.replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        graph.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / n for i in range(reps))
+    pick = lambda q: per[min(reps - 1, int(round(q * (reps - 1))))]  # noqa: E731
+    return {"p10_us": round(pick(0.1), 2), "p50_us": round(pick(0.5), 2), "p90_us": round(pick(0.9), 2)}
 
 
 def cpu_baseline(budget_s=12.0):
@@ -380,10 +422,17 @@ def main():
     cases, copies = decode_cases()
     step_weight_bytes = sum(c.weight_bytes for c in cases)
     step_algo_bytes = sum(c.algo_bytes for c in cases)
-    # One graph per copy index: graph j runs the 12 GEMMs on copy j.
-    graphs = capture_graphs([[(lambda c=c, j=j: c.launch(j)) for c in cases] for j in range(copies)])
+    # Steps are replayed from graphs of ROUND_STEPS steps each (the 12 GEMMs
+    # on copy j for step j of the round), as a serving loop captures a whole
+    # forward pass; one-step graphs make up a remainder, so exactly
+    # args.steps steps are timed.
+    round_steps = ROUND_STEPS - ROUND_STEPS % copies if ROUND_STEPS >= copies else copies
+    step_graphs = capture_graphs([[(lambda c=c, j=j: c.launch(j)) for c in cases] for j in range(copies)])
+    round_graph = capture_graphs([[(lambda c=c, j=j: c.launch(j % copies)) for j in range(round_steps)
+                                   for c in cases]])[0]
     torch.cuda.synchronize()
-    ms = time_graphs(graphs, args.steps, args.warmup)
+    ms = time_steps(round_graph, round_steps, step_graphs, args.steps, args.warmup)
+    graphs = step_graphs + [round_graph]
     ms_per_step = ms / args.steps
     value = step_weight_bytes / (ms_per_step * 1e-3) / 1e9
     launches = len(cases)
@@ -392,10 +441,17 @@ def main():
 
     breakdown = []
     for c in ([] if args.no_breakdown else cases):
-        us = per_case_rate(c, reps=10)
+        # Each shape alone, over its own rotation of at least ROTATE_BYTES of
+        # weight copies (more than the last-level cache holds).
+        n0 = len(c.packed)
+        c.packed += [c.packed[0].clone() for _ in range(max(0, copies_for(c.weight_bytes) - n0))]
+        us = per_case_rate(c, reps=5)
         breakdown.append({"M": c.M, "N": c.N, "K": c.K, "us": round(us, 2),
                           "weight_GBps": round(c.weight_bytes / us / 1e3, 1),
-                          "frac_of_hbm_peak": round(c.weight_bytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+                          "frac_of_hbm_peak": round(c.weight_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                          "copies": len(c.packed), **per_case_spread(c)})
+        del c.packed[n0:]
+        torch.cuda.empty_cache()
 
     traffic = measured_traffic()
     result = {

@@ -505,9 +505,14 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
         u32x4 bq2[2][NJ];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            __builtin_amdgcn_sched_barrier(0);
+            // The loads of step st + 2 stay at their slice. With one group per
+            // row, LDS reads, VALU and MFMA may move across that point (mask
+            // 0x18F), so the next slice's fragment reads are hoisted over the
+            // current MFMAs; with groups the register budget is spent and the
+            // point is a full scheduling barrier.
+            __builtin_amdgcn_sched_barrier(OCM == 1 ? 0x18F : 0);
             issue(st + 2, s, nabuf, nbbuf, nsb, nzb);
-            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(OCM == 1 ? 0x18F : 0);
             if ((s & 1) == 0) {
                 // Slices s and s + 1 together: their words are adjacent
                 // registers, so one 64-bit shift serves both.
