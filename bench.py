@@ -48,6 +48,7 @@ MFMA_PEAK_TFLOPS = 2516.6  # dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/
 DEV = "cuda:0"
 ROTATE_BYTES = 1 << 30
 ROUND_STEPS = 8  # decode steps per captured graph
+PREFILL_WARM_MS = 200.0  # GPU time of the same GEMM replayed before a prefill shape is timed
 
 
 def weight_stream_bytes(N, K, G, qtype, with_zero_point):
@@ -181,11 +182,28 @@ def decode_cases():
     return cases, copies
 
 
-def per_case_rate(g: Gemm, launches=None, reps=20):
+def warm_up(graphs, warm_ms):
+    """Replays graphs until about warm_ms of GPU time has passed, so that
+    the clocks have left their idle state before anything is timed (a
+    prefill GEMM follows seconds of host-side input generation)."""
+    done, i = 0.0, 0
+    while done < warm_ms:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(4):
+            graphs[i % len(graphs)].replay()
+            i += 1
+        e.record()
+        torch.cuda.synchronize()
+        done += s.elapsed_time(e)
+
+
+def per_case_rate(g: Gemm, launches=None, reps=20, warm_ms=0.0):
     """Average duration of one launch of g, from graphs of back-to-back
-    launches over its rotating copies."""
+    launches over its rotating copies (after warm_ms of the same work)."""
     n = launches or len(g.packed)
     graphs = capture_graphs([[(lambda c=c: g.launch(c)) for c in range(n)]])
+    warm_up(graphs, warm_ms)
     ms = time_graphs(graphs, reps, 3)
     return ms * 1e3 / (reps * n)  # us per launch
 
@@ -269,7 +287,7 @@ def prefill_rates():
     for (G, qt) in wl["variants"]:
         for (M, N, K) in wl["shapes"]:
             g = Gemm(wl["cfg_id"], M, N, K, G, qt, wl["dtype"], wl["sigma"], 2)
-            us = per_case_rate(g, launches=2, reps=5)
+            us = per_case_rate(g, launches=2, reps=10, warm_ms=PREFILL_WARM_MS)
             tf = g.flops / us / 1e6
             rows.append({"M": M, "N": N, "K": K, "G": G, "qtype": qt, "us": round(us, 1), "tflops": round(tf, 1),
                          "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4)})
@@ -286,6 +304,31 @@ def prefill_rates():
     }
 
 
+def row_stride_rates(pads=(0, 64, 256, 0)):
+    """Prefill GEMMs (G = -1, uint4b8, bf16) with the activation and output
+    row strides at their widths (8 KB to 28 KB rows, multiples of large powers
+    of two) and padded by `pad` elements (64 = one 128-byte line): does a
+    power-of-two row stride cost HBM channel balance on gfx950? Each stride
+    is timed after the same warm-up, and the unpadded one again last, so an
+    order effect would show as two different pad0 values."""
+    rows = []
+    for (M, N, K) in [(8192, 14336, 4096), (8192, 4096, 14336), (2048, 14336, 4096)]:
+        g = Gemm(5, M, N, K, -1, wi.UINT4B8, "bf16", 1.0, 2)
+        A0 = g.A
+        row = {"M": M, "N": N, "K": K}
+        for pad in pads:
+            g.A = torch.empty((M, K + pad), dtype=A0.dtype, device=DEV)[:, :K]
+            g.A.copy_(A0)
+            g.C = torch.empty((M, N + pad), dtype=A0.dtype, device=DEV)[:, :N]
+            us = per_case_rate(g, launches=2, reps=10, warm_ms=PREFILL_WARM_MS)
+            key = f"pad{pad}_us" if f"pad{pad}_us" not in row else f"pad{pad}_again_us"
+            row[key] = round(us, 1)
+        rows.append(row)
+        del g, A0
+        torch.cuda.empty_cache()
+    return {"workload": "lda = K + pad, ldc = N + pad (elements), G=-1 uint4b8 bf16, MFMA path", "rows": rows}
+
+
 def prefill_dense_rates():
     """The dense prefill variant on the prefill workload: the dequantisation of
     each weight into a dense copy (w4a16_dequant) and hipBLASLt on that copy
@@ -300,9 +343,11 @@ def prefill_dense_rates():
             dense = [torch.empty((N, K), dtype=dt, device=DEV) for _ in range(2)]
             deq = capture_graphs([[(lambda c=c: w4.dequant(g.packed[c], N, K, G, qt, dt, out=dense[c]))
                                    for c in range(2)]])
+            warm_up(deq, 20.0)
             us_deq = time_graphs(deq, 5, 2) * 1e3 / 10
             mm = capture_graphs([[(lambda c=c: w4.gemm_dense(g.A, dense[c], out=g.C)) for c in range(2)]])
-            us_mm = time_graphs(mm, 5, 2) * 1e3 / 10
+            warm_up(mm, PREFILL_WARM_MS)
+            us_mm = time_graphs(mm, 10, 2) * 1e3 / 20
             rows.append({"M": M, "N": N, "K": K, "G": G, "qtype": qt, "dequant_us": round(us_deq, 1),
                          "gemm_us": round(us_mm, 1), "gemm_tflops": round(g.flops / us_mm / 1e6, 1),
                          "total_tflops": round(g.flops / (us_mm + us_deq) / 1e6, 1)})
@@ -391,6 +436,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-shape decode timings")
+    ap.add_argument("--strides-only", action="store_true",
+                    help="only time prefill GEMMs with padded and unpadded activation/output row strides")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time the prefill workload (MFMA kernel, and the dense variant) and print its JSON")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -415,6 +462,9 @@ def main():
         print(json.dumps({"calibration_copy_bytes": n, "copies": 10}), flush=True)
         return
     w4.load_library()
+    if args.strides_only:
+        print(json.dumps({"row_strides": row_stride_rates()}), flush=True)
+        return
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_rates(), "prefill_dense": prefill_dense_rates()}), flush=True)
         return
