@@ -477,6 +477,16 @@ def test_device_size_hand_values(oracle_mod):
     assert oracle_mod.device_size(16, 128, -1, UINT4) == 1536
     # N=4096, K=4096, G=128: 8 MiB codes + 256 KiB scales.
     assert oracle_mod.device_size(4096, 4096, 128, UINT4B8) == 4096 * 2048 + 4096 * 32 * 2
+    # K not a multiple of 128 pads K to Kp and the groups to Kp / G.
+    # N=16, K=96, G=32: Kp=128, 4 stored groups: codes 1024; scales 16*4*2 = 128
+    # -> 1152; zeros at 1280, 64 bytes -> 1344 -> 1536 (uint4b8: 1152 -> 1280).
+    assert oracle_mod.device_size(16, 96, 32, UINT4) == 1536
+    assert oracle_mod.device_size(16, 96, 32, UINT4B8) == 1280
+    # N=16, K=40, one group: Kp=128: codes 1024, scales 32 -> 1056 -> 1280.
+    assert oracle_mod.device_size(16, 40, -1, UINT4B8) == 1280
+    # N=32, K=2880, G=64: Kp=2944, 46 stored groups (45 real): codes 47104
+    # (256-aligned), scales 32*46*2 = 2944 -> 50048 -> 50176.
+    assert oracle_mod.device_size(32, 2880, 64, UINT4B8) == 50176
 
 
 def test_device_encoder_hand_words(oracle_mod):
@@ -514,6 +524,73 @@ def test_device_encoder_hand_words(oracle_mod):
     sb = out[4096 : 4096 + 64 * 2].view(np.uint16)
     assert np.all(sb == 0x3800)
     assert len(out) == 4352
+
+
+def test_device_encoder_padded_k_hand_words(oracle_mod):
+    # N = 16, K = 40 (one group): Kp = 128, one tile; codes c(n, k) = k % 16.
+    # Word 4l + s holds row l%16 at k = 32s + 8(l//16) + i; k >= 40 holds 0.
+    N, K = 16, 40
+    codes = np.tile((np.arange(K) % 16).astype(np.uint8), (N, 1))
+    out = oracle_mod.encode_device(codes, torch.full((N, 1), 0.5, dtype=torch.float16), None, UINT4B8, -1)
+    assert len(out) == 1280
+    w = out[:1024].view(np.uint32)
+    assert w[4 * 0 + 0] == 0x75316420  # l=0,  s=0: k 0..7   -> codes 0..7
+    assert w[4 * 16 + 0] == 0xFDB9ECA8  # l=16, s=0: k 8..15  -> codes 8..15
+    assert w[4 * 48 + 0] == 0xFDB9ECA8  # l=48, s=0: k 24..31 -> codes 8..15
+    assert w[4 * 0 + 1] == 0x75316420  # l=0,  s=1: k 32..39 -> codes 0..7
+    assert w[4 * 16 + 1] == 0  # l=16, s=1: k 40..47, past K
+    assert w[4 * 5 + 2] == 0 and w[4 * 63 + 3] == 0  # k >= 64
+    # 1 KB of codes, then the 16 scales (fp16 0.5 = 0x3800) at 1024.
+    assert np.all(out[1024:1056].view(np.uint16) == 0x3800)
+    assert np.all(out[1056:] == 0)
+
+
+def test_device_encoder_padded_groups_hand_values(oracle_mod):
+    # N = 16, K = 96, G = 32: Kg = 3 real groups, 4 stored; scale of group g
+    # is g + 1 (fp16 0x3C00, 0x4000, 0x4200), zero of (n, g) is (n + g) % 16.
+    N, K, G = 16, 96, 32
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = torch.tensor([[1.0, 2.0, 3.0]] * N, dtype=torch.float16)
+    zeros = np.array([[(n + g) % 16 for g in range(3)] for n in range(N)], dtype=np.uint8)
+    out = oracle_mod.encode_device(codes, scales, zeros, UINT4, G)
+    assert len(out) == 1536
+    sreg = out[1024:1024 + 4 * 16 * 2].view(np.uint16).reshape(4, 16)  # (g, r) of n-tile 0
+    assert np.all(sreg[0] == 0x3C00) and np.all(sreg[1] == 0x4000) and np.all(sreg[2] == 0x4200)
+    assert np.all(sreg[3] == 0)
+    zreg = out[1280:1280 + 64].reshape(4, 16)
+    for g in range(3):
+        assert list(zreg[g]) == [(r + g) % 16 for r in range(16)]
+    assert np.all(zreg[3] == 0)
+    assert np.all(out[:1024] == 0) and np.all(out[1344:] == 0)
+
+
+def test_device_encoder_padded_inverse(oracle_mod):
+    # K = 160, G = 32: Kp = 256 (two k-tiles), Kg = 5, Kgp = 8; read every
+    # code, scale and zero back by the layout rule, and check the padding.
+    c = wi.make_case(38, 1, 32, 160, 32, UINT4, "f16")
+    codes = oracle_mod.unpack_codes(c.weight_packed)
+    zeros = oracle_mod.unpack_zeros(c.weight_zero_point, 32)
+    out = oracle_mod.encode_device(codes, c.weight_scale, zeros, UINT4, 32)
+    N, K, Kp, Kg, Kgp, KT = 32, 160, 256, 5, 8, 2
+    words = out[: N * Kp // 2].view(np.uint32)
+    for n in range(N):
+        for k in range(0, Kp, 8):
+            nt, r, kt = n // 16, n % 16, k // 128
+            s_, sub = (k % 128) // 32, (k % 32) // 8
+            word = int(words[(nt * KT + kt) * 256 + 4 * (16 * sub + r) + s_])
+            for i in range(8):
+                want = codes[n, k + i] if k + i < K else 0
+                assert (word >> (4 * (i // 2) + 16 * (i % 2))) & 0xF == want
+    S0 = N * Kp // 2
+    sbits = c.weight_scale.view(torch.int16).numpy().view(np.uint16)
+    sreg = out[S0 : S0 + N * Kgp * 2].view(np.uint16)
+    Z0 = S0 + ((N * Kgp * 2 + 255) // 256) * 256
+    for n in range(N):
+        for g in range(Kgp):
+            idx = ((n // 16) * Kgp + g) * 16 + n % 16
+            assert sreg[idx] == (sbits[n, g] if g < Kg else 0)
+            assert out[Z0 + idx] == (zeros[n, g] if g < Kg else 0)
+    assert len(out) == oracle_mod.device_size(N, K, 32, UINT4)
 
 
 def test_device_encoder_inverse(oracle_mod):

@@ -54,8 +54,13 @@ MUTANTS = [
     ("encode_lane_rows", "const int64_t n = 16 * nt + l % 16;", "const int64_t n = 16 * nt + (l / 4) % 16;"),
     ("encode_subblock", "const int64_t k0 = 128 * kt + 32 * s + 8 * (l / 16);",
      "const int64_t k0 = 128 * kt + 32 * (l / 16) + 8 * s;"),
-    ("encode_scale_order", "const int64_t off = S0 + ((nt * Kg + g) * 16 + r) * 2;",
-     "const int64_t off = S0 + ((nt * 16 + r) * Kg + g) * 2;"),
+    ("encode_scale_order", "const int64_t off = S0 + ((nt * Kgp + g) * 16 + r) * 2;",
+     "const int64_t off = S0 + ((nt * 16 + r) * Kgp + g) * 2;"),
+    ("encode_scales_unpadded_stride", "const int64_t off = S0 + ((nt * Kgp + g) * 16 + r) * 2;",
+     "const int64_t off = S0 + ((nt * Kg + g) * 16 + r) * 2;"),
+    ("layout_k_rounded_to_64", "return (K + 127) / 128 * 128;", "return (K + 63) / 64 * 64;"),
+    ("layout_groups_unpadded", "return K / Ge == 1 ? 1 : padded_k(K) / Ge;", "return K / Ge;"),
+    ("encode_zeros_unpadded_stride", "out[Z0 + (nt * Kgp + g) * 16 + r]", "out[Z0 + (nt * Kg + g) * 16 + r]"),
 ]
 
 # Pins to run (function, kwargs). Parametrised pins are listed per case.
@@ -76,6 +81,10 @@ PIN_CALLS = [
     (pins.test_gemm_exact_rational, dict(M=2, N=16, K=128, G=128, qtype=pins.UINT4, with_bias=True)),
     (pins.test_device_encoder_hand_words, {}),
     (pins.test_device_encoder_inverse, {}),
+    (pins.test_device_size_hand_values, {}),
+    (pins.test_device_encoder_padded_k_hand_words, {}),
+    (pins.test_device_encoder_padded_groups_hand_values, {}),
+    (pins.test_device_encoder_padded_inverse, {}),
 ]
 
 
