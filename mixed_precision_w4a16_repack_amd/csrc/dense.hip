@@ -28,7 +28,7 @@ template <int DT, int QT>
 __global__ __launch_bounds__(256) void dequant_kernel(const u32x4* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t KTT, int64_t Kg,
-                                                      int gshift, int one_group, int64_t tiles,
+                                                      int gshift, int one_group, int64_t tiles, int64_t K,
                                                       uint16_t* __restrict__ dense, int64_t ldw) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= tiles) return;
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const u32x4* __restrict__ 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int64_t k0 = kt * 128 + 32 * s + 8 * g4;
+        if (k0 >= K) continue;  // padding of K (K % 8 == 0: all eight or none)
         const int64_t g = one_group ? 0 : (k0 >> gshift);
         const int64_t idx = (nt * Kg + g) * 16 + r;
         const int z = QT ? (int)zeros[idx] : 8;
@@ -93,17 +94,17 @@ hipError_t launch_dequant(const void* packed, const Geometry& g, int dtype, void
     const u32x4* codes = reinterpret_cast<const u32x4*>(base);
     const uint16_t* scales = reinterpret_cast<const uint16_t*>(base + g.scales_off);
     const uint8_t* zeros = g.qtype == 1 ? base + g.zeros_off : nullptr;
-    const int64_t KTT = g.K / 128;
+    const int64_t KTT = g.Kp / 128;
     const int64_t tiles = (g.N / 16) * KTT;
     const dim3 grid((unsigned)((tiles + 3) / 4));
     const int one = g.Kg == 1;
     uint16_t* out = static_cast<uint16_t*>(dense);
     if (dtype == 0) {
-        if (g.qtype) hipLaunchKernelGGL((dequant_kernel<0, 1>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, out, ldw);
-        else hipLaunchKernelGGL((dequant_kernel<0, 0>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, out, ldw);
+        if (g.qtype) hipLaunchKernelGGL((dequant_kernel<0, 1>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.K, out, ldw);
+        else hipLaunchKernelGGL((dequant_kernel<0, 0>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.K, out, ldw);
     } else {
-        if (g.qtype) hipLaunchKernelGGL((dequant_kernel<1, 1>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, out, ldw);
-        else hipLaunchKernelGGL((dequant_kernel<1, 0>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, out, ldw);
+        if (g.qtype) hipLaunchKernelGGL((dequant_kernel<1, 1>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.K, out, ldw);
+        else hipLaunchKernelGGL((dequant_kernel<1, 0>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.K, out, ldw);
     }
     return hipGetLastError();
 }

@@ -12,8 +12,10 @@ namespace w4a16 {
 // Geometry of one packed weight (see the layout in include/w4a16.h).
 struct Geometry {
     int64_t N = 0, K = 0;
+    int64_t Kp = 0;       // K padded to a multiple of 128 (the packed layout's K)
     int32_t Ge = 0;       // effective group size
-    int64_t Kg = 0;       // groups per row
+    int64_t Kg = 0;       // groups per row stored in the layout (Kp / Ge, or 1)
+    int64_t Kg_ck = 0;    // groups per row of the checkpoint (K / Ge)
     int32_t gshift = 0;   // log2(Ge) when Kg > 1 (Ge is then a power of two)
     int32_t qtype = 0;    // 0 uint4b8, 1 uint4
     size_t codes_bytes = 0, scales_off = 0, zeros_off = 0, total_bytes = 0;

@@ -39,7 +39,8 @@ struct MfmaArgs {
     const uint16_t* scales;
     const uint8_t* zeros;
     int64_t N;
-    int64_t KTT;  // K / 128
+    int64_t KTT;  // padded K / 128
+    int64_t K;    // K: activation columns past it read as zero
     int64_t Kg;
     int gshift;
     int one_group;
@@ -102,7 +103,7 @@ __device__ __forceinline__ TileBufs tile_bufs(const MfmaArgs& a, int64_t m0, int
     const int64_t mr = a.M - t.mb < rows ? a.M - t.mb : rows;  // >= 1 rows of A
     const int64_t nn = NT - nt0 < ntn ? NT - nt0 : ntn;        // >= 1 n-tiles
     t.A = a.A + t.mb * a.lda;
-    t.a_bytes = (uint32_t)(((mr - 1) * a.lda + a.KTT * 128) * 2);
+    t.a_bytes = (uint32_t)(((mr - 1) * a.lda + a.K) * 2);
     t.codes = a.codes + nt0 * a.KTT * 64;
     t.codes_bytes = (uint32_t)(nn * a.KTT * 1024);
     t.scales = a.scales + nt0 * a.Kg * 16;
@@ -131,7 +132,7 @@ __device__ __forceinline__ TileBufs tile_bufs(const MfmaArgs& a, int64_t m0, int
 // registers for the accumulators.
 // OCM: 0 scale-first dequantisation; 1 offset-corrected with one group per
 // row (scales applied in the epilogue).
-template <int DT, int QT, int SPT, int BM, int WM, int NJ, int KS, int OCM>
+template <int DT, int QT, int SPT, int BM, int WM, int NJ, int KS, int OCM, int KT = 0>
 __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
     static_assert(OCM == 0 || OCM == 1, "scale first, or one group per row");
     constexpr bool OC = OCM != 0;
@@ -183,6 +184,9 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         if (row > a.M - 1) row = a.M - 1;
         a_off[t] = (uint32_t)(((row - tb.mb) * a.lda + 8 * g4) * 2);
     }
+    // KT (K % 128 != 0): a lane whose 8 columns start at or past K reads
+    // zeros (offset 2^31 is past the descriptor's range: no memory access).
+    const int32_t k_end = (int32_t)a.K - 8 * g4;
     auto stage_a = [&](int64_t st, int buf, bool live) {
 #pragma unroll
         for (int t = 0; t < BPW; ++t) {
@@ -190,7 +194,8 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
             const int kk = (b / 4) % KS, s = b % 4;
             const int64_t kt = st * KS + kk;
             const __amdgpu_buffer_rsrc_t rs_a = rsrc(tb.A, tb.a_bytes, live && kt < a.KTT);
-            load_lds16(rs_a, (buf ? abuf1 : abuf0) + b * 1024, a_off[t], (uint32_t)((kt * 128 + 32 * s) * 2));
+            const uint32_t voff = KT && (int32_t)(kt * 128 + 32 * s) >= k_end ? 0x80000000u : a_off[t];
+            load_lds16(rs_a, (buf ? abuf1 : abuf0) + b * 1024, voff, (uint32_t)((kt * 128 + 32 * s) * 2));
         }
     };
 
@@ -349,9 +354,12 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
 //    sum_g s_g * P_g without ever clearing P, and the correction
 //    -s_g * (m+z_g) * S_g is applied one step later, once the row sums of
 //    the group have passed the step's barrier.
-template <int DT, int QT, int OCM, int BM>
+template <int DT, int QT, int OCM, int BM, int KT>
 __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     static_assert(OCM == 1 || OCM == 2, "offset-corrected modes only");
+    // KT: K is not a multiple of 128 (possible with one group per row only:
+    // groups of 128 or 256 divide K), so the last step masks the activation.
+    static_assert(KT == 0 || OCM == 1, "a K tail needs one group per row");
     static_assert(BM == 128 || BM == 64, "whole or half tiles");
     constexpr int WN = 4, MI = BM / 32, NJ = 4;
     constexpr int ABLK = BM / 4, BBLK = 16;         // 1 KB blocks per stage
@@ -405,6 +413,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
         b_tile[t] = (uint32_t)((nt < NT ? nt : NT - 1) - ntb);
     }
     const uint32_t lane16 = (uint32_t)lane * 16;
+    const int32_t k_end = (int32_t)a.K - 8 * g4;
     auto nt_of = [&](int j) { return ntb + wn * NJ + j; };
     auto nt_ld = [&](int j) { return nt_of(j) < NT ? nt_of(j) : NT - 1; };
 
@@ -417,8 +426,12 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
                      uint32_t (&zb)[NJ]) {
         const bool live = st < steps;
         const int b = wave * APW + p;
+        // With a K tail, a lane whose 8 columns start at or past K reads
+        // zeros (offset 2^31 is past the descriptor's range: no memory access).
         if (p < APW)
-            load_lds16(rsrc(tb.A, tb.a_bytes, live), abuf + b * 1024, a_off[p], (uint32_t)((st * 128 + 32 * (b & 3)) * 2));
+            load_lds16(rsrc(tb.A, tb.a_bytes, live), abuf + b * 1024,
+                       KT && (int32_t)(st * 128 + 32 * (b & 3)) >= k_end ? 0x80000000u : a_off[p],
+                       (uint32_t)((st * 128 + 32 * (b & 3)) * 2));
         if (p < BPW)
             load_lds16(rsrc(tb.codes, tb.codes_bytes, live), bbuf + (wave * BPW + p) * 1024, lane16,
                        (uint32_t)((b_tile[p] * a.KTT + st) * 1024));
@@ -615,7 +628,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     }
 }
 
-template <int DT, int QT, int OCM>
+template <int DT, int QT, int OCM, int KT>
 hipError_t launch_ring_ocm(MfmaArgs a, hipStream_t stream) {
     // 128 x 256 tiles, row-major over m-tiles x n-blocks, one workgroup per
     // CU at a time. When the last round of workgroups would be at most half
@@ -625,12 +638,12 @@ hipError_t launch_ring_ocm(MfmaArgs a, hipStream_t stream) {
     const int64_t tail = tiles % kCUs;
     const int64_t full = tiles > kCUs && tail > 0 && 2 * tail <= kCUs ? tiles - tail : tiles;
     a.tile0 = 0;
-    hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, OCM, 128>), dim3((unsigned)full), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, OCM, 128, KT>), dim3((unsigned)full), dim3(512), 0, stream, a);
     if (full < tiles) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         a.tile0 = full;
-        hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, OCM, 64>), dim3((unsigned)(2 * (tiles - full))), dim3(512), 0,
+        hipLaunchKernelGGL((mfma_ring_kernel<DT, QT, OCM, 64, KT>), dim3((unsigned)(2 * (tiles - full))), dim3(512), 0,
                            stream, a);
     }
     return hipGetLastError();
@@ -640,7 +653,8 @@ template <int DT, int QT>
 hipError_t launch_ring_t(MfmaArgs a, hipStream_t stream) {
     a.m_tiles = (a.M + 127) / 128;
     a.n_blocks = (a.N + 255) / 256;
-    return a.one_group ? launch_ring_ocm<DT, QT, 1>(a, stream) : launch_ring_ocm<DT, QT, 2>(a, stream);
+    if (!a.one_group) return launch_ring_ocm<DT, QT, 2, 0>(a, stream);
+    return a.K % 128 ? launch_ring_ocm<DT, QT, 1, 1>(a, stream) : launch_ring_ocm<DT, QT, 1, 0>(a, stream);
 }
 
 template <int DT, int QT, int BM, int WM, int NJ, int KS>
@@ -672,8 +686,28 @@ hipError_t launch_lds_wide(const MfmaArgs& a, int spt, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// K % 128 != 0 with groups below 128 or a narrow launch: one tile shape of
+// the staged kernel, built with the K mask (the other shapes stay without it).
+template <int DT, int QT>
+hipError_t launch_lds_ktail(const MfmaArgs& a, int spt, hipStream_t stream) {
+    constexpr int BM = 64, WM = 2, NJ = 1, KS = 2, BN = (8 / WM) * NJ * 16;
+    const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
+    if (a.one_group) {
+        hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 1, BM, WM, NJ, KS, 1, 1>), grid, dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
+    switch (spt) {  // a K tail leaves groups of 32 or 64 only
+        case 2: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 2, BM, WM, NJ, KS, 0, 1>), grid, dim3(512), 0, stream, a); break;
+        default: hipLaunchKernelGGL((mfma_lds_kernel<DT, QT, 4, BM, WM, NJ, KS, 0, 1>), grid, dim3(512), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
 template <int DT, int QT>
 hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, hipStream_t stream) {
+    // The ring kernel masks a K tail itself (one group per row); every other
+    // K % 128 != 0 case takes the staged kernel's masked instance.
+    if (a.K % 128 != 0 && !(p.BN == 256 && spt == 1)) return launch_lds_ktail<DT, QT>(a, spt, stream);
     if (p.BN == 256) {
         // Offset-corrected modes run on the three-stage ring.
         return spt == 1 ? launch_ring_t<DT, QT>(a, stream) : launch_lds_wide<DT, QT>(a, spt, stream);
@@ -715,7 +749,8 @@ hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed
     a.scales = reinterpret_cast<const uint16_t*>(base + g.scales_off);
     a.zeros = g.qtype == 1 ? base + g.zeros_off : nullptr;
     a.N = g.N;
-    a.KTT = g.K / 128;
+    a.KTT = g.Kp / 128;
+    a.K = g.K;
     a.Kg = g.Kg;
     a.gshift = g.gshift;
     a.one_group = g.Kg == 1;

@@ -42,7 +42,7 @@ struct SkinnyArgs {
     const uint16_t* scales;
     const uint8_t* zeros;
     int64_t NT;   // N / 16
-    int64_t KTT;  // K / 128
+    int64_t KTT;  // padded K / 128
     int64_t Kg;
     int gshift;
     int one_group;
@@ -59,6 +59,7 @@ struct SkinnyArgs {
     int kc_tiles;          // split register variant: k-tiles per K chunk
     int nn_max;            // full-K variants: n-tiles per workgroup, at most
     uint32_t codes_bytes, scales_bytes, zeros_bytes;  // region sizes (< 2^31 on the full-K paths)
+    int64_t K;    // activation columns past K read as zero (split kernel; the full-K paths need K % 128 == 0)
 };
 
 // Cross-workgroup exchange of split-K partial sums. Every access carries the
@@ -121,19 +122,20 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
 
     // 1. Activation fragments: lane (r, g4) of word s of tile j holds
     //    A[r][128*(kt0+j) + 32*s + 8*g4 .. +7]; rows past M read row M-1.
-    //    A k-tile past K (a ragged last chunk) contributes zeros.
-    //    (The load itself uses a clamped k-tile, so it is always in bounds.)
+    //    A k-tile past the last one (a ragged last chunk) and the columns
+    //    past K (K % 128 != 0) contribute zeros and are not read.
     const int rr = r < a.M ? r : a.M - 1;
     const uint16_t* arow = a.A + (int64_t)rr * a.lda + 8 * g4;
     u32x4 av[KT][4];
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
-        const bool live = kt0 + j < a.KTT;
-        const int64_t kt = live ? kt0 + j : a.KTT - 1;
+        const int64_t kt = kt0 + j;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(arow + kt * 128 + 32 * s);
-            av[j][s] = live ? v : u32x4{0u, 0u, 0u, 0u};
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (kt < a.KTT && (int32_t)(kt * 128 + 32 * s + 8 * g4) < (int32_t)a.K)
+                v = *reinterpret_cast<const u32x4*>(arow + kt * 128 + 32 * s);
+            av[j][s] = v;
         }
     }
 
@@ -330,6 +332,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // Activation rows [0, M) of one launch; a_bytes = ((M-1)*lda + K)*2 < 2^31.
+// The full-K variants that use it run only with K % 128 == 0 (the planner
+// sends other K to the split kernel), so every k-tile is whole.
 struct ActRows {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t lane_off;  // byte offset of this lane's row and 8-element slice
@@ -629,7 +633,8 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
     //    real rows are read: the padding rows of the MFMA operand come from
     //    LDS later, which has about three times the return bandwidth.
     //    Chunk c is row c / CPR, column chunk c % CPR (CPR = KTW*16, a
-    //    constant); columns past the wave's kc k-tiles are not loaded.
+    //    constant); columns past the wave's kc k-tiles are not loaded. K is
+    //    a multiple of 128 here, so every loaded column is < K.
     constexpr int CPR = KTW * 16;
     const int nch = a.M * CPR;
     const int ccols = kc * 16;
@@ -887,10 +892,13 @@ void launch_skinny_q(const SkinnyArgs& a, const SkinnyPlan& p, int spt, dim3 gri
 
 SkinnyPlan plan_skinny(int64_t M, const Geometry& g) {
     SkinnyPlan p;  // the workspace is sized for 16 rows, so one serves every M <= 16
-    const int64_t NT = g.N / 16, KTT = g.K / 128;
+    const int64_t NT = g.N / 16, KTT = g.Kp / 128;
     // The wide-weight variants address each region of the packed weight with
     // 32-bit offsets below 2^31 (codes N*K/2 bytes, the largest).
-    if (NT >= kFullKMinTiles && g.codes_bytes < ((size_t)1 << 31)) {
+    // The wide-weight variants read whole k-tiles of A: K % 128 == 0 only.
+    // A K that is not (the layout pads it) goes to the split kernel below,
+    // whose activation loads stop at K.
+    if (NT >= kFullKMinTiles && g.codes_bytes < ((size_t)1 << 31) && g.K % 128 == 0) {
         // Wide weights: one workgroup per CU while N allows, n-tiles spread
         // evenly.
         p.full_k = true;
@@ -967,7 +975,8 @@ hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* pack
     a.scales = reinterpret_cast<const uint16_t*>(base + g.scales_off);
     a.zeros = g.qtype == 1 ? base + g.zeros_off : nullptr;
     a.NT = g.N / 16;
-    a.KTT = g.K / 128;
+    a.KTT = g.Kp / 128;
+    a.K = g.K;
     a.Kg = g.Kg;
     a.gshift = g.gshift;
     a.one_group = g.Kg == 1;

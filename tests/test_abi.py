@@ -60,11 +60,20 @@ def test_packed_size_values(lib):
     assert w4.packed_size(4096, 14336, 14336, w4.UINT4) == w4.packed_size(4096, 14336, -1, w4.UINT4)
 
 
+@pytest.mark.parametrize("N,K,G,qtype", [(16, 40, -1, 0), (48, 96, 32, 1), (32, 2880, 64, 0), (4096, 1216, 64, 1),
+                                          (256, 200, -1, 1), (4096, 14344, -1, 0)])
+def test_packed_size_padded_k_matches_oracle(N, K, G, qtype):
+    import oracle
+
+    assert w4.packed_size(N, K, G, qtype) == oracle.device_size(N, K, G, qtype)
+
+
 @pytest.mark.parametrize(
     "N,K,G,qtype,status,needle",
     [
         (4100, 4096, 128, 0, UNSUPPORTED, "N=4100 must be divisible by 16"),
-        (4096, 4100, 128, 0, UNSUPPORTED, "K=4100 must be divisible by 128"),
+        (4096, 4100, 128, 0, UNSUPPORTED, "K=4100 must be divisible by 8"),
+        (4096, 4000, 128, 0, UNSUPPORTED, "K=4000 must be divisible by group_size=128"),
         (4096, 4096, 96, 0, UNSUPPORTED, "group_size=96 not supported"),
         (4096, 4096, 16, 0, UNSUPPORTED, "group_size=16 not supported"),
         (4096, 384, 256, 0, UNSUPPORTED, "K=384 must be divisible by group_size=256"),
@@ -107,7 +116,7 @@ def _gemm(lib, **kw):
         (dict(lda=4100), UNSUPPORTED, "lda % 8 == 0"),
         (dict(A=ctypes.c_void_p(4104)), UNSUPPORTED, "16-byte aligned"),
         (dict(packed=ctypes.c_void_p(4100)), INVALID, "256-byte aligned"),
-        (dict(K=4000, lda=4000), UNSUPPORTED, "K=4000 must be divisible by 128"),
+        (dict(K=4004, lda=4004), UNSUPPORTED, "K=4004 must be divisible by 8"),
         (dict(bias=ctypes.c_void_p(4097)), INVALID, "2-byte aligned"),
         # the tiled path addresses one workgroup's tile with 32-bit offsets
         (dict(M=256, lda=1 << 23), UNSUPPORTED, "too large for the tiled path"),
@@ -199,7 +208,7 @@ def _dequant(lib, **kw):
     "kw,status,needle",
     [
         (dict(dtype=2), INVALID, "dtype=2"),
-        (dict(K=4000, ldw=4000), UNSUPPORTED, "K=4000 must be divisible by 128"),
+        (dict(K=4004, ldw=4004), UNSUPPORTED, "K=4004 must be divisible by 8"),
         (dict(packed=None), INVALID, "must not be NULL"),
         (dict(dense=None), INVALID, "must not be NULL"),
         (dict(packed=ctypes.c_void_p(4100)), INVALID, "256-byte aligned"),

@@ -181,6 +181,120 @@ def test_repack_layout_binding_rejects_shapes():
         w4.repack_layout(w, 1, 1, s, 1, z.t().contiguous(), 1, 32, UINT4)
 
 
+# ------------------------------------------- K not a multiple of 128
+
+
+KTAIL_REPACK = [
+    # (N, K, G, qtype, zero points): the packed layout pads K to a multiple of 128
+    (16, 40, -1, UINT4B8, False),
+    (48, 96, 32, UINT4, True),
+    (32, 2880, 64, UINT4, True),
+    (64, 1216, 64, UINT4B8, False),
+    (256, 200, -1, UINT4, True),
+    (4096, 2880, 32, UINT4, True),
+]
+
+
+@pytest.mark.parametrize("N,K,G,qtype,zp", KTAIL_REPACK, ids=[f"{c[0]}x{c[1]}g{c[2]}q{c[3]}" for c in KTAIL_REPACK])
+def test_repack_k_tail_bit_exact(N, K, G, qtype, zp):
+    case = _case(41, 1, N, K, G, qtype, "bf16", with_zero_point=zp)
+    packed = repack(case)
+    codes, scales, zeros = expected_codes_scales_zeros(case)
+    expect = oracle.encode_device(codes, scales, zeros, qtype, G)
+    got = packed.cpu().numpy()
+    assert got.shape == expect.shape
+    mism = np.flatnonzero(got != expect)
+    assert mism.size == 0, f"{mism.size} bytes differ, first at {mism[:8]}"
+    c2, s2, z2 = w4.unpack(packed, N, K, G, qtype)
+    np.testing.assert_array_equal(c2.cpu().numpy(), codes)
+    np.testing.assert_array_equal(s2.cpu().numpy(), scales.view(torch.int16).numpy())
+    if qtype == UINT4:
+        np.testing.assert_array_equal(z2.cpu().numpy(), zeros)
+
+
+@pytest.mark.parametrize("od,pd", [(1, 1), (1, 0), (0, 0)])
+def test_repack_layout_k_tail_bit_exact(od, pd):
+    N, K, G = 48, 160, 32
+    L = wi.make_layout_weights(42, N, K, G, UINT4, "f16", od, pd, 1, 1)
+    w, s_, z = _layout_dev(L)
+    packed = w4.repack_layout(w, od, pd, s_, 1, z, 1, G, UINT4)
+    codes, scales, zeros = _layout_expect(L)
+    np.testing.assert_array_equal(packed.cpu().numpy(), oracle.encode_device(codes, scales, zeros, UINT4, G))
+
+
+def _nan_padded(A: torch.Tensor, pad: int = 64) -> torch.Tensor:
+    """A as a view with lda = K + pad whose padding columns hold NaN: any
+    read of a column past K would reach C."""
+    M, K = A.shape
+    big = torch.full((M, K + pad), float("nan"), dtype=A.dtype, device=A.device)
+    big[:, :K] = A
+    return big[:, :K]
+
+
+KTAIL_GEMM = [
+    # (M, N, K, G, qtype, dtype, path): every kernel family with K % 128 != 0
+    (1, 256, 2880, 64, UINT4, "bf16", SKINNY),  # few n-tiles: split-K skinny kernel
+    (4, 4096, 1216, 64, UINT4B8, "f16", SKINNY),  # one n-tile per workgroup (resident)
+    (1, 4096, 40, -1, UINT4, "f16", SKINNY),  # a single, mostly padded k-tile
+    (8, 14336, 2880, -1, UINT4B8, "bf16", SKINNY),  # several n-tiles per workgroup (registers)
+    (16, 4096, 14400, 64, UINT4, "f16", SKINNY),  # K > 4096: K chunks meet in the workspace
+    (3, 1024, 2880, 32, UINT4, "bf16", SKINNY),
+    (200, 2880, 2880, 64, UINT4, "f16", MFMA),  # staged kernel (G < 128)
+    (64, 4096, 1216, -1, UINT4B8, "bf16", MFMA),
+    (2048, 4096, 2880, -1, UINT4B8, "bf16", MFMA),  # ring kernel (one group per row)
+    (2048, 4096, 2880, -1, UINT4, "f16", MFMA),
+    (1990, 2880, 1216, 32, UINT4, "bf16", MFMA),
+    (96, 256, 96, 32, UINT4, "f16", MFMA),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,qtype,dtype,path", KTAIL_GEMM,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}g{c[3]}q{c[4]}{c[5]}p{c[6]}" for c in KTAIL_GEMM])
+def test_gemm_k_tail(M, N, K, G, qtype, dtype, path):
+    case = _case(43, M, N, K, G, qtype, dtype, with_bias=True)
+    wq, ws, zp, A, bias = to_dev(case)
+    packed = w4.repack(wq, ws, zp, G, qtype)
+    C = w4.gemm(_nan_padded(A), packed, N, K, G, qtype, bias=bias, path=path)
+    torch.cuda.synchronize()
+    assert not torch.isnan(C).any(), "a column past K reached C"
+    rows = sample_rows(M)
+    err = rel_err_rows(C, oracle_ref(case, rows=rows), rows)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
+    # The same with lda == K (nothing past K exists to read).
+    C2 = w4.gemm(A, packed, N, K, G, qtype, bias=bias, path=path)
+    assert torch.equal(C, C2)
+
+
+@pytest.mark.parametrize("path", [SKINNY, MFMA])
+def test_identity_k_tail(path):
+    # A = I (M = K = 96): C = RN((q - z) * s) bit for bit, through the padded layout.
+    N, K, G = 256, 96, 32
+    for qtype, dtype in [(UINT4, "bf16"), (UINT4B8, "f16")]:
+        case = _case(44, K, N, K, G, qtype, dtype)
+        wq, ws, zp, _, _ = to_dev(case)
+        packed = w4.repack(wq, ws, zp, G, qtype)
+        eye = torch.eye(K, dtype=case.torch_dtype, device=DEV)
+        if path == SKINNY:
+            C = torch.cat([w4.gemm(eye[i:i + 16], packed, N, K, G, qtype, path=SKINNY) for i in range(0, K, 16)])
+        else:
+            C = w4.gemm(eye, packed, N, K, G, qtype, path=MFMA)
+        W = oracle.dequant(case.weight_packed, case.weight_scale, case.weight_zero_point, qtype, G)
+        assert torch.equal(C.cpu(), torch.from_numpy(W.T.copy()).to(case.torch_dtype))
+
+
+def test_dense_variant_k_tail():
+    N, K, G, M = 2880, 2880, 64, 512
+    case = _case(45, M, N, K, G, UINT4, "bf16", with_bias=True)
+    wq, ws, zp, A, bias = to_dev(case)
+    packed = w4.repack(wq, ws, zp, G, UINT4)
+    dense = w4.dequant(packed, N, K, G, UINT4, torch.bfloat16)
+    W = oracle.dequant(case.weight_packed, case.weight_scale, case.weight_zero_point, UINT4, G)
+    assert torch.equal(dense.cpu(), torch.from_numpy(W).to(torch.bfloat16))
+    C = w4.gemm_dense(A, dense, bias=bias)
+    rows = sample_rows(M)
+    assert rel_err_rows(C, oracle_ref(case, rows=rows), rows) <= oracle.TOLERANCE["bf16"]
+
+
 # ------------------------------------------------------------------ dequant
 
 
