@@ -178,36 +178,39 @@ int w4o_gemm(const double *A, int64_t M, int64_t lda, const uint32_t *words, con
 
 /*
  * Device layout ("packed buffer") used by this project's gfx950 kernels.
- * Requires N % 16 == 0, K % 8 == 0, Ge | K with Ge in {32, 64, 128, 256} or
- * Ge == K; Kg = K / Ge groups. K is padded to Kp, the next multiple of 128,
- * and the groups to Kgp = (Kg == 1 ? 1 : Kp / Ge) (Kp = K and Kgp = Kg when
- * K % 128 == 0). All offsets in bytes; words are little-endian uint32.
+ * Requires N % 8 == 0, K % 8 == 0, Ge | K with Ge in {32, 64, 128, 256} or
+ * Ge == K; Kg = K / Ge groups. N is padded to Np, the next multiple of 16,
+ * K to Kp, the next multiple of 128, and the groups to
+ * Kgp = (Kg == 1 ? 1 : Kp / Ge) (Np = N, Kp = K and Kgp = Kg when N % 16 == 0
+ * and K % 128 == 0). All offsets in bytes; words are little-endian uint32.
  *
- *  Q region at 0, N*Kp/2 bytes: 1024-byte tiles, tile (nt, kt) for
- *    nt in [0, N/16), kt in [0, Kp/128) at ((nt * (Kp/128)) + kt) * 1024.
+ *  Q region at 0, Np*Kp/2 bytes: 1024-byte tiles, tile (nt, kt) for
+ *    nt in [0, Np/16), kt in [0, Kp/128) at ((nt * (Kp/128)) + kt) * 1024.
  *    Word 4*l + s of a tile (lane l in [0,64), s in [0,4)) holds the codes of
  *    row n = 16*nt + l%16 at k = 128*kt + 32*s + 8*(l/16) + i, i = 0..7,
- *    code i in bits [4*(i/2) + 16*(i%2), +4); codes at k >= K are 0.
- *  S region at S0 = align256(N*Kp/2): N*Kgp 2-byte scales (the raw fp16/bf16
- *    bits), element (nt, g, r) = scale[16*nt + r][g] at
- *    S0 + ((nt*Kgp + g)*16 + r)*2, and 0 for g >= Kg.
- *  Z region (uint4 only) at Z0 = align256(S0 + N*Kgp*2): N*Kgp bytes, element
- *    (nt, g, r) = zero nibble of (row 16*nt + r, group g) at
- *    Z0 + (nt*Kgp + g)*16 + r, 0 for g >= Kg; all zero when the checkpoint
- *    has no zero points.
+ *    code i in bits [4*(i/2) + 16*(i%2), +4); codes at n >= N or k >= K
+ *    are 0.
+ *  S region at S0 = align256(Np*Kp/2): Np*Kgp 2-byte scales (the raw
+ *    fp16/bf16 bits), element (nt, g, r) = scale[16*nt + r][g] at
+ *    S0 + ((nt*Kgp + g)*16 + r)*2, and 0 for 16*nt + r >= N or g >= Kg.
+ *  Z region (uint4 only) at Z0 = align256(S0 + Np*Kgp*2): Np*Kgp bytes,
+ *    element (nt, g, r) = zero nibble of (row 16*nt + r, group g) at
+ *    Z0 + (nt*Kgp + g)*16 + r, 0 for rows >= N or g >= Kg; all zero when the
+ *    checkpoint has no zero points.
  *  Total size = align256(end of the last region).
  */
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 static int64_t padded_k(int64_t K) { return (K + 127) / 128 * 128; }
+static int64_t padded_n(int64_t N) { return (N + 15) / 16 * 16; }
 static int64_t stored_groups(int64_t K, int64_t G) {
     const int64_t Ge = effective_group(K, G);
     return K / Ge == 1 ? 1 : padded_k(K) / Ge;
 }
 
 int64_t w4o_device_size(int64_t N, int64_t K, int64_t G, int qtype) {
-    const int64_t Kgp = stored_groups(K, G);
-    int64_t end = align256(N * padded_k(K) / 2) + N * Kgp * 2;
-    if (qtype == W4O_UINT4) end = align256(end) + N * Kgp;
+    const int64_t Kgp = stored_groups(K, G), Np = padded_n(N);
+    int64_t end = align256(Np * padded_k(K) / 2) + Np * Kgp * 2;
+    if (qtype == W4O_UINT4) end = align256(end) + Np * Kgp;
     return align256(end);
 }
 
@@ -217,9 +220,9 @@ int64_t w4o_device_size(int64_t N, int64_t K, int64_t G, int qtype) {
 void w4o_encode_device(const uint8_t *codes, const uint16_t *scale_bits, const uint8_t *zeros, int qtype, int64_t N,
                        int64_t K, int64_t G, uint8_t *out) {
     const int64_t Kg = K / effective_group(K, G), Kp = padded_k(K), KT = Kp / 128;
-    const int64_t Kgp = stored_groups(K, G);
+    const int64_t Kgp = stored_groups(K, G), Np = padded_n(N);
     memset(out, 0, (size_t)w4o_device_size(N, K, G, qtype));
-    for (int64_t nt = 0; nt < N / 16; ++nt)
+    for (int64_t nt = 0; nt < Np / 16; ++nt)
         for (int64_t kt = 0; kt < KT; ++kt)
             for (int l = 0; l < 64; ++l)
                 for (int s = 0; s < 4; ++s) {
@@ -227,25 +230,25 @@ void w4o_encode_device(const uint8_t *codes, const uint16_t *scale_bits, const u
                     const int64_t k0 = 128 * kt + 32 * s + 8 * (l / 16);
                     uint32_t w = 0;
                     for (int i = 0; i < 8; ++i)
-                        if (k0 + i < K)
+                        if (n < N && k0 + i < K)
                             w |= (uint32_t)(codes[n * K + k0 + i] & 0xFu) << (4 * (i / 2) + 16 * (i % 2));
                     const int64_t off = (nt * KT + kt) * 1024 + (4 * l + s) * 4;
                     for (int b = 0; b < 4; ++b) out[off + b] = (uint8_t)(w >> (8 * b));
                 }
-    const int64_t S0 = align256(N * Kp / 2);
-    for (int64_t nt = 0; nt < N / 16; ++nt)
+    const int64_t S0 = align256(Np * Kp / 2);
+    for (int64_t nt = 0; nt < Np / 16; ++nt)
         for (int64_t g = 0; g < Kg; ++g)
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16 && 16 * nt + r < N; ++r) {
                 const uint16_t v = scale_bits[(16 * nt + r) * Kg + g];
                 const int64_t off = S0 + ((nt * Kgp + g) * 16 + r) * 2;
                 out[off] = (uint8_t)(v & 0xFF);
                 out[off + 1] = (uint8_t)(v >> 8);
             }
     if (qtype == W4O_UINT4) {
-        const int64_t Z0 = align256(S0 + N * Kgp * 2);
-        for (int64_t nt = 0; nt < N / 16; ++nt)
+        const int64_t Z0 = align256(S0 + Np * Kgp * 2);
+        for (int64_t nt = 0; nt < Np / 16; ++nt)
             for (int64_t g = 0; g < Kg; ++g)
-                for (int r = 0; r < 16; ++r)
+                for (int r = 0; r < 16 && 16 * nt + r < N; ++r)
                     out[Z0 + (nt * Kgp + g) * 16 + r] = zeros ? (uint8_t)(zeros[(16 * nt + r) * Kg + g] & 0xFu) : 0;
     }
 }

@@ -487,6 +487,12 @@ def test_device_size_hand_values(oracle_mod):
     # N=32, K=2880, G=64: Kp=2944, 46 stored groups (45 real): codes 47104
     # (256-aligned), scales 32*46*2 = 2944 -> 50048 -> 50176.
     assert oracle_mod.device_size(32, 2880, 64, UINT4B8) == 50176
+    # N not a multiple of 16 pads N to Np. N=24, K=128, one group: Np=32:
+    # codes 2048; scales 64 -> 2112 -> 2304.
+    assert oracle_mod.device_size(24, 128, 128, UINT4B8) == 2304
+    # N=8, K=40, uint4: Np=16, Kp=128: codes 1024, scales 32 -> 1056; zeros at
+    # 1280, 16 bytes -> 1296 -> 1536.
+    assert oracle_mod.device_size(8, 40, -1, UINT4) == 1536
 
 
 def test_device_encoder_hand_words(oracle_mod):
@@ -543,6 +549,50 @@ def test_device_encoder_padded_k_hand_words(oracle_mod):
     # 1 KB of codes, then the 16 scales (fp16 0.5 = 0x3800) at 1024.
     assert np.all(out[1024:1056].view(np.uint16) == 0x3800)
     assert np.all(out[1056:] == 0)
+
+
+def test_device_encoder_padded_n_hand_words(oracle_mod):
+    # N = 8, K = 128: one tile whose rows 8..15 are padding; c(n, k) = k % 16.
+    N, K = 8, 128
+    codes = np.tile((np.arange(K) % 16).astype(np.uint8), (N, 1))
+    out = oracle_mod.encode_device(codes, torch.full((N, 1), 0.5, dtype=torch.float16), None, UINT4B8, -1)
+    assert len(out) == 1280
+    w = out[:1024].view(np.uint32)
+    assert w[4 * 0 + 0] == 0x75316420  # l=0 (row 0), s=0: k 0..7
+    assert w[4 * 23 + 0] == 0xFDB9ECA8  # l=23 (row 7, k-subblock 1), s=0: k 8..15
+    assert w[4 * 8 + 0] == 0 and w[4 * 31 + 3] == 0 and w[4 * 63 + 2] == 0  # rows 8, 15, 15
+    # scales (nt=0, g=0, r): rows 0..7 hold 0.5 (0x3800), rows 8..15 hold 0
+    sreg = out[1024:1056].view(np.uint16)
+    assert np.all(sreg[:8] == 0x3800) and np.all(sreg[8:] == 0)
+
+
+def test_device_encoder_padded_n_inverse(oracle_mod):
+    # N = 24 (Np = 32), K = 160 (Kp = 256), G = 32 (Kg 5, Kgp 8), uint4.
+    c = wi.make_case(39, 1, 24, 160, 32, UINT4, "bf16")
+    codes = oracle_mod.unpack_codes(c.weight_packed)
+    zeros = oracle_mod.unpack_zeros(c.weight_zero_point, 24)
+    out = oracle_mod.encode_device(codes, c.weight_scale, zeros, UINT4, 32)
+    N, Np, K, Kp, Kg, Kgp, KT = 24, 32, 160, 256, 5, 8, 2
+    words = out[: Np * Kp // 2].view(np.uint32)
+    for n in range(Np):
+        for k in range(0, Kp, 8):
+            nt, r, kt = n // 16, n % 16, k // 128
+            s_, sub = (k % 128) // 32, (k % 32) // 8
+            word = int(words[(nt * KT + kt) * 256 + 4 * (16 * sub + r) + s_])
+            for i in range(8):
+                want = codes[n, k + i] if (n < N and k + i < K) else 0
+                assert (word >> (4 * (i // 2) + 16 * (i % 2))) & 0xF == want
+    S0 = Np * Kp // 2
+    sbits = c.weight_scale.view(torch.int16).numpy().view(np.uint16)
+    sreg = out[S0 : S0 + Np * Kgp * 2].view(np.uint16)
+    Z0 = S0 + ((Np * Kgp * 2 + 255) // 256) * 256
+    for n in range(Np):
+        for g in range(Kgp):
+            idx = ((n // 16) * Kgp + g) * 16 + n % 16
+            real = n < N and g < Kg
+            assert sreg[idx] == (sbits[n, g] if real else 0)
+            assert out[Z0 + idx] == (zeros[n, g] if real else 0)
+    assert len(out) == oracle_mod.device_size(N, K, 32, UINT4)
 
 
 def test_device_encoder_padded_groups_hand_values(oracle_mod):

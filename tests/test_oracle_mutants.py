@@ -59,6 +59,9 @@ MUTANTS = [
     ("encode_scales_unpadded_stride", "const int64_t off = S0 + ((nt * Kgp + g) * 16 + r) * 2;",
      "const int64_t off = S0 + ((nt * Kg + g) * 16 + r) * 2;"),
     ("layout_k_rounded_to_64", "return (K + 127) / 128 * 128;", "return (K + 63) / 64 * 64;"),
+    ("layout_n_rounded_to_8", "return (N + 15) / 16 * 16;", "return (N + 7) / 8 * 8;"),
+    ("encode_scales_of_padding_rows", "for (int r = 0; r < 16 && 16 * nt + r < N; ++r) {",
+     "for (int r = 0; r < 16 && 16 * nt + r < N - 1; ++r) {"),
     ("layout_groups_unpadded", "return K / Ge == 1 ? 1 : padded_k(K) / Ge;", "return K / Ge;"),
     ("encode_zeros_unpadded_stride", "out[Z0 + (nt * Kgp + g) * 16 + r]", "out[Z0 + (nt * Kg + g) * 16 + r]"),
 ]
@@ -85,6 +88,8 @@ PIN_CALLS = [
     (pins.test_device_encoder_padded_k_hand_words, {}),
     (pins.test_device_encoder_padded_groups_hand_values, {}),
     (pins.test_device_encoder_padded_inverse, {}),
+    (pins.test_device_encoder_padded_n_hand_words, {}),
+    (pins.test_device_encoder_padded_n_inverse, {}),
 ]
 
 
