@@ -43,35 +43,39 @@
  *    library never aborts and no exception crosses the ABI.
  *  - qtype is a w4a16_qtype, dtype a w4a16_dtype, path a w4a16_path (passed
  *    as int32_t so the ABI does not depend on enum sizes).
- *  - Shapes: N % 16 == 0, K % 8 == 0 (the checkpoint packs eight codes per
- *    word); group_size in {-1, 32, 64, 128, 256} or group_size == K, with
- *    K % group_size == 0; uint4 zero points also need N % 8 == 0 (implied).
- *    Other shapes return W4A16_ERR_UNSUPPORTED. K need not be a multiple of
- *    128 (the row-parallel shard of a layer often is not): the packed layout
- *    pads it, and the kernels read the activation columns past K as zeros
- *    (never touching them), so A needs only lda >= K.
+ *  - Shapes: N % 8 == 0 (zero points, and AWQ words, pack eight values along
+ *    N), K % 8 == 0 (the checkpoint packs eight codes per word); group_size
+ *    in {-1, 32, 64, 128, 256} or group_size == K, with K % group_size == 0.
+ *    Other shapes return W4A16_ERR_UNSUPPORTED. Neither N need be a multiple
+ *    of 16 nor K of 128 (shards of a layer often are not): the packed layout
+ *    pads both, the kernels read the activation columns past K as zeros
+ *    (never touching them) and store no column of C past N, so A needs only
+ *    lda >= K, C ldc >= N and bias N elements.
  *
  * Device layout of the packed buffer (written by w4a16_repack, read by
- * w4a16_gemm; Ge = K if group_size == -1 else group_size; Kp = K rounded up
- * to a multiple of 128; Kg = 1 if K == Ge, else Kp / Ge stored groups, of
- * which the first K / Ge are the checkpoint's; align256(x) rounds x up to a
- * multiple of 256; words are little-endian):
- *  - Codes at byte 0, N*Kp/2 bytes: 1024-byte tiles; tile (nt, kt), nt in
- *    [0, N/16), kt in [0, Kp/128), starts at ((nt * (Kp/128)) + kt) * 1024.
+ * w4a16_gemm; Ge = K if group_size == -1 else group_size; Np = N rounded up
+ * to a multiple of 16; Kp = K rounded up to a multiple of 128; Kg = 1 if
+ * K == Ge, else Kp / Ge stored groups, of which the first K / Ge are the
+ * checkpoint's; align256(x) rounds x up to a multiple of 256; words are
+ * little-endian):
+ *  - Codes at byte 0, Np*Kp/2 bytes: 1024-byte tiles; tile (nt, kt), nt in
+ *    [0, Np/16), kt in [0, Kp/128), starts at ((nt * (Kp/128)) + kt) * 1024.
  *    32-bit word 4*l + s of a tile (l in [0, 64), s in [0, 4)) holds the codes
  *    of row n = 16*nt + l%16 at k = 128*kt + 32*s + 8*(l/16) + i, i = 0..7,
- *    code i in bits [4*(i/2) + 16*(i%2), +4); codes at k >= K are 0. One
- *    16-byte load per lane of a 64-wide wavefront moves a whole tile, and
- *    word s of lane l is the B operand of a 16x16x32 fp16/bf16 MFMA over k in
- *    [128*kt + 32*s, +32).
- *  - Scales at S0 = align256(N*Kp/2): N*Kg raw 2-byte fp16/bf16 values;
+ *    code i in bits [4*(i/2) + 16*(i%2), +4); codes at n >= N or k >= K are
+ *    0. One 16-byte load per lane of a 64-wide wavefront moves a whole tile,
+ *    and word s of lane l is the B operand of a 16x16x32 fp16/bf16 MFMA over
+ *    k in [128*kt + 32*s, +32).
+ *  - Scales at S0 = align256(Np*Kp/2): Np*Kg raw 2-byte fp16/bf16 values;
  *    element (nt, g, r) = weight_scale[16*nt + r][g] at
- *    S0 + ((nt*Kg + g)*16 + r)*2, and 0 for the groups g >= K / Ge.
- *  - Zeros (uint4 only) at Z0 = align256(S0 + N*Kg*2): N*Kg bytes, element
+ *    S0 + ((nt*Kg + g)*16 + r)*2, and 0 for rows 16*nt + r >= N and for the
+ *    groups g >= K / Ge.
+ *  - Zeros (uint4 only) at Z0 = align256(S0 + Np*Kg*2): Np*Kg bytes, element
  *    (nt, g, r) = zero of (row 16*nt + r, group g) at Z0 + (nt*Kg + g)*16 + r,
- *    0 for g >= K / Ge; all 0 when the checkpoint has no zero points.
+ *    0 for rows >= N and g >= K / Ge; all 0 when the checkpoint has no zero
+ *    points.
  *  - Total size = align256(end of the last region) = w4a16_packed_size().
- *  When K % 128 == 0, Kp = K and Kg = K / Ge.
+ *  When N % 16 == 0 and K % 128 == 0, Np = N, Kp = K and Kg = K / Ge.
  */
 #ifndef W4A16_H
 #define W4A16_H

@@ -28,7 +28,7 @@ template <int DT, int QT>
 __global__ __launch_bounds__(256) void dequant_kernel(const u32x4* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t KTT, int64_t Kg,
-                                                      int gshift, int one_group, int64_t tiles, int64_t K,
+                                                      int gshift, int one_group, int64_t tiles, int64_t N, int64_t K,
                                                       uint16_t* __restrict__ dense, int64_t ldw) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= tiles) return;
@@ -37,6 +37,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const u32x4* __restrict__ 
     const int64_t nt = t / KTT, kt = t - nt * KTT;
     const u32x4 w = __builtin_nontemporal_load(codes + t * 64 + lane);
     const int64_t n = nt * 16 + r;
+    if (n >= N) return;  // padding of N
     uint32_t mask = 0x000F000Fu, magic = kMagic<DT>;
     asm volatile("" : "+v"(mask), "+v"(magic));
 #pragma unroll
@@ -95,16 +96,16 @@ hipError_t launch_dequant(const void* packed, const Geometry& g, int dtype, void
     const uint16_t* scales = reinterpret_cast<const uint16_t*>(base + g.scales_off);
     const uint8_t* zeros = g.qtype == 1 ? base + g.zeros_off : nullptr;
     const int64_t KTT = g.Kp / 128;
-    const int64_t tiles = (g.N / 16) * KTT;
+    const int64_t tiles = (g.Np / 16) * KTT;
     const dim3 grid((unsigned)((tiles + 3) / 4));
     const int one = g.Kg == 1;
     uint16_t* out = static_cast<uint16_t*>(dense);
     if (dtype == 0) {
-        if (g.qtype) hipLaunchKernelGGL((dequant_kernel<0, 1>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.K, out, ldw);
-        else hipLaunchKernelGGL((dequant_kernel<0, 0>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.K, out, ldw);
+        if (g.qtype) hipLaunchKernelGGL((dequant_kernel<0, 1>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.N, g.K, out, ldw);
+        else hipLaunchKernelGGL((dequant_kernel<0, 0>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.N, g.K, out, ldw);
     } else {
-        if (g.qtype) hipLaunchKernelGGL((dequant_kernel<1, 1>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.K, out, ldw);
-        else hipLaunchKernelGGL((dequant_kernel<1, 0>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.K, out, ldw);
+        if (g.qtype) hipLaunchKernelGGL((dequant_kernel<1, 1>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.N, g.K, out, ldw);
+        else hipLaunchKernelGGL((dequant_kernel<1, 0>), grid, dim3(256), 0, stream, codes, scales, zeros, KTT, g.Kg, g.gshift, one, tiles, g.N, g.K, out, ldw);
     }
     return hipGetLastError();
 }

@@ -12,6 +12,7 @@ namespace w4a16 {
 // Geometry of one packed weight (see the layout in include/w4a16.h).
 struct Geometry {
     int64_t N = 0, K = 0;
+    int64_t Np = 0;       // N padded to a multiple of 16 (the packed layout's N)
     int64_t Kp = 0;       // K padded to a multiple of 128 (the packed layout's K)
     int32_t Ge = 0;       // effective group size
     int64_t Kg = 0;       // groups per row stored in the layout (Kp / Ge, or 1)

@@ -38,7 +38,7 @@ struct MfmaArgs {
     const u32x4* codes;
     const uint16_t* scales;
     const uint8_t* zeros;
-    int64_t N;
+    int64_t N;    // N rounded up to 16: the n-tiles of the packed weight
     int64_t KTT;  // padded K / 128
     int64_t K;    // K: activation columns past it read as zero
     int64_t Kg;
@@ -49,6 +49,7 @@ struct MfmaArgs {
     int64_t ldc;
     int64_t m_tiles, n_blocks;
     int64_t tile0;  // mfma_ring_kernel: first 128 x 256 tile (row-major over m-tiles x n-blocks)
+    int64_t Nst;    // columns of C (N above is rounded up to 16); stores and bias stop at Nst
 };
 
 // 16 bytes per lane from buffer `rs` (lane offset voff + scalar offset soff)
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
     for (int j = 0; j < NJ; ++j) {
         if (nt0 + j >= NT) continue;
         const int64_t n = (nt0 + j) * 16 + r;
-        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+        const float bv = a.bias && n < a.Nst ? act_to_float<DT>(a.bias[n]) : 0.f;
         float sf = 1.f, zf = 0.f;
         if (OCM == 1) {  // the row's only scale and zero
             sf = act_to_float<DT>(a.scales[n]);
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
                 const int64_t m = m0 + wm * (BM / WM) + 16 * i + 4 * g4 + jj;
                 float v = acc[i][j][jj];
                 if (OCM == 1) v = sf * __builtin_fmaf(zf, S[OC ? i : 0][jj], v);
-                if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
+                if (m < a.M && n < a.Nst) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
             }
         }
     }
@@ -609,7 +610,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     for (int j = 0; j < NJ; ++j) {
         if (nt_of(j) >= NT) continue;
         const int64_t n = nt_of(j) * 16 + r;
-        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+        const float bv = a.bias && n < a.Nst ? act_to_float<DT>(a.bias[n]) : 0.f;
         float sf = 1.f, zf = 0.f;
         if (OCM == 1) {  // the row's only scale and zero
             sf = act_to_float<DT>(a.scales[n]);
@@ -622,7 +623,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
                 const int64_t m = m0 + wm * (BM / 2) + 16 * i + 4 * g4 + jj;
                 float v = acc[i][j][jj];
                 if (OCM == 1) v = sf * __builtin_fmaf(zf, Sf[i][jj], v);
-                if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
+                if (m < a.M && n < a.Nst) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
             }
         }
     }
@@ -727,7 +728,7 @@ MfmaPlan plan_mfma(int64_t M, const Geometry& g) {
     // otherwise 64-column tiles (four times the workgroups) with as few rows
     // as M needs, so that the weight stream still spreads over the chip at
     // small and medium M.
-    const int64_t wide = ((M + 127) / 128) * ((g.N + 255) / 256);
+    const int64_t wide = ((M + 127) / 128) * ((g.Np + 255) / 256);
     if (wide >= kCUs) {
         p.BM = 128;
         p.BN = 256;
@@ -748,7 +749,8 @@ hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed
     a.codes = reinterpret_cast<const u32x4*>(base);
     a.scales = reinterpret_cast<const uint16_t*>(base + g.scales_off);
     a.zeros = g.qtype == 1 ? base + g.zeros_off : nullptr;
-    a.N = g.N;
+    a.N = g.Np;
+    a.Nst = g.N;
     a.KTT = g.Kp / 128;
     a.K = g.K;
     a.Kg = g.Kg;
@@ -758,7 +760,7 @@ hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed
     a.C = static_cast<uint16_t*>(C);
     a.ldc = ldc;
     a.m_tiles = (M + p.BM - 1) / p.BM;
-    a.n_blocks = (g.N + p.BN - 1) / p.BN;
+    a.n_blocks = (g.Np + p.BN - 1) / p.BN;
     a.tile0 = 0;
     const int spt = g.Kg == 1 ? 1 : (g.Ge >= 128 ? 1 : 128 / g.Ge);
     if (dtype == 0) return g.qtype ? launch_mfma_q<0, 1>(a, p, spt, stream) : launch_mfma_q<0, 0>(a, p, spt, stream);

@@ -56,10 +56,10 @@ __device__ __forceinline__ int64_t word_index(int64_t nw, int64_t kw, int64_t Nw
 // come from nibble n%8 of eight words, one per k.
 template <bool NFIRST, bool KPACKED>
 __global__ __launch_bounds__(256) void repack_codes_kernel(const uint32_t* __restrict__ wq, uint4* __restrict__ out,
-                                                           int64_t N, int64_t K, int64_t Kp) {
+                                                           int64_t N, int64_t Np, int64_t K, int64_t Kp) {
     const int64_t KT = Kp / 128;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (N / 16) * KT * 64;
+    const int64_t total = (Np / 16) * KT * 64;
     if (t >= total) return;
     const int64_t tile = t >> 6;
     const int l = (int)(t & 63);
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void repack_codes_kernel(const uint32_t* __res
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int64_t k0 = k + 32 * s;
-        if (k0 >= K) {  // padding of K up to Kp (K % 8 == 0: all eight or none)
+        if (n >= N || k0 >= K) {  // padding of N up to Np, of K up to Kp (K % 8 == 0)
             w[s] = 0u;
         } else if constexpr (KPACKED) {
             w[s] = gptq_to_pair_order(wq[word_index<NFIRST>(n, k0 / 8, N, K / 8)]);
@@ -90,20 +90,21 @@ __global__ __launch_bounds__(256) void repack_codes_kernel(const uint32_t* __res
 
 // One thread per (row, group): scales to [N/16][Kg][16], zeros likewise.
 // Kg stored groups per row; the checkpoint holds Kg_ck <= Kg of them, and
-// the rest (groups of the padding of K) get scale 0 and zero 0.
+// the rest (groups of the padding of K), like the rows of the padding of N,
+// get scale 0 and zero 0.
 template <bool SNFIRST, bool ZNFIRST>
 __global__ __launch_bounds__(256) void repack_scales_kernel(const uint16_t* __restrict__ ws,
                                                             const uint32_t* __restrict__ wzp,
                                                             uint16_t* __restrict__ s_out, uint8_t* __restrict__ z_out,
-                                                            int64_t N, int64_t Kg, int64_t Kg_ck) {
+                                                            int64_t N, int64_t Np, int64_t Kg, int64_t Kg_ck) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= N * Kg) return;
+    if (t >= Np * Kg) return;
     // t enumerates the destination order so the stores are contiguous.
     const int r = (int)(t & 15);
     const int64_t ng = t >> 4;  // nt * Kg + g
     const int64_t nt = ng / Kg, g = ng - nt * Kg;
     const int64_t n = 16 * nt + r;
-    const bool real = g < Kg_ck;
+    const bool real = n < N && g < Kg_ck;
     s_out[t] = real ? ws[SNFIRST ? n * Kg_ck + g : g * N + n] : (uint16_t)0;
     if (z_out != nullptr) {
         uint8_t z = 0;
@@ -114,15 +115,16 @@ __global__ __launch_bounds__(256) void repack_scales_kernel(const uint16_t* __re
 }
 
 __global__ __launch_bounds__(256) void unpack_codes_kernel(const uint4* __restrict__ in, uint8_t* __restrict__ codes,
-                                                           int64_t N, int64_t K, int64_t Kp) {
+                                                           int64_t N, int64_t Np, int64_t K, int64_t Kp) {
     const int64_t KT = Kp / 128;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (N / 16) * KT * 64;
+    const int64_t total = (Np / 16) * KT * 64;
     if (t >= total) return;
     const int64_t tile = t >> 6;
     const int l = (int)(t & 63);
     const int64_t nt = tile / KT, kt = tile - nt * KT;
     const int64_t n = 16 * nt + (l & 15);
+    if (n >= N) return;  // padding of N
     const uint4 v = in[t];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -139,14 +141,14 @@ __global__ __launch_bounds__(256) void unpack_codes_kernel(const uint4* __restri
 __global__ __launch_bounds__(256) void unpack_scales_kernel(const uint16_t* __restrict__ s_in,
                                                             const uint8_t* __restrict__ z_in,
                                                             uint16_t* __restrict__ s_out, uint8_t* __restrict__ z_out,
-                                                            int64_t N, int64_t Kg, int64_t Kg_ck) {
+                                                            int64_t N, int64_t Np, int64_t Kg, int64_t Kg_ck) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= N * Kg) return;
+    if (t >= Np * Kg) return;
     const int r = (int)(t & 15);
     const int64_t ng = t >> 4;
     const int64_t nt = ng / Kg, g = ng - nt * Kg;
-    if (g >= Kg_ck) return;  // a group of the padding of K
     const int64_t n = 16 * nt + r;
+    if (n >= N || g >= Kg_ck) return;  // padding of N or of K
     if (s_out != nullptr) s_out[n * Kg_ck + g] = s_in[t];
     if (z_out != nullptr && z_in != nullptr) z_out[n * Kg_ck + g] = z_in[t];
 }
@@ -165,32 +167,32 @@ inline unsigned blocks_for(int64_t threads, int per_block) { return (unsigned)((
 hipError_t launch_repack(const int32_t* wq, const uint16_t* ws, const int32_t* wzp, const CheckpointLayout& lay,
                          const Geometry& g, void* packed, hipStream_t stream) {
     uint8_t* base = static_cast<uint8_t*>(packed);
-    const int64_t code_threads = (g.N / 16) * (g.Kp / 128) * 64;
+    const int64_t code_threads = (g.Np / 16) * (g.Kp / 128) * 64;
     const dim3 cgrid(blocks_for(code_threads, 256));
     const uint32_t* src = reinterpret_cast<const uint32_t*>(wq);
     uint4* dst = reinterpret_cast<uint4*>(base);
     if (lay.weight_n_first && lay.weight_k_packed)
-        hipLaunchKernelGGL((repack_codes_kernel<true, true>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.K, g.Kp);
+        hipLaunchKernelGGL((repack_codes_kernel<true, true>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.Np, g.K, g.Kp);
     else if (lay.weight_n_first)
-        hipLaunchKernelGGL((repack_codes_kernel<true, false>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.K, g.Kp);
+        hipLaunchKernelGGL((repack_codes_kernel<true, false>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.Np, g.K, g.Kp);
     else if (lay.weight_k_packed)
-        hipLaunchKernelGGL((repack_codes_kernel<false, true>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.K, g.Kp);
+        hipLaunchKernelGGL((repack_codes_kernel<false, true>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.Np, g.K, g.Kp);
     else
-        hipLaunchKernelGGL((repack_codes_kernel<false, false>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.K, g.Kp);
+        hipLaunchKernelGGL((repack_codes_kernel<false, false>), cgrid, dim3(256), 0, stream, src, dst, g.N, g.Np, g.K, g.Kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     uint8_t* z_out = g.qtype == 1 ? base + g.zeros_off : nullptr;
     const uint32_t* zp = g.qtype == 1 ? reinterpret_cast<const uint32_t*>(wzp) : nullptr;
     uint16_t* s_out = reinterpret_cast<uint16_t*>(base + g.scales_off);
-    const dim3 sgrid(blocks_for(g.N * g.Kg, 256));
+    const dim3 sgrid(blocks_for(g.Np * g.Kg, 256));
     if (lay.scale_n_first && lay.zero_n_first)
-        hipLaunchKernelGGL((repack_scales_kernel<true, true>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Kg, g.Kg_ck);
+        hipLaunchKernelGGL((repack_scales_kernel<true, true>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Np, g.Kg, g.Kg_ck);
     else if (lay.scale_n_first)
-        hipLaunchKernelGGL((repack_scales_kernel<true, false>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Kg, g.Kg_ck);
+        hipLaunchKernelGGL((repack_scales_kernel<true, false>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Np, g.Kg, g.Kg_ck);
     else if (lay.zero_n_first)
-        hipLaunchKernelGGL((repack_scales_kernel<false, true>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Kg, g.Kg_ck);
+        hipLaunchKernelGGL((repack_scales_kernel<false, true>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Np, g.Kg, g.Kg_ck);
     else
-        hipLaunchKernelGGL((repack_scales_kernel<false, false>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Kg, g.Kg_ck);
+        hipLaunchKernelGGL((repack_scales_kernel<false, false>), sgrid, dim3(256), 0, stream, ws, zp, s_out, z_out, g.N, g.Np, g.Kg, g.Kg_ck);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Padding bytes between and after the regions are part of the contract
@@ -198,8 +200,8 @@ hipError_t launch_repack(const int32_t* wq, const uint16_t* ws, const int32_t* w
     // gap is shorter than 256 bytes (alignment padding only).
     const size_t gaps[3][2] = {
         {g.codes_bytes, g.scales_off},
-        {g.scales_off + (size_t)(g.N * g.Kg * 2), g.qtype == 1 ? g.zeros_off : g.total_bytes},
-        {g.qtype == 1 ? g.zeros_off + (size_t)(g.N * g.Kg) : g.total_bytes, g.total_bytes},
+        {g.scales_off + (size_t)(g.Np * g.Kg * 2), g.qtype == 1 ? g.zeros_off : g.total_bytes},
+        {g.qtype == 1 ? g.zeros_off + (size_t)(g.Np * g.Kg) : g.total_bytes, g.total_bytes},
     };
     for (auto& gap : gaps) {
         if (gap[1] > gap[0]) {
@@ -215,17 +217,17 @@ hipError_t launch_unpack(const void* packed, const Geometry& g, uint8_t* codes, 
                          hipStream_t stream) {
     const uint8_t* base = static_cast<const uint8_t*>(packed);
     if (codes != nullptr) {
-        const int64_t code_threads = (g.N / 16) * (g.Kp / 128) * 64;
+        const int64_t code_threads = (g.Np / 16) * (g.Kp / 128) * 64;
         hipLaunchKernelGGL(unpack_codes_kernel, dim3(blocks_for(code_threads, 256)), dim3(256), 0, stream,
-                           reinterpret_cast<const uint4*>(base), codes, g.N, g.K, g.Kp);
+                           reinterpret_cast<const uint4*>(base), codes, g.N, g.Np, g.K, g.Kp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     uint8_t* z_out = g.qtype == 1 ? zeros : nullptr;
     if (scale_bits != nullptr || z_out != nullptr) {
-        hipLaunchKernelGGL(unpack_scales_kernel, dim3(blocks_for(g.N * g.Kg, 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(unpack_scales_kernel, dim3(blocks_for(g.Np * g.Kg, 256)), dim3(256), 0, stream,
                            reinterpret_cast<const uint16_t*>(base + g.scales_off),
-                           g.qtype == 1 ? base + g.zeros_off : nullptr, scale_bits, z_out, g.N, g.Kg, g.Kg_ck);
+                           g.qtype == 1 ? base + g.zeros_off : nullptr, scale_bits, z_out, g.N, g.Np, g.Kg, g.Kg_ck);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

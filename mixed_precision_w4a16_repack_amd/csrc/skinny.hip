@@ -41,7 +41,7 @@ struct SkinnyArgs {
     const u32x4* codes;
     const uint16_t* scales;
     const uint8_t* zeros;
-    int64_t NT;   // N / 16
+    int64_t NT;   // n-tiles: N rounded up to 16, / 16
     int64_t KTT;  // padded K / 128
     int64_t Kg;
     int gshift;
@@ -60,6 +60,7 @@ struct SkinnyArgs {
     int nn_max;            // full-K variants: n-tiles per workgroup, at most
     uint32_t codes_bytes, scales_bytes, zeros_bytes;  // region sizes (< 2^31 on the full-K paths)
     int64_t K;    // activation columns past K read as zero (split kernel; the full-K paths need K % 128 == 0)
+    int64_t N;    // columns of C (NT covers N rounded up to 16); the split kernel's stores and bias stop at N
 };
 
 // Cross-workgroup exchange of split-K partial sums. Every access carries the
@@ -195,11 +196,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
         for (int i = 0; i < NW; ++i) {
             if (nt[i] >= a.NT) continue;
             const int64_t n = nt[i] * 16 + r;
-            const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+            const float bv = a.bias && n < a.N ? act_to_float<DT>(a.bias[n]) : 0.f;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int m = 4 * g4 + jj;
-                if (m < a.M) a.C[(int64_t)m * a.ldc + n] = to_act_bits<DT>(acc[i][jj] + bv);
+                if (m < a.M && n < a.N) a.C[(int64_t)m * a.ldc + n] = to_act_bits<DT>(acc[i][jj] + bv);
             }
         }
         return;
@@ -260,11 +261,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
             for (int g = 1; g < G; ++g) tot += red[g * (256 / G) + t];
             const int64_t n = ng * W + col;
             if (n < a.NT * 16) {
-                const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+                const float bv = a.bias && n < a.N ? act_to_float<DT>(a.bias[n]) : 0.f;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int m = 4 * qd + jj;
-                    if (m < a.M) a.C[(int64_t)m * a.ldc + n] = to_act_bits<DT>(tot[jj] + bv);
+                    if (m < a.M && n < a.N) a.C[(int64_t)m * a.ldc + n] = to_act_bits<DT>(tot[jj] + bv);
                 }
             }
         }
@@ -332,8 +333,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // Activation rows [0, M) of one launch; a_bytes = ((M-1)*lda + K)*2 < 2^31.
-// The full-K variants that use it run only with K % 128 == 0 (the planner
-// sends other K to the split kernel), so every k-tile is whole.
+// The full-K variants that use it run only with K % 128 == 0 and
+// N % 16 == 0 (the planner sends other shapes to the split kernel), so every
+// k-tile and n-tile is whole.
 struct ActRows {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t lane_off;  // byte offset of this lane's row and 8-element slice
@@ -892,13 +894,14 @@ void launch_skinny_q(const SkinnyArgs& a, const SkinnyPlan& p, int spt, dim3 gri
 
 SkinnyPlan plan_skinny(int64_t M, const Geometry& g) {
     SkinnyPlan p;  // the workspace is sized for 16 rows, so one serves every M <= 16
-    const int64_t NT = g.N / 16, KTT = g.Kp / 128;
+    const int64_t NT = g.Np / 16, KTT = g.Kp / 128;
     // The wide-weight variants address each region of the packed weight with
     // 32-bit offsets below 2^31 (codes N*K/2 bytes, the largest).
-    // The wide-weight variants read whole k-tiles of A: K % 128 == 0 only.
-    // A K that is not (the layout pads it) goes to the split kernel below,
-    // whose activation loads stop at K.
-    if (NT >= kFullKMinTiles && g.codes_bytes < ((size_t)1 << 31) && g.K % 128 == 0) {
+    // The wide-weight variants read whole k-tiles of A and store whole
+    // n-tiles of C: K % 128 == 0 and N % 16 == 0 only. Other shapes (the
+    // layout pads them) go to the split kernel below, whose activation loads
+    // stop at K and whose stores stop at N.
+    if (NT >= kFullKMinTiles && g.codes_bytes < ((size_t)1 << 31) && g.K % 128 == 0 && g.N % 16 == 0) {
         // Wide weights: one workgroup per CU while N allows, n-tiles spread
         // evenly.
         p.full_k = true;
@@ -974,7 +977,8 @@ hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* pack
     a.codes = reinterpret_cast<const u32x4*>(base);
     a.scales = reinterpret_cast<const uint16_t*>(base + g.scales_off);
     a.zeros = g.qtype == 1 ? base + g.zeros_off : nullptr;
-    a.NT = g.N / 16;
+    a.NT = g.Np / 16;
+    a.N = g.N;
     a.KTT = g.Kp / 128;
     a.K = g.K;
     a.Kg = g.Kg;
@@ -993,8 +997,8 @@ hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* pack
     a.kc_tiles = p.kc_tiles;
     a.nn_max = p.nn_max;
     a.codes_bytes = (uint32_t)g.codes_bytes;  // the full-K paths need all three < 2^31
-    a.scales_bytes = (uint32_t)(g.N * g.Kg * 2);
-    a.zeros_bytes = g.qtype == 1 ? (uint32_t)(g.N * g.Kg) : 0u;
+    a.scales_bytes = (uint32_t)(g.Np * g.Kg * 2);
+    a.zeros_bytes = g.qtype == 1 ? (uint32_t)(g.Np * g.Kg) : 0u;
     a.mask = 0x000F000Fu;
     a.magic = dtype == 0 ? 0x64006400u : 0x43004300u;
     const int spt = g.Kg == 1 ? 1 : (g.Ge >= 128 ? 1 : 128 / g.Ge);

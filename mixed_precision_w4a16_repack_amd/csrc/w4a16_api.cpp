@@ -48,7 +48,7 @@ w4a16_status make_geometry(int64_t N, int64_t K, int32_t group_size, int32_t qty
     if (N <= 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "N=%lld and K=%lld must be positive", (long long)N, (long long)K);
     if (qtype != W4A16_UINT4B8 && qtype != W4A16_UINT4)
         return fail(W4A16_ERR_INVALID_ARG, "qtype=%d is not a w4a16_qtype (0 uint4b8, 1 uint4)", qtype);
-    if (N % 16 != 0) return fail(W4A16_ERR_UNSUPPORTED, "N=%lld must be divisible by 16", (long long)N);
+    if (N % 8 != 0) return fail(W4A16_ERR_UNSUPPORTED, "N=%lld must be divisible by 8", (long long)N);
     if (K % 8 != 0) return fail(W4A16_ERR_UNSUPPORTED, "K=%lld must be divisible by 8", (long long)K);
     const int64_t Ge = group_size == -1 ? K : group_size;
     const bool listed = group_size == -1 || group_size == 32 || group_size == 64 || group_size == 128 ||
@@ -59,6 +59,7 @@ w4a16_status make_geometry(int64_t N, int64_t K, int32_t group_size, int32_t qty
     if (K % Ge != 0)
         return fail(W4A16_ERR_UNSUPPORTED, "K=%lld must be divisible by group_size=%d", (long long)K, group_size);
     g->N = N;
+    g->Np = (N + 15) / 16 * 16;
     g->K = K;
     g->Kp = (K + 127) / 128 * 128;
     g->Ge = (int32_t)Ge;
@@ -69,12 +70,12 @@ w4a16_status make_geometry(int64_t N, int64_t K, int32_t group_size, int32_t qty
     g->Kg = g->Kg_ck == 1 ? 1 : g->Kp / Ge;
     g->gshift = g->Kg > 1 ? ilog2(Ge) : 0;
     g->qtype = qtype;
-    g->codes_bytes = (size_t)N * (size_t)g->Kp / 2;
+    g->codes_bytes = (size_t)g->Np * (size_t)g->Kp / 2;
     g->scales_off = align256(g->codes_bytes);
-    size_t end = g->scales_off + (size_t)N * (size_t)g->Kg * 2;
+    size_t end = g->scales_off + (size_t)g->Np * (size_t)g->Kg * 2;
     if (qtype == W4A16_UINT4) {
         g->zeros_off = align256(end);
-        end = g->zeros_off + (size_t)N * (size_t)g->Kg;
+        end = g->zeros_off + (size_t)g->Np * (size_t)g->Kg;
     } else {
         g->zeros_off = 0;
     }

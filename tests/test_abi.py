@@ -61,7 +61,8 @@ def test_packed_size_values(lib):
 
 
 @pytest.mark.parametrize("N,K,G,qtype", [(16, 40, -1, 0), (48, 96, 32, 1), (32, 2880, 64, 0), (4096, 1216, 64, 1),
-                                          (256, 200, -1, 1), (4096, 14344, -1, 0)])
+                                          (256, 200, -1, 1), (4096, 14344, -1, 0), (24, 128, 128, 0),
+                                          (8, 40, -1, 1), (1224, 2880, 64, 1)])
 def test_packed_size_padded_k_matches_oracle(N, K, G, qtype):
     import oracle
 
@@ -71,7 +72,7 @@ def test_packed_size_padded_k_matches_oracle(N, K, G, qtype):
 @pytest.mark.parametrize(
     "N,K,G,qtype,status,needle",
     [
-        (4100, 4096, 128, 0, UNSUPPORTED, "N=4100 must be divisible by 16"),
+        (4100, 4096, 128, 0, UNSUPPORTED, "N=4100 must be divisible by 8"),
         (4096, 4100, 128, 0, UNSUPPORTED, "K=4100 must be divisible by 8"),
         (4096, 4000, 128, 0, UNSUPPORTED, "K=4000 must be divisible by group_size=128"),
         (4096, 4096, 96, 0, UNSUPPORTED, "group_size=96 not supported"),
@@ -166,7 +167,7 @@ def test_repack_layout_rejects_like_repack(lib):
             assert lib.w4a16_repack_layout(None, od, pd, p, 1, None, 1, 16, 128, 128, 0, p, 1 << 20, None) == INVALID
             assert "weight_packed is NULL" in w4.last_error()
             assert lib.w4a16_repack_layout(p, od, pd, p, 1, None, 1, 16, 128, 128, 0, p, 1000, None) == SIZE
-            assert lib.w4a16_repack_layout(p, od, pd, p, 1, None, 1, 24, 128, 128, 0, p, 1 << 20, None) == UNSUPPORTED
+            assert lib.w4a16_repack_layout(p, od, pd, p, 1, None, 1, 20, 128, 128, 0, p, 1 << 20, None) == UNSUPPORTED
 
 
 def test_select_path(lib):

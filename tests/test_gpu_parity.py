@@ -295,6 +295,105 @@ def test_dense_variant_k_tail():
     assert rel_err_rows(C, oracle_ref(case, rows=rows), rows) <= oracle.TOLERANCE["bf16"]
 
 
+# ------------------------------------------- N not a multiple of 16
+
+
+NTAIL_REPACK = [
+    # (N, K, G, qtype, zero points): the packed layout pads N to a multiple of 16
+    (24, 128, 128, UINT4B8, False),
+    (8, 40, -1, UINT4, True),
+    (1224, 2880, 64, UINT4, True),
+    (4104, 4096, 128, UINT4B8, False),
+]
+
+
+@pytest.mark.parametrize("N,K,G,qtype,zp", NTAIL_REPACK, ids=[f"{c[0]}x{c[1]}g{c[2]}q{c[3]}" for c in NTAIL_REPACK])
+def test_repack_n_tail_bit_exact(N, K, G, qtype, zp):
+    case = _case(46, 1, N, K, G, qtype, "f16", with_zero_point=zp)
+    packed = repack(case)
+    codes, scales, zeros = expected_codes_scales_zeros(case)
+    expect = oracle.encode_device(codes, scales, zeros, qtype, G)
+    got = packed.cpu().numpy()
+    assert got.shape == expect.shape
+    mism = np.flatnonzero(got != expect)
+    assert mism.size == 0, f"{mism.size} bytes differ, first at {mism[:8]}"
+    c2, s2, z2 = w4.unpack(packed, N, K, G, qtype)
+    np.testing.assert_array_equal(c2.cpu().numpy(), codes)
+    np.testing.assert_array_equal(s2.cpu().numpy(), scales.view(torch.int16).numpy())
+    if qtype == UINT4:
+        np.testing.assert_array_equal(z2.cpu().numpy(), zeros)
+
+
+def test_repack_layout_n_tail_bit_exact():
+    N, K, G = 40, 160, 32  # AWQ words (K, N/8 = 5), AutoGPTQ zero points (K/G, 5)
+    L = wi.make_layout_weights(47, N, K, G, UINT4, "bf16", 1, 1, 1, 1)
+    w, s_, z = _layout_dev(L)
+    packed = w4.repack_layout(w, 1, 1, s_, 1, z, 1, G, UINT4)
+    codes, scales, zeros = _layout_expect(L)
+    np.testing.assert_array_equal(packed.cpu().numpy(), oracle.encode_device(codes, scales, zeros, UINT4, G))
+
+
+NTAIL_GEMM = [
+    # (M, N, K, G, qtype, dtype, path): every kernel family with N % 16 != 0
+    (1, 24, 512, 128, UINT4B8, "f16", SKINNY),  # split kernel, one n-tile
+    (8, 4104, 4096, 128, UINT4, "bf16", SKINNY),  # wide N: still the split kernel (N tail)
+    (4, 4104, 4096, -1, UINT4B8, "f16", SKINNY),
+    (16, 1224, 2880, 64, UINT4, "bf16", SKINNY),  # N and K tails together
+    (2048, 4104, 4096, -1, UINT4B8, "bf16", MFMA),  # ring kernel, one group per row
+    (2048, 14344, 4096, 256, UINT4, "bf16", MFMA),  # ring kernel, groups of 256
+    (200, 1224, 1216, 64, UINT4, "f16", MFMA),  # staged kernel with both tails
+    (64, 4104, 4096, 32, UINT4B8, "f16", MFMA),  # staged kernel
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,qtype,dtype,path", NTAIL_GEMM,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}g{c[3]}q{c[4]}{c[5]}p{c[6]}" for c in NTAIL_GEMM])
+def test_gemm_n_tail(M, N, K, G, qtype, dtype, path):
+    case = _case(48, M, N, K, G, qtype, dtype, with_bias=True)
+    wq, ws, zp, A, bias = to_dev(case)
+    packed = w4.repack(wq, ws, zp, G, qtype)
+    # C as a view of a wider buffer whose extra columns hold a sentinel: no
+    # store may land past column N.
+    sentinel = 1234.0
+    big = torch.full((M, N + 24), sentinel, dtype=case.torch_dtype, device=DEV)
+    C = w4.gemm(_nan_padded(A) if K % 128 else A, packed, N, K, G, qtype, bias=bias, out=big[:, :N], path=path)
+    torch.cuda.synchronize()
+    assert torch.all(big[:, N:] == sentinel), "a store landed past column N"
+    rows = sample_rows(M)
+    err = rel_err_rows(C, oracle_ref(case, rows=rows), rows)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
+
+
+def test_identity_n_tail():
+    N, K, G = 24, 128, 32
+    for path in (SKINNY, MFMA):
+        case = _case(49, K, N, K, G, UINT4, "bf16")
+        wq, ws, zp, _, _ = to_dev(case)
+        packed = w4.repack(wq, ws, zp, G, UINT4)
+        eye = torch.eye(K, dtype=torch.bfloat16, device=DEV)
+        if path == SKINNY:
+            C = torch.cat([w4.gemm(eye[i:i + 16], packed, N, K, G, UINT4, path=SKINNY) for i in range(0, K, 16)])
+        else:
+            C = w4.gemm(eye, packed, N, K, G, UINT4, path=MFMA)
+        W = oracle.dequant(case.weight_packed, case.weight_scale, case.weight_zero_point, UINT4, G)
+        assert torch.equal(C.cpu(), torch.from_numpy(W.T.copy()).to(torch.bfloat16))
+
+
+def test_dense_variant_n_tail():
+    N, K, G, M = 1224, 2880, 64, 300
+    case = _case(50, M, N, K, G, UINT4B8, "f16", with_bias=True)
+    wq, ws, _, A, bias = to_dev(case)
+    packed = w4.repack(wq, ws, None, G, UINT4B8)
+    big = torch.full((N + 8, K), 7.0, dtype=torch.float16, device=DEV)
+    dense = w4.dequant(packed, N, K, G, UINT4B8, torch.float16, out=big[:N])
+    assert torch.all(big[N:] == 7.0)
+    W = oracle.dequant(case.weight_packed, case.weight_scale, None, UINT4B8, G)
+    assert torch.equal(dense.cpu(), torch.from_numpy(W).to(torch.float16))
+    C = w4.gemm_dense(A, dense, bias=bias)
+    rows = sample_rows(M)
+    assert rel_err_rows(C, oracle_ref(case, rows=rows), rows) <= oracle.TOLERANCE["f16"]
+
+
 # ------------------------------------------------------------------ dequant
 
 
