@@ -44,7 +44,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC]
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -64,6 +64,8 @@ def _open(path: str):
     lib.w4o_device_size.restype = i64
     lib.w4o_encode_device.argtypes = [p, p, p, i32, i64, i64, i64, p]
     lib.w4o_max_threads.restype = i32
+    lib.w4o_quant_rows_a8.argtypes = [p, i64, i64, p, p]
+    lib.w4o_gemm_w4a8.argtypes = [p, p, i64, i64, p, p, i64, i64, p, p]
     return lib
 
 
@@ -254,6 +256,33 @@ def gemm(A, words, scales, zp_words, qtype: int, G: int, bias=None, rows=None, n
     if used < 0:
         raise MemoryError("oracle could not allocate a row buffer")
     return C, int(used)
+
+
+def quant_rows_a8(A):
+    """Per-token symmetric int8 quantisation of A [M, K] (fp16/bf16/fp32
+    values) -> (q int8 [M, K], xs float32 [M]); see the C file for the rule."""
+    a = _f64(A)
+    M, K = a.shape
+    q = np.empty((M, K), dtype=np.int8)
+    xs = np.empty((M,), dtype=np.float32)
+    _load().w4o_quant_rows_a8(_ptr(a), M, K, _ptr(q), _ptr(xs))
+    return q, xs
+
+
+def gemm_w4a8(q, xs, words, scales, G: int, bias=None) -> np.ndarray:
+    """fp64 C[M, N] = xs[m] * sum_g s[n,g] * sum_{k in g} q[m,k] * (code[n,k] - 8) (+ bias)."""
+    qq = np.ascontiguousarray(np.asarray(q, dtype=np.int8))
+    x = np.ascontiguousarray(np.asarray(xs, dtype=np.float32))
+    w = _words(words)
+    s = _f64(scales)
+    M, K = qq.shape
+    N = w.shape[0]
+    if w.shape[1] * 8 != K or x.shape != (M,) or s.shape[0] != N:
+        raise ValueError("shape mismatch")
+    b = None if bias is None else _f64(bias)
+    C = np.empty((M, N), dtype=np.float64)
+    _load().w4o_gemm_w4a8(_ptr(qq), _ptr(x), M, K, _ptr(w), _ptr(s), N, G, _ptr(b), _ptr(C))
+    return C
 
 
 def device_size(N: int, K: int, G: int, qtype: int) -> int:

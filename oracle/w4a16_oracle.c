@@ -32,12 +32,15 @@
  *      the view [N, K/G, G]; w = (q - zp) * scale.
  *  [PKG-58588] "mixed_precision" package page (vLLM docs, build 58588),
  *      zentorch W4A16 section -- an [N, K/8] int32 tensor is the same memory as
- *      [N, K/2] bytes in little-endian order (used by the tests as a pin).
+ *      [N, K/2] bytes in little-endian order (used by the tests as a pin);
+ *      XPUW4A8IntLinearKernel -- symmetric int4 weights, activations
+ *      quantised per token to symmetric int8 (the W4A8 functions at the end).
  *
  * The device-layout encoder at the end follows the layout this project
  * defines for its gfx950 kernels (the specification is restated beside the
  * function); it is written from that specification, not from the kernels.
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -250,5 +253,63 @@ void w4o_encode_device(const uint8_t *codes, const uint16_t *scale_bits, const u
             for (int64_t g = 0; g < Kg; ++g)
                 for (int r = 0; r < 16 && 16 * nt + r < N; ++r)
                     out[Z0 + (nt * Kgp + g) * 16 + r] = zeros ? (uint8_t)(zeros[(16 * nt + r) * Kg + g] & 0xFu) : 0;
+    }
+}
+
+/*
+ * W4A8: activations quantised per token to symmetric int8, weights
+ * symmetric int4 ("mixed_precision" package page, XPUW4A8IntLinearKernel:
+ * its class docstring and `apply_weights`, which quantises each row of x
+ * dynamically to symmetric int8 and multiplies the int8 rows by the int4
+ * weights with the row scale and the group scales). The pages do not print
+ * the quantiser; the reading taken (stated where the project documents its
+ * readings): the row scale is fp32(max |x|) / 127 in fp32 with IEEE
+ * division, each value is rint(fp32(x) / scale) (round half to even)
+ * clamped to [-127, 127], and a row of zeros has scale 0 and codes 0.
+ */
+void w4o_quant_rows_a8(const double *A, int64_t M, int64_t K, int8_t *q, float *xs) {
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = fabsf((float)A[m * K + k]);
+            if (v > amax) amax = v;
+        }
+        const float s = amax / 127.0f;
+        xs[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            int v = 0;
+            if (amax > 0.0f) {
+                const float t = rintf((float)A[m * K + k] / s);
+                /* |x / s| is within a few ulps of 127 at most, so the clamp
+                 * never binds; it is kept as the rule's statement. */
+                v = t > 127.0f ? 127 : (t < -127.0f ? -127 : (int)t);
+            }
+            q[m * K + k] = (int8_t)v;
+        }
+    }
+}
+
+/* C[m, n] = xs[m] * sum_g s[n, g] * sum_{k in g} q[m, k] * (code[n, k] - 8)
+ * (+ bias[n]), in fp64: the integer sums are exact, and so is their product
+ * with an fp32 row scale and an fp16/bf16 group scale. */
+void w4o_gemm_w4a8(const int8_t *q, const float *xs, int64_t M, int64_t K, const uint32_t *words, const double *scales,
+                   int64_t N, int64_t G, const double *bias, double *C) {
+    const int64_t Ge = effective_group(K, G), Kg = K / Ge, K8 = K / 8;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < Kg; ++g) {
+                int64_t isum = 0;
+                for (int64_t k = g * Ge; k < (g + 1) * Ge; ++k) {
+                    const int code = (int)((words[n * K8 + k / 8] >> (4 * (k % 8))) & 0xFu);
+                    isum += (int64_t)q[m * K + k] * (code - 8);
+                }
+                acc += scales[n * Kg + g] * (double)isum;
+            }
+            acc *= (double)xs[m];
+            if (bias) acc += bias[n];
+            C[n + m * N] = acc;
+        }
     }
 }

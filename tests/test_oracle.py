@@ -666,3 +666,81 @@ def test_device_encoder_inverse(oracle_mod):
         for g in range(Kg):
             assert sreg[((n // 16) * Kg + g) * 16 + n % 16] == sbits[n, g]
             assert out[Z0 + ((n // 16) * Kg + g) * 16 + n % 16] == zeros[n, g]
+
+
+# ---------------------------------------------------------------- W4A8
+
+
+def test_quant_a8_hand_values(oracle_mod):
+    # Row 0: max |x| = 127, so the scale is exactly 1 and q = rint(x) (half to
+    # even: 2.5 -> 2); fp16 0.4 is 0.39990234375 -> 0, fp16 -0.6 -> -1.
+    # Row 1: max |x| = 254, scale 2: 3/2 = 1.5 -> 2, 5/2 = 2.5 -> 2, 1/2 -> 0.
+    # Row 2: all zero: scale 0, codes 0.
+    A = torch.tensor([[127.0, -63.0, 1.0, 0.4, -0.6, 2.5, 0.0, 0.0],
+                      [3.0, 5.0, -254.0, 1.0, 0.0, 0.0, 0.0, 0.0],
+                      [0.0] * 8], dtype=torch.float16)
+    q, xs = oracle_mod.quant_rows_a8(A)
+    assert q.tolist() == [[127, -63, 1, 0, -1, 2, 0, 0], [2, 2, -127, 0, 0, 0, 0, 0], [0] * 8]
+    assert xs.tolist() == [1.0, 2.0, 0.0]
+
+
+def test_quant_a8_properties(oracle_mod):
+    rng = np.random.default_rng(31)
+    A = torch.from_numpy(rng.normal(0, 3, size=(40, 96))).to(torch.bfloat16)
+    q, xs = oracle_mod.quant_rows_a8(A)
+    a = A.to(torch.float32).numpy()
+    amax = np.abs(a).max(axis=1)
+    assert np.array_equal(xs, (amax / np.float32(127)).astype(np.float32))
+    assert np.abs(q.astype(int)).max() <= 127
+    assert np.all(np.abs(q.astype(int)).max(axis=1) == 127)  # the largest value maps to +-127
+    # |q*s - x| <= s/2 (plus the rounding of the division)
+    err = np.abs(q * xs[:, None].astype(np.float64) - a)
+    assert np.all(err <= xs[:, None] * (0.5 + 2e-5))  # x / s rounds with relative error 2^-24 on |q| <= 127
+
+
+@pytest.mark.parametrize("G,with_bias", [(32, True), (-1, False), (64, True)])
+def test_gemm_w4a8_exact_rational(oracle_mod, G, with_bias):
+    rng = np.random.default_rng([32, G + 2])
+    M, N, K = 2, 8, 64
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    xs = rng.uniform(0.001, 0.05, size=M).astype(np.float32)
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    Ge = K if G == -1 else G
+    scales = torch.from_numpy(rng.uniform(0.005, 0.02, size=(N, K // Ge))).to(torch.float16)
+    bias = torch.from_numpy(rng.normal(0, 1, size=N)).to(torch.float16) if with_bias else None
+    C = oracle_mod.gemm_w4a8(q, xs, oracle_mod.pack_codes(codes), scales, G, bias)
+    sf = scales.to(torch.float64).numpy()
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for g in range(K // Ge):
+                isum = sum(int(q[m, k]) * (int(codes[n, k]) - 8) for k in range(g * Ge, (g + 1) * Ge))
+                acc += Fraction(float(sf[n, g])) * isum
+            acc *= Fraction(float(xs[m]))
+            if bias is not None:
+                acc += Fraction(float(bias[n]))
+            assert abs(Fraction(C[m, n]) - acc) <= abs(acc) * Fraction(1, 2**50) + Fraction(1, 2**80)
+
+
+def test_gemm_w4a8_zero_weights_give_bias(oracle_mod):
+    M, N, K = 3, 16, 128
+    q = np.full((M, K), 100, dtype=np.int8)
+    codes = np.full((N, K), 8, dtype=np.uint8)
+    bias = torch.arange(N, dtype=torch.float16)
+    C = oracle_mod.gemm_w4a8(q, np.ones(M, np.float32), oracle_mod.pack_codes(codes),
+                             torch.ones((N, 1), dtype=torch.float16), -1, bias)
+    assert np.array_equal(C, np.tile(np.arange(N, dtype=np.float64), (M, 1)))
+
+
+def test_gemm_w4a8_matches_dequantised_product(oracle_mod):
+    # xs * (q @ W^T) with W the dequantised symmetric weights, by the library matmul.
+    rng = np.random.default_rng(33)
+    M, N, K, G = 5, 24, 256, 128
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    xs = rng.uniform(0.001, 0.05, size=M).astype(np.float32)
+    words = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    scales = torch.from_numpy(rng.uniform(0.005, 0.02, size=(N, K // G))).to(torch.bfloat16)
+    W = oracle_mod.dequant(words, scales, None, UINT4B8, G)
+    ref = (q.astype(np.float64) @ W.T) * xs[:, None].astype(np.float64)
+    C = oracle_mod.gemm_w4a8(q, xs, words, scales, G)
+    assert np.max(np.abs(C - ref)) <= 1e-12 * np.max(np.abs(ref))

@@ -64,6 +64,11 @@ MUTANTS = [
      "for (int r = 0; r < 16 && 16 * nt + r < N - 1; ++r) {"),
     ("layout_groups_unpadded", "return K / Ge == 1 ? 1 : padded_k(K) / Ge;", "return K / Ge;"),
     ("encode_zeros_unpadded_stride", "out[Z0 + (nt * Kgp + g) * 16 + r]", "out[Z0 + (nt * Kg + g) * 16 + r]"),
+    ("a8_truncates", "const float t = rintf((float)A[m * K + k] / s);", "const float t = truncf((float)A[m * K + k] / s);"),
+    ("a8_scale_128", "const float s = amax / 127.0f;", "const float s = amax / 128.0f;"),
+    ("w4a8_zero_7", "isum += (int64_t)q[m * K + k] * (code - 8);", "isum += (int64_t)q[m * K + k] * (code - 7);"),
+    ("w4a8_no_row_scale", "acc *= (double)xs[m];", "acc *= 1.0;"),
+    ("w4a8_group_scale_index", "acc += scales[n * Kg + g] * (double)isum;", "acc += scales[n * Kg] * (double)isum;"),
 ]
 
 # Pins to run (function, kwargs). Parametrised pins are listed per case.
@@ -90,6 +95,11 @@ PIN_CALLS = [
     (pins.test_device_encoder_padded_inverse, {}),
     (pins.test_device_encoder_padded_n_hand_words, {}),
     (pins.test_device_encoder_padded_n_inverse, {}),
+    (pins.test_quant_a8_hand_values, {}),
+    (pins.test_quant_a8_properties, {}),
+    (pins.test_gemm_w4a8_exact_rational, {"G": 32, "with_bias": True}),
+    (pins.test_gemm_w4a8_zero_weights_give_bias, {}),
+    (pins.test_gemm_w4a8_matches_dequantised_product, {}),
 ]
 
 
@@ -110,7 +120,7 @@ def test_planted_mistake_is_caught(oracle_mod, tmp_path, name, orig, planted):
     mut_c = tmp_path / "mutant.c"
     mut_c.write_text(src.replace(orig, planted))
     lib = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", "-std=c99", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(mut_c)], check=True)
+    subprocess.run(["gcc", "-std=c99", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(mut_c), "-lm"], check=True)
     torch.manual_seed(0)
     with oracle_mod._use_library(str(lib)):
         failed = _run_pins(oracle_mod)
