@@ -236,6 +236,43 @@ w4a16_status w4a16_gemm_dense(const void *A, int64_t M, int64_t lda, const void 
                               int64_t ldw, int32_t dtype, const void *bias, void *C, int64_t ldc, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* W4A8: int8 activations with the int4 weights, as the "mixed_precision"
+ * package page describes XPUW4A8IntLinearKernel (class docstring and
+ * `apply_weights`): each row of A is quantised dynamically to symmetric int8
+ * with one scale per row, and the int8 rows are multiplied by symmetric int4
+ * weights with the row scale and the group scales. Two calls.
+ *
+ * w4a8_quantize: per-token symmetric int8 quantisation of A.
+ *   xs[m]     = fp32(max_k |A[m, k]|) / 127   (fp32, IEEE division)
+ *   qa[m, k]  = rint(A[m, k] / xs[m])         (round half to even; always in
+ *               [-127, 127]); a row of zeros gets xs[m] = 0 and codes 0
+ *   A   [M, lda] act dtype, lda >= K, 16-byte aligned with lda % 8 == 0
+ *   qa  [M, ldq] int8, ldq >= K, 8-byte aligned with ldq % 8 == 0
+ *   xs  [M] fp32
+ * K % 8 == 0. M == 0 is a no-op. */
+w4a16_status w4a8_quantize(const void *A, int64_t M, int64_t K, int64_t lda, int32_t dtype, int8_t *qa, int64_t ldq,
+                           float *xs, hipStream_t stream);
+
+/* Bytes of device workspace w4a8_gemm needs for these arguments (0 if none):
+ * split-K partial results. out_bytes is a host pointer. */
+w4a16_status w4a8_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size, size_t *out_bytes);
+
+/* C[M, N] = xs[m] * sum_g s[n, g] * sum_{k in g} qa[m, k] * (q[n, k] - 8)
+ * (+ bias[n]), rounded once to the act dtype:
+ *   qa, xs   as written by w4a8_quantize (qa [M, ldq] int8, xs [M] fp32)
+ *   packed   the buffer w4a16_repack writes for the same N, K, group_size
+ *            and qtype W4A16_UINT4B8 (symmetric weights only, as on the
+ *            pages; the call cannot check this)
+ *   bias     [N] act dtype, or NULL; C [M, ldc] act dtype, ldc >= N
+ *   workspace, workspace_bytes  at least w4a8_workspace_size() bytes (may
+ *            be NULL when that is 0); calls that share one must be ordered
+ * The integer group sums are exact (int8 MFMA, int32 accumulation); each
+ * group's sum is scaled in fp32. Shapes as for w4a16_repack. M == 0 is a
+ * no-op. W4A16_ERR_SIZE if the workspace is too small. */
+w4a16_status w4a8_gemm(const int8_t *qa, const float *xs, int64_t M, int64_t ldq, const void *packed, int64_t N,
+                       int64_t K, int32_t group_size, int32_t dtype, const void *bias, void *C, int64_t ldc,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,9 @@ SIGNATURES = {
         [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _P, _SZ, _P],
     ),
     "w4a16_dequant": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _I32, _P, _I64, _P]),
+    "w4a8_quantize": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _P, _I64, _P, _P]),
+    "w4a8_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.POINTER(_SZ)]),
+    "w4a8_gemm": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _P, _P, _I64, _P, _SZ, _P]),
     "w4a16_gemm_dense": (
         ctypes.c_int,
         [_P, _I64, _I64, _P, _I64, _I64, _I64, _I32, _P, _P, _I64, _P, _SZ, _P],
@@ -277,6 +280,63 @@ def dequant(packed: torch.Tensor, N: int, K: int, group_size: int, qtype: int, d
         raise ValueError(f"out must be [N={N}, K={K}] with unit column stride")
     _check(load_library().w4a16_dequant(_ptr(packed), N, K, group_size, qtype, _DTYPE_CODE[dtype], _ptr(out),
                                         out.stride(0), _stream(packed)))
+    return out
+
+
+def quantize_a8(A: torch.Tensor, out: tuple[torch.Tensor, torch.Tensor] | None = None):
+    """Per-token symmetric int8 quantisation: A [M, K] -> (qa [M, K] int8, xs [M] fp32)."""
+    _need_cuda("A", A, (torch.float16, torch.bfloat16))
+    if A.dim() != 2 or A.stride(1) != 1:
+        raise ValueError("A must be 2-D with unit column stride")
+    M, K = A.shape
+    if out is None:
+        qa = torch.empty((M, K), dtype=torch.int8, device=A.device)
+        xs = torch.empty((M,), dtype=torch.float32, device=A.device)
+    else:
+        qa, xs = out
+        _need_cuda("qa", qa, torch.int8)
+        _need_cuda("xs", xs, torch.float32)
+        if qa.dim() != 2 or tuple(qa.shape) != (M, K) or qa.stride(1) != 1 or xs.shape != (M,):
+            raise ValueError("out must be (qa [M, K] with unit column stride, xs [M])")
+    _check(load_library().w4a8_quantize(_ptr(A), M, K, A.stride(0), _DTYPE_CODE[A.dtype], _ptr(qa), qa.stride(0),
+                                        _ptr(xs), _stream(A)))
+    return qa, xs
+
+
+def w4a8_workspace_size(M: int, N: int, K: int, group_size: int) -> int:
+    out = _SZ(0)
+    _check(load_library().w4a8_workspace_size(M, N, K, group_size, ctypes.byref(out)))
+    return int(out.value)
+
+
+def gemm_w4a8(qa: torch.Tensor, xs: torch.Tensor, packed: torch.Tensor, N: int, K: int, group_size: int,
+              dtype: torch.dtype, bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+              workspace: Workspace | None = None) -> torch.Tensor:
+    """C[M, N] from int8 activations (quantize_a8) and a symmetric (uint4b8) packed weight."""
+    _need_cuda("qa", qa, torch.int8)
+    _need_cuda("xs", xs, torch.float32)
+    _need_cuda("packed", packed)
+    if dtype not in _DTYPE_CODE:
+        raise ValueError(f"dtype {dtype} is not fp16 or bf16")
+    _need_cuda("bias", bias, dtype)
+    if qa.dim() != 2 or qa.shape[1] != K or qa.stride(1) != 1:
+        raise ValueError(f"qa must be [M, K={K}] with unit column stride")
+    M = qa.shape[0]
+    if xs.shape != (M,) or not xs.is_contiguous():
+        raise ValueError(f"xs must be a contiguous [M={M}] tensor")
+    if out is None:
+        out = torch.empty((M, N), dtype=dtype, device=qa.device)
+    _need_cuda("out", out, dtype)
+    if out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError(f"out must be [M={M}, N={N}] with unit column stride")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != N or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous [N={N}] tensor")
+    ws_bytes = w4a8_workspace_size(M, N, K, group_size) if M > 0 else 0
+    ws = (workspace or _default_workspace(qa.device)).get(ws_bytes)
+    _check(load_library().w4a8_gemm(
+        _ptr(qa), _ptr(xs), M, qa.stride(0), _ptr(packed), N, K, group_size, _DTYPE_CODE[dtype], _ptr(bias),
+        _ptr(out), out.stride(0), _ptr(ws) if ws_bytes else None, ws.numel() if (ws is not None and ws_bytes) else 0,
+        _stream(qa)))
     return out
 
 

@@ -78,6 +78,17 @@ constexpr size_t kCounterRegionBytes = 64 * 1024;  // 16384 u32 arrival counters
 SkinnyPlan plan_skinny(int64_t M, const Geometry& g);
 MfmaPlan plan_mfma(int64_t M, const Geometry& g);
 
+// W4A8 launch plan: MI row blocks of 16 per wave, the grid, and the K split
+// (partial results in the workspace when ksplit > 1).
+struct W4a8Plan {
+    int MI = 1;
+    int64_t blocks_n = 0, blocks_m = 0;
+    int64_t kc = 0;
+    int64_t ksplit = 1;
+    size_t partial_bytes = 0;
+};
+W4a8Plan plan_w4a8(int64_t M, const Geometry& g);
+
 // Launchers; each returns hipSuccess or the launch error. Shapes are already
 // validated by the caller.
 // Orientation of the checkpoint tensors read by launch_repack.
@@ -99,6 +110,11 @@ hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed
                        const void* bias, void* C, int64_t ldc, const MfmaPlan& p, hipStream_t stream);
 hipError_t launch_dequant(const void* packed, const Geometry& g, int dtype, void* dense, int64_t ldw,
                           hipStream_t stream);
+hipError_t launch_a8_quant(const void* A, int64_t M, int64_t K, int64_t lda, int dtype, int8_t* qa, int64_t ldq,
+                           float* xs, hipStream_t stream);
+hipError_t launch_w4a8(const int8_t* qa, const float* xs, int64_t M, int64_t ldq, const void* packed, const Geometry& g,
+                       int dtype, const void* bias, void* C, int64_t ldc, const W4a8Plan& p, void* workspace,
+                       hipStream_t stream);
 // hipBLASLt GEMM on a dense weight; returns a hipblasStatus_t value (0 on
 // success) and names the failing step in *what.
 int dense_gemm(const void* A, int64_t M, int64_t lda, const void* W, int64_t N, int64_t K, int64_t ldw, int dtype,

@@ -278,6 +278,76 @@ w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packe
 }
 
 
+w4a16_status w4a8_quantize(const void* A, int64_t M, int64_t K, int64_t lda, int32_t dtype, int8_t* qa, int64_t ldq,
+                           float* xs, hipStream_t stream) {
+    clear_error();
+    if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M=%lld must be >= 0", (long long)M);
+    if (K <= 0) return fail(W4A16_ERR_INVALID_ARG, "K=%lld must be positive", (long long)K);
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+        return fail(W4A16_ERR_INVALID_ARG, "dtype=%d is not a w4a16_dtype (0 fp16, 1 bf16)", dtype);
+    if (K % 8 != 0) return fail(W4A16_ERR_UNSUPPORTED, "K=%lld must be divisible by 8", (long long)K);
+    if (lda < K) return fail(W4A16_ERR_INVALID_ARG, "lda=%lld must be >= K=%lld", (long long)lda, (long long)K);
+    if (ldq < K) return fail(W4A16_ERR_INVALID_ARG, "ldq=%lld must be >= K=%lld", (long long)ldq, (long long)K);
+    if (M >= ((int64_t)1 << 31)) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld is too large (one workgroup per row)", (long long)M);
+    if (M == 0) return W4A16_OK;
+    if (A == nullptr || qa == nullptr || xs == nullptr) return fail(W4A16_ERR_INVALID_ARG, "A, qa and xs must not be NULL");
+    if (!aligned16(A) || lda % 8 != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "A must be 16-byte aligned with lda %% 8 == 0 (lda=%lld)", (long long)lda);
+    if ((reinterpret_cast<uintptr_t>(qa) & 7u) || ldq % 8 != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "qa must be 8-byte aligned with ldq %% 8 == 0 (ldq=%lld)", (long long)ldq);
+    if (reinterpret_cast<uintptr_t>(xs) & 3u) return fail(W4A16_ERR_INVALID_ARG, "xs must be 4-byte aligned");
+    hipError_t e = launch_a8_quant(A, M, K, lda, dtype, qa, ldq, xs, stream);
+    if (e != hipSuccess) return hip_fail("quantize kernel launch", e);
+    return W4A16_OK;
+}
+
+w4a16_status w4a8_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_size, size_t* out_bytes) {
+    clear_error();
+    if (out_bytes == nullptr) return fail(W4A16_ERR_INVALID_ARG, "out_bytes is NULL");
+    if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M=%lld must be >= 0", (long long)M);
+    Geometry g;
+    w4a16_status st = make_geometry(N, K, group_size, W4A16_UINT4B8, &g);
+    if (st != W4A16_OK) return st;
+    *out_bytes = M > 0 ? plan_w4a8(M, g).partial_bytes : 0;
+    return W4A16_OK;
+}
+
+w4a16_status w4a8_gemm(const int8_t* qa, const float* xs, int64_t M, int64_t ldq, const void* packed, int64_t N,
+                       int64_t K, int32_t group_size, int32_t dtype, const void* bias, void* C, int64_t ldc,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    clear_error();
+    Geometry g;
+    // The weights are symmetric (uint4b8), as the pages' W4A8 kernel requires.
+    w4a16_status st = make_geometry(N, K, group_size, W4A16_UINT4B8, &g);
+    if (st != W4A16_OK) return st;
+    if (M < 0) return fail(W4A16_ERR_INVALID_ARG, "M=%lld must be >= 0", (long long)M);
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+        return fail(W4A16_ERR_INVALID_ARG, "dtype=%d is not a w4a16_dtype (0 fp16, 1 bf16)", dtype);
+    if (ldq < K) return fail(W4A16_ERR_INVALID_ARG, "ldq=%lld must be >= K=%lld", (long long)ldq, (long long)K);
+    if (ldc < N) return fail(W4A16_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc, (long long)N);
+    if (M == 0) return W4A16_OK;
+    if (qa == nullptr || xs == nullptr || packed == nullptr || C == nullptr)
+        return fail(W4A16_ERR_INVALID_ARG, "qa, xs, packed and C must not be NULL");
+    if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(qa) & 7u) || ldq % 8 != 0)
+        return fail(W4A16_ERR_UNSUPPORTED, "qa must be 8-byte aligned with ldq %% 8 == 0 (ldq=%lld)", (long long)ldq);
+    if ((reinterpret_cast<uintptr_t>(xs) & 3u) || (reinterpret_cast<uintptr_t>(C) & 1u) ||
+        (reinterpret_cast<uintptr_t>(bias) & 1u))
+        return fail(W4A16_ERR_INVALID_ARG, "xs must be 4-byte and C, bias 2-byte aligned");
+    const W4a8Plan p = plan_w4a8(M, g);
+    if (p.blocks_m > 65535 || p.ksplit > 65535)
+        return fail(W4A16_ERR_UNSUPPORTED, "M=%lld is too large for one W4A8 launch", (long long)M);
+    if (p.partial_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < p.partial_bytes)
+            return fail(W4A16_ERR_SIZE, "a workspace of %zu bytes is smaller than the %zu bytes this call needs",
+                        workspace == nullptr ? (size_t)0 : workspace_bytes, p.partial_bytes);
+        if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(W4A16_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+    }
+    hipError_t e = launch_w4a8(qa, xs, M, ldq, packed, g, dtype, bias, C, ldc, p, workspace, stream);
+    if (e != hipSuccess) return hip_fail("w4a8 kernel launch", e);
+    return W4A16_OK;
+}
+
 w4a16_status w4a16_dequant(const void* packed, int64_t N, int64_t K, int32_t group_size, int32_t qtype, int32_t dtype,
                            void* dense, int64_t ldw, hipStream_t stream) {
     clear_error();

@@ -33,7 +33,7 @@ def lib():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w4a(?:16|8)_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_signatures():
@@ -254,3 +254,72 @@ def test_gemm_dense_rejects_before_any_hip_call(lib, kw, status, needle):
 def test_gemm_dense_m_zero_is_a_noop(lib):
     assert _gemm_dense(lib, M=0) == OK
     assert w4.last_error() == ""
+
+
+# ---------------------------------------------------------------- W4A8
+
+
+def _quant(lib, **kw):
+    a = dict(A=ctypes.c_void_p(4096), M=4, K=4096, lda=4096, dtype=0, qa=ctypes.c_void_p(8192), ldq=4096,
+             xs=ctypes.c_void_p(16384))
+    a.update(kw)
+    return lib.w4a8_quantize(a["A"], a["M"], a["K"], a["lda"], a["dtype"], a["qa"], a["ldq"], a["xs"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,needle",
+    [
+        (dict(dtype=2), INVALID, "dtype=2"),
+        (dict(K=12, lda=12, ldq=16), UNSUPPORTED, "K=12 must be divisible by 8"),
+        (dict(lda=4000), INVALID, "lda=4000 must be >= K=4096"),
+        (dict(ldq=4000), INVALID, "ldq=4000 must be >= K=4096"),
+        (dict(A=None), INVALID, "must not be NULL"),
+        (dict(A=ctypes.c_void_p(4104)), UNSUPPORTED, "16-byte aligned"),
+        (dict(qa=ctypes.c_void_p(8196)), UNSUPPORTED, "8-byte aligned"),
+        (dict(M=-1), INVALID, "M=-1"),
+    ],
+)
+def test_quantize_a8_rejects_before_any_hip_call(lib, kw, status, needle):
+    assert _quant(lib, **kw) == status
+    assert needle in w4.last_error()
+
+
+def test_quantize_a8_m_zero_is_a_noop(lib):
+    assert _quant(lib, M=0, A=None, qa=None, xs=None) == OK
+
+
+def _w4a8(lib, **kw):
+    a = dict(qa=ctypes.c_void_p(4096), xs=ctypes.c_void_p(8192), M=4096, ldq=4096, packed=ctypes.c_void_p(1 << 20),
+             N=4096, K=4096, G=128, dtype=1, bias=None, C=ctypes.c_void_p(16384), ldc=4096, ws=None, wsb=0)
+    a.update(kw)
+    return lib.w4a8_gemm(a["qa"], a["xs"], a["M"], a["ldq"], a["packed"], a["N"], a["K"], a["G"], a["dtype"],
+                         a["bias"], a["C"], a["ldc"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,needle",
+    [
+        (dict(G=96), UNSUPPORTED, "group_size=96 not supported"),
+        (dict(dtype=3), INVALID, "dtype=3"),
+        (dict(ldq=100), INVALID, "ldq=100 must be >= K=4096"),
+        (dict(ldc=100), INVALID, "ldc=100 must be >= N=4096"),
+        (dict(qa=None), INVALID, "must not be NULL"),
+        (dict(packed=ctypes.c_void_p(4100)), INVALID, "256-byte aligned"),
+        (dict(qa=ctypes.c_void_p(4100)), UNSUPPORTED, "8-byte aligned"),
+        # one row over 4096 x 4096 splits K and needs the partials workspace
+        (dict(M=1), SIZE, "workspace of 0 bytes is smaller"),
+    ],
+)
+def test_w4a8_gemm_rejects_before_any_hip_call(lib, kw, status, needle):
+    assert _w4a8(lib, **kw) == status
+    assert needle in w4.last_error()
+
+
+def test_w4a8_gemm_m_zero_is_a_noop(lib):
+    assert _w4a8(lib, M=0, qa=None, xs=None, C=None) == OK
+
+
+def test_w4a8_workspace_size():
+    assert w4.w4a8_workspace_size(1, 4096, 4096, 128) > 0
+    assert w4.w4a8_workspace_size(4096, 4096, 4096, 128) == 0
+    assert w4.w4a8_workspace_size(0, 4096, 4096, 128) == 0

@@ -790,3 +790,66 @@ def test_weights_beyond_2gib(M, path):
         ref, _ = oracle.gemm(A_rows, wq[n0:n0 + 48].cpu().numpy(), ws[n0:n0 + 48].cpu(), None, UINT4B8, G)
         err = oracle.rel_err(C[:, n0:n0 + 48].cpu()[rows], ref)
         assert err <= oracle.TOLERANCE["bf16"], f"columns {n0}..: rel err {err:.3e}"
+
+
+# ------------------------------------------------------------------ W4A8
+
+
+A8_QUANT = [(1, 4096, "f16", 0), (16, 14336, "bf16", 0), (37, 2880, "bf16", 64), (300, 1216, "f16", 8)]
+
+
+@pytest.mark.parametrize("M,K,dtype,pad", A8_QUANT, ids=[f"{c[0]}x{c[1]}{c[2]}p{c[3]}" for c in A8_QUANT])
+def test_quantize_a8_bit_exact(M, K, dtype, pad):
+    A = wi.random_activations(51, M, K, dtype, sigma=2.0)
+    A[min(3, M - 1)] = 0  # a row of zeros: scale 0, codes 0
+    if M > 5:
+        A[5, 7] = 1000.0  # one large value sets the row's scale
+    big = torch.zeros((M, K + pad), dtype=A.dtype, device=DEV)
+    big[:, :K] = A.to(DEV)
+    qa, xs = w4.quantize_a8(big[:, :K])
+    q_ref, xs_ref = oracle.quant_rows_a8(A)
+    np.testing.assert_array_equal(xs.cpu().numpy(), xs_ref)
+    np.testing.assert_array_equal(qa.cpu().numpy(), q_ref)
+
+
+W4A8_GEMM = [
+    # (M, N, K, G, dtype)
+    (1, 4096, 4096, 128, "f16"),
+    (8, 14336, 4096, -1, "bf16"),
+    (16, 4096, 14336, 32, "f16"),
+    (3, 1224, 2880, 64, "bf16"),  # N and K tails
+    (100, 4096, 4096, 256, "bf16"),
+    (2048, 4096, 4096, 128, "f16"),
+    (2048, 14336, 4096, -1, "bf16"),
+    (600, 2880, 1216, 32, "f16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,dtype", W4A8_GEMM, ids=[f"{c[0]}x{c[1]}x{c[2]}g{c[3]}{c[4]}" for c in W4A8_GEMM])
+def test_w4a8_gemm_parity(M, N, K, G, dtype):
+    case = _case(52, M, N, K, G, UINT4B8, dtype, with_bias=True)
+    wq, ws, _, A, bias = to_dev(case)
+    packed = w4.repack(wq, ws, None, G, UINT4B8)
+    qa, xs = w4.quantize_a8(A)
+    C = w4.gemm_w4a8(qa, xs, packed, N, K, G, case.torch_dtype, bias=bias)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    q_ref, xs_ref = oracle.quant_rows_a8(case.A[torch.as_tensor(rows)])
+    np.testing.assert_array_equal(qa.cpu().numpy()[rows], q_ref)
+    ref = oracle.gemm_w4a8(q_ref, xs_ref, case.weight_packed, case.weight_scale, G, case.bias)
+    err = rel_err_rows(C, ref, rows)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
+
+
+def test_w4a8_zero_row_gives_bias_and_no_store_past_n():
+    M, N, K, G = 4, 1224, 1216, 64
+    case = _case(53, M, N, K, G, UINT4B8, "bf16", with_bias=True)
+    wq, ws, _, A, bias = to_dev(case)
+    A[2] = 0
+    packed = w4.repack(wq, ws, None, G, UINT4B8)
+    qa, xs = w4.quantize_a8(A)
+    big = torch.full((M, N + 16), 77.0, dtype=torch.bfloat16, device=DEV)
+    C = w4.gemm_w4a8(qa, xs, packed, N, K, G, torch.bfloat16, bias=bias, out=big[:, :N])
+    torch.cuda.synchronize()
+    assert torch.all(big[:, N:] == 77.0)
+    assert torch.equal(C[2].cpu(), case.bias)
