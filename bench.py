@@ -329,6 +329,65 @@ def row_stride_rates(pads=(0, 64, 256, 0)):
     return {"workload": "lda = K + pad, ldc = N + pad (elements), G=-1 uint4b8 bf16, MFMA path", "rows": rows}
 
 
+INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
+
+
+def w4a8_rates():
+    """The W4A8 variant (w4a8_quantize + w4a8_gemm) on the decode shapes
+    (fp16, G = 128, weight-stream GB/s of the GEMM) and the prefill shapes
+    (bf16, G in {-1, 256}, symmetric weights; TOP/s against the int8 MFMA
+    peak), after the same warm-up and weight rotation as the other paths."""
+    out = {"int8_peak_tops": INT8_PEAK_TOPS}
+
+    def timed(g, fn_of_copy, n, warm_ms, reps):
+        graphs = capture_graphs([[(lambda c=c: fn_of_copy(c)) for c in range(n)]])
+        warm_up(graphs, warm_ms)
+        return time_graphs(graphs, reps, 3) * 1e3 / (reps * n)
+
+    wl = wi.WORKLOADS["decode_sym"]
+    dec = []
+    for (M, N, K) in wl["shapes"]:
+        g = Gemm(wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], wl["sigma"],
+                 copies_for(weight_stream_bytes(N, K, wl["G"], wl["qtype"], False)))
+        qa, xs = w4.quantize_a8(g.A)
+        C = torch.empty((M, N), dtype=g.A.dtype, device=DEV)
+        ws = w4.Workspace(DEV)
+        ws.get(w4.w4a8_workspace_size(M, N, K, wl["G"]))
+        n = len(g.packed)
+        gemm = lambda c: w4.gemm_w4a8(qa, xs, g.packed[c], N, K, wl["G"], g.A.dtype, out=C, workspace=ws)  # noqa: E731
+        both = lambda c: (w4.quantize_a8(g.A, out=(qa, xs)), gemm(c))  # noqa: E731
+        us = timed(g, gemm, n, 20.0, 5)
+        us_both = timed(g, both, n, 20.0, 5)
+        dec.append({"M": M, "N": N, "K": K, "gemm_us": round(us, 2), "with_quantize_us": round(us_both, 2),
+                    "weight_GBps": round(g.weight_bytes / us / 1e3, 1)})
+        del g
+        torch.cuda.empty_cache()
+    out["decode"] = {"workload": "decode shapes, G=128 symmetric weights, fp16 act", "rows": dec}
+
+    wl = wi.WORKLOADS["prefill"]
+    pre, tot_op, tot_us = [], 0.0, 0.0
+    for G in (-1, 256):
+        for (M, N, K) in wl["shapes"]:
+            g = Gemm(wl["cfg_id"], M, N, K, G, wi.UINT4B8, wl["dtype"], wl["sigma"], 2)
+            qa, xs = w4.quantize_a8(g.A)
+            C = torch.empty((M, N), dtype=g.A.dtype, device=DEV)
+            gemm = lambda c: w4.gemm_w4a8(qa, xs, g.packed[c], N, K, G, g.A.dtype, out=C)  # noqa: E731
+            quant = lambda c: w4.quantize_a8(g.A, out=(qa, xs))  # noqa: E731
+            us = timed(g, gemm, 2, PREFILL_WARM_MS, 10)
+            us_q = timed(g, quant, 2, 20.0, 10)
+            tops = g.flops / us / 1e6
+            pre.append({"M": M, "N": N, "K": K, "G": G, "gemm_us": round(us, 1), "quantize_us": round(us_q, 1),
+                        "tops": round(tops, 1), "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)})
+            tot_op += g.flops
+            tot_us += us
+            del g
+            torch.cuda.empty_cache()
+    out["prefill"] = {"workload": "prefill shapes, G in {-1, 256}, symmetric weights, bf16 act",
+                      "tops": round(tot_op / tot_us / 1e6, 1),
+                      "frac_of_int8_peak": round(tot_op / tot_us / 1e6 / INT8_PEAK_TOPS, 4), "rows": pre}
+    return out
+
+
 def prefill_dense_rates():
     """The dense prefill variant on the prefill workload: the dequantisation of
     each weight into a dense copy (w4a16_dequant) and hipBLASLt on that copy
@@ -401,6 +460,7 @@ def extras(warmup):
     out["repack"] = {"N": 14336, "K": 4096, "us": round(us, 1),
                      "GBps_read_plus_write": round(2 * g.weight_bytes / us / 1e3, 1)}
     out["repack_layout"] = time_repack_layouts(14336, 4096, 128)
+    out["w4a8"] = w4a8_rates()
     return out
 
 
@@ -436,6 +496,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-shape decode timings")
+    ap.add_argument("--w4a8-only", action="store_true",
+                    help="only time the W4A8 variant (int8 activations) on the decode and prefill shapes")
     ap.add_argument("--strides-only", action="store_true",
                     help="only time prefill GEMMs with padded and unpadded activation/output row strides")
     ap.add_argument("--prefill-only", action="store_true",
@@ -462,6 +524,9 @@ def main():
         print(json.dumps({"calibration_copy_bytes": n, "copies": 10}), flush=True)
         return
     w4.load_library()
+    if args.w4a8_only:
+        print(json.dumps({"w4a8": w4a8_rates()}), flush=True)
+        return
     if args.strides_only:
         print(json.dumps({"row_strides": row_stride_rates()}), flush=True)
         return

@@ -17,6 +17,7 @@ namespace w4a16 {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kA8DecodeChunk = 4;  // k-tiles per K chunk (and register stages) for up to 16 rows
 
 // ---------------------------------------------------------------- quantiser
 
@@ -99,8 +100,10 @@ __device__ __forceinline__ int64_t b_operand(uint32_t w) {
 
 // A wave owns MI row blocks of 16 and 4 n-tiles; a workgroup of 4 waves owns
 // 16*MI rows x 256 columns over one K chunk (blockIdx.z). Lane l of a 16x16
-// output block holds rows 4*(l/16) .. +3 of column l%16.
-template <int DT, int MI>
+// output block holds rows 4*(l/16) .. +3 of column l%16. The loads of NS
+// k-tiles are in flight at a time (a ring of register stages): with NS equal
+// to the chunk length every load is issued before the first MFMA.
+template <int DT, int MI, int NS>
 __global__ __launch_bounds__(256) void w4a8_kernel(A8Args a) {
     constexpr int NJ = 4;
     const int lane = threadIdx.x & 63;
@@ -142,18 +145,18 @@ __global__ __launch_bounds__(256) void w4a8_kernel(A8Args a) {
         for (int i = 0; i < MI; ++i) S[i] = i32x4{0, 0, 0, 0};
     };
 
-    for (int64_t kt = kt0; kt < kt1; ++kt) {
-        // The weight words of the wave's n-tiles (tiles past the padded N
-        // read tile NT-1 and are never stored).
-        u32x4 w[NJ];
+    // Stage u holds k-tile kt: the weight words of the wave's n-tiles (tiles
+    // past the padded N read tile NT-1 and are never stored) and the
+    // activation chunks of rows m0 + 16i + r at k = 128kt + 32s + 8g4 (rows
+    // past M and columns past K read as zero, never loaded).
+    u32x4 w[NS][NJ];
+    uint2 av[NS][MI][4];
+    auto load = [&](int u, int64_t kt) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int64_t nt = nt0 + j < a.NT ? nt0 + j : a.NT - 1;
-            w[j] = __builtin_nontemporal_load(a.codes + (nt * a.KTT + kt) * 64 + lane);
+            w[u][j] = __builtin_nontemporal_load(a.codes + (nt * a.KTT + kt) * 64 + lane);
         }
-        // The activation chunks: row m0 + 16i + r, k = 128kt + 32s + 8g4;
-        // rows past M and columns past K read as zero (never loaded).
-        uint2 av[MI][4];
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int64_t m = m0 + 16 * i + r;
@@ -162,26 +165,41 @@ __global__ __launch_bounds__(256) void w4a8_kernel(A8Args a) {
                 const int64_t k = kt * 128 + 32 * s + 8 * g4;
                 uint2 v = make_uint2(0u, 0u);
                 if (m < a.M && k < a.K) v = *reinterpret_cast<const uint2*>(a.qa + m * a.ldq + k);
-                av[i][s] = v;
+                av[u][i][s] = v;
             }
         }
+    };
+    auto compute = [&](int u, int64_t kt) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             int64_t A8[MI];
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                A8[i] = a_operand(av[i][s]);
+                A8[i] = a_operand(av[u][i][s]);
                 S[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A8[i], ones, S[i], 0, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int64_t B8 = b_operand(w[j][s]);
+                const int64_t B8 = b_operand(w[u][j][s]);
 #pragma unroll
                 for (int i = 0; i < MI; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A8[i], B8, acc[i][j], 0, 0, 0);
             }
             // A group ends with this slice: fold its integer sums.
             const int64_t kend = kt * 128 + 32 * (s + 1);
             if (!a.one_group && kend % a.Ge == 0) fold((kend - 1) / a.Ge);
+        }
+    };
+
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+        if (kt0 + u < kt1) load(u, kt0 + u);
+    for (int64_t kt = kt0; kt < kt1; kt += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            if (kt + u < kt1) {
+                compute(u, kt + u);
+                if (kt + u + NS < kt1) load(u, kt + u + NS);
+            }
         }
     }
     // The rest of a group cut by the chunk's end (or the only group).
@@ -234,12 +252,14 @@ W4a8Plan plan_w4a8(int64_t M, const Geometry& g) {
     const int64_t KTT = g.Kp / 128;
     p.blocks_n = (g.Np / 16 + 15) / 16;
     p.blocks_m = (M + 16 * p.MI - 1) / (16 * p.MI);
-    // Split K until there are about two workgroups per CU.
+    // Split K until there are about two workgroups per CU; up to 16 rows,
+    // chunks of at most 4 k-tiles, whose loads are all in flight at once.
     const int64_t blocks = p.blocks_n * p.blocks_m;
     int64_t ks = (2 * kCUs + blocks - 1) / blocks;
     if (ks > KTT) ks = KTT;
     if (ks < 1) ks = 1;
     p.kc = (KTT + ks - 1) / ks;
+    if (p.MI == 1 && p.kc > kA8DecodeChunk) p.kc = kA8DecodeChunk;
     p.ksplit = (KTT + p.kc - 1) / p.kc;
     p.partial_bytes = p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)g.Np * sizeof(float) : 0;
     return p;
@@ -278,11 +298,11 @@ hipError_t launch_w4a8(const int8_t* qa, const float* xs, int64_t M, int64_t ldq
     a.partials = p.ksplit > 1 ? static_cast<float*>(workspace) : nullptr;
     const dim3 grid((unsigned)p.blocks_n, (unsigned)p.blocks_m, (unsigned)p.ksplit);
     if (dtype == 0) {
-        if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<0, 1>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((w4a8_kernel<0, 2>), grid, dim3(256), 0, stream, a);
+        if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<0, 1, kA8DecodeChunk>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((w4a8_kernel<0, 2, 2>), grid, dim3(256), 0, stream, a);
     } else {
-        if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<1, 1>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((w4a8_kernel<1, 2>), grid, dim3(256), 0, stream, a);
+        if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<1, 1, kA8DecodeChunk>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((w4a8_kernel<1, 2, 2>), grid, dim3(256), 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.ksplit == 1) return e;
