@@ -80,14 +80,20 @@ MfmaPlan plan_mfma(int64_t M, const Geometry& g);
 
 // W4A8 launch plan: MI row blocks of 16 per wave, the grid, and the K split
 // (partial results in the workspace when ksplit > 1).
+// ring >= 0 selects the tiled ring kernel for large M instead (128 x 256
+// tiles, no K split): 0 for one group per row, else the 64-k slices per group.
 struct W4a8Plan {
     int MI = 1;
     int64_t blocks_n = 0, blocks_m = 0;
     int64_t kc = 0;
     int64_t ksplit = 1;
     size_t partial_bytes = 0;
+    int ring = -1;
+    int64_t m_tiles = 0, n_blocks = 0;
 };
-W4a8Plan plan_w4a8(int64_t M, const Geometry& g);
+// qa16: the activation codes are 16-byte aligned with ldq % 16 == 0 (the
+// ring kernel's loads need it; the workspace size assumes it is not).
+W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16 = false, int64_t ldq = 0);
 
 // Launchers; each returns hipSuccess or the launch error. Shapes are already
 // validated by the caller.

@@ -12,6 +12,7 @@
 // bias at the end, and C is rounded once.
 #include "device_common.h"
 #include "internal.h"
+#include "lds_stage.h"
 
 namespace w4a16 {
 namespace {
@@ -80,6 +81,7 @@ struct A8Args {
     uint16_t* C;
     int64_t ldc;
     float* partials;             // [ksplit][M][16*NT] when ksplit > 1
+    int64_t n_blocks;            // ring kernel: 256-column blocks of C
 };
 
 // Bytes of one activation chunk (k .. k+7 of a row) in the order the packed
@@ -244,9 +246,229 @@ __global__ __launch_bounds__(256) void w4a8_reduce_kernel(const float* __restric
     C[m * ldc + n] = to_act_bits<DT>(__builtin_fmaf(xs[m], sum, bv));
 }
 
+
+// Tiled ring kernel for large M (K % 128 == 0, one group per row or groups
+// of 64, 128 or 256 k). A workgroup of 8 waves computes a 128 x 256 tile of C;
+// wave (wm, wn) owns rows 64 wm .. +63 (4 row blocks) and n-tiles 4 wn .. +3.
+//  * Per K step of 128, the 128 x 128-byte activation tile and the
+//    workgroup's 16 packed weight tiles go from HBM/L2 straight into LDS
+//    with direct 16-byte buffer loads. Activation block 2 rb + h (1 KB) holds
+//    rows 16 rb .. +15 at k = 64 h .. +63; lane l's 16 bytes (row l % 16,
+//    k = 64 h + 16 (l / 16) .. +15) sit at 16 l.
+//  * Four LDS stages form a ring: step t reads stage t % 4 while the loads
+//    of steps t + 1 .. t + 3 are in flight. One barrier per step.
+//  * v_mfma_i32_16x16x64_i8 takes two packed words per lane (64 k). A word
+//    becomes signed bytes 16 (q - 8) without a zero-point term: with the
+//    sign bit of each nibble flipped, a nibble is the 4-bit two's complement
+//    of q - 8, and placed in the high half of a byte it reads as 16 (q - 8).
+//    The low nibbles (codes 0, 4, 1, 5 in pair order) move up by a shift;
+//    two v_perm put each 8-byte activation chunk in the same order.
+//  * Integer sums are exact (|16 (q - 8) qa| <= 16256; a chunk of at most
+//    131072 k stays below 2^31). GP = 0: one group per row, the scale is
+//    applied in the epilogue. GP > 0: a group spans GP slices of 64 k; at
+//    its end each sum is scaled by s / 16 into an fp32 result and the
+//    integer sum restarts.
+template <int DT, int GP>
+__global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
+    static_assert(GP == 0 || GP == 1 || GP == 2 || GP == 4, "groups of 64, 128 or 256 k, or one group");
+    constexpr int MI = 4, NJ = 4;
+    constexpr int NSC = GP == 0 ? 0 : (GP == 1 ? 2 : 1) * NJ;  // scale loads per wave and step
+    constexpr int STAGE_LOADS = 4 + NSC;
+    __shared__ __attribute__((aligned(1024))) unsigned char a0[16 * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char a1[16 * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char a2[16 * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char a3[16 * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b0[16 * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b1[16 * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b2[16 * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b3[16 * 1024];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int r = lane & 15, g4 = lane >> 4;
+    const int64_t lin = blockIdx.x;
+    const int64_t ty = lin / a.n_blocks, tx = lin - ty * a.n_blocks;
+    const int64_t m0 = ty * 128;
+    const int64_t ntb = tx * 16;  // first n-tile of the workgroup
+    const int64_t steps = a.KTT;
+
+    // The workgroup's operands as buffers based at its tile: rows
+    // [mb, mb + mr) of the activation codes (rows past M clamp to M - 1) and
+    // n-tiles [ntb, ntb + nn) of the packed weight (tiles past it clamp).
+    const int64_t mb = m0 < a.M - 1 ? m0 : a.M - 1;
+    const int64_t mr = a.M - mb < 128 ? a.M - mb : 128;
+    const int64_t nn = a.NT - ntb < 16 ? a.NT - ntb : 16;
+    const int8_t* abase = a.qa + mb * a.ldq;
+    const uint32_t a_bytes = (uint32_t)((mr - 1) * a.ldq + a.K);
+    const u32x4* cbase = a.codes + ntb * a.KTT * 64;
+    const uint32_t c_bytes = (uint32_t)(nn * a.KTT * 1024);
+    const uint16_t* sbase = a.scales + ntb * a.Kg * 16;
+    const uint32_t s_bytes = (uint32_t)(nn * a.Kg * 32);
+    auto rsrc = [&](const void* base, uint32_t bytes, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
+    };
+    // This wave loads activation blocks 2 wave + h (row block `wave`) and
+    // weight tiles 2 wave + t of the workgroup.
+    int64_t arow = m0 + 16 * wave + r;
+    if (arow > a.M - 1) arow = a.M - 1;
+    const uint32_t a_off = (uint32_t)((arow - mb) * a.ldq + 16 * g4);
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    // LDS offset of this lane's first activation chunk in the wave's rows.
+    const uint32_t a_rd = (uint32_t)(8 * wm * 1024 + 16 * (16 * (g4 >> 1) + r) + 8 * (g4 & 1));
+    uint32_t b_tile[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int64_t nt = ntb + 2 * wave + t;
+        b_tile[t] = (uint32_t)((nt < a.NT ? nt : a.NT - 1) - ntb);
+    }
+    auto nt_ld = [&](int j) {
+        const int64_t nt = ntb + 4 * wn + j;
+        return nt < a.NT ? nt : a.NT - 1;
+    };
+
+    // Part h (0, 1) of the loads of step st: activation block h and weight
+    // tile h of the wave, and with h == 1 the scales of the step's groups.
+    auto issue = [&](int64_t st, int h, unsigned char* abuf, unsigned char* bbuf, uint32_t (&sb)[NSC > 0 ? NSC : 1]) {
+        const bool live = st < steps;
+        load_lds16(rsrc(abase, a_bytes, live), abuf + (2 * wave + h) * 1024, a_off, (uint32_t)(st * 128 + 64 * h));
+        load_lds16(rsrc(cbase, c_bytes, live), bbuf + (2 * wave + h) * 1024, lane16,
+                   (uint32_t)((b_tile[h] * a.KTT + st) * 1024));
+        if (GP > 0 && h == 1) {
+            const __amdgpu_buffer_rsrc_t rs = rsrc(sbase, s_bytes, live);
+            constexpr int NG = GP == 1 ? 2 : 1;
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                const int64_t g = GP == 1 ? 2 * st + q : (GP == 2 ? st : st / 2);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const uint32_t so = (uint32_t)(((nt_ld(j) - ntb) * a.Kg + g) * 16);
+                    sb[q * NJ + j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)r * 2, so * 2, 0);
+                }
+            }
+        }
+    };
+
+    i32x4 acc[MI][NJ];
+    floatx4 accf[GP > 0 ? MI : 1][GP > 0 ? NJ : 1];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            acc[i][j] = i32x4{0, 0, 0, 0};
+            if (GP > 0) accf[GP > 0 ? i : 0][GP > 0 ? j : 0] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    const i32x4 zero4 = {0, 0, 0, 0};
+
+    // Step st (u = st % 4, known at compile time after inlining) reads stage
+    // u and issues the loads of step st + 3 into stage (u + 3) % 4.
+    auto step = [&](int64_t st, int u, unsigned char* abuf, unsigned char* bbuf,
+                    const uint32_t (&sb)[NSC > 0 ? NSC : 1], unsigned char* nabuf, unsigned char* nbbuf,
+                    uint32_t (&nsb)[NSC > 0 ? NSC : 1]) {
+        u32x4 raw[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) raw[j] = *reinterpret_cast<const u32x4*>(bbuf + (4 * wn + j) * 1024 + lane16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            issue(st + 3, h, nabuf, nbbuf, nsb);
+            // Weight operands of slice h: words 2h and 2h + 1 (k = 64 h + 8 g4
+            // and 64 h + 32 + 8 g4), low nibbles then high nibbles of each.
+            i32x4 B[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint32_t w = raw[j][2 * h + e];
+                    B[j][2 * e] = (int32_t)(((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
+                    B[j][2 * e + 1] = (int32_t)((w & 0xF0F0F0F0u) ^ 0x80808080u);
+                }
+            }
+            // A slice starts a group: its first product starts from zero.
+            const bool start = GP > 0 && ((2 * u + h) % (GP > 0 ? GP : 1)) == 0;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                // Row 16 (4 wm + i) + r: 8 bytes at k = 64 h + 8 g4 (lane
+                // 16 (g4 / 2) + r of block 2 (4 wm + i) + h, half g4 % 2) and
+                // 8 bytes at k + 32 (512 bytes on).
+                const unsigned char* ap = abuf + (a_rd + (2 * i + h) * 1024);
+                const uint64_t v0 = *reinterpret_cast<const uint64_t*>(ap);
+                const uint64_t v1 = *reinterpret_cast<const uint64_t*>(ap + 512);
+                i32x4 A;
+                A[0] = (int32_t)__builtin_amdgcn_perm((uint32_t)(v0 >> 32), (uint32_t)v0, 0x05010400u);
+                A[1] = (int32_t)__builtin_amdgcn_perm((uint32_t)(v0 >> 32), (uint32_t)v0, 0x07030602u);
+                A[2] = (int32_t)__builtin_amdgcn_perm((uint32_t)(v1 >> 32), (uint32_t)v1, 0x05010400u);
+                A[3] = (int32_t)__builtin_amdgcn_perm((uint32_t)(v1 >> 32), (uint32_t)v1, 0x07030602u);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B[j], start ? zero4 : acc[i][j], 0, 0, 0);
+            }
+            // A slice ends a group: fold the integer sums with s / 16.
+            if (GP > 0 && ((2 * u + h + 1) % (GP > 0 ? GP : 1)) == 0) {
+                const int q = GP == 1 ? h : 0;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const float sc = 0.0625f * act_to_float<DT>((uint16_t)sb[q * NJ + j]);
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            accf[GP > 0 ? i : 0][GP > 0 ? j : 0][jj] =
+                                __builtin_fmaf(sc, (float)acc[i][j][jj], accf[GP > 0 ? i : 0][GP > 0 ? j : 0][jj]);
+                }
+            }
+        }
+        // Stage st + 1 has landed once only the loads of steps st + 2 and
+        // st + 3 may be outstanding; the barrier then also frees stage u for
+        // step st + 4.
+        wait_vmcnt<2 * STAGE_LOADS>();
+        stage_barrier();
+    };
+
+    uint32_t sb0[NSC > 0 ? NSC : 1], sb1[NSC > 0 ? NSC : 1], sb2[NSC > 0 ? NSC : 1], sb3[NSC > 0 ? NSC : 1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) issue(0, h, a0, b0, sb0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) issue(1, h, a1, b1, sb1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) issue(2, h, a2, b2, sb2);
+    wait_vmcnt<2 * STAGE_LOADS>();
+    stage_barrier();
+    int64_t st = 0;
+    for (; st + 4 <= steps; st += 4) {
+        step(st, 0, a0, b0, sb0, a3, b3, sb3);
+        step(st + 1, 1, a1, b1, sb1, a0, b0, sb0);
+        step(st + 2, 2, a2, b2, sb2, a1, b1, sb1);
+        step(st + 3, 3, a3, b3, sb3, a2, b2, sb2);
+    }
+    if (st < steps) step(st, 0, a0, b0, sb0, a3, b3, sb3);
+    if (st + 1 < steps) step(st + 1, 1, a1, b1, sb1, a0, b0, sb0);
+    if (st + 2 < steps) step(st + 2, 2, a2, b2, sb2, a1, b1, sb1);
+    wait_vmcnt<0>();
+
+    // Epilogue: lane l holds rows 4 (l / 16) .. +3 of column l % 16 of each block.
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int64_t nt = ntb + 4 * wn + j;
+        if (nt >= a.NT) continue;
+        const int64_t n = nt * 16 + r;
+        if (n >= a.N) continue;
+        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+        const float sc = GP == 0 ? 0.0625f * act_to_float<DT>(a.scales[nt * a.Kg * 16 + r]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int64_t m = m0 + 64 * wm + 16 * i + 4 * g4 + jj;
+                if (m >= a.M) continue;
+                const float v = GP == 0 ? sc * (float)acc[i][j][jj] : accf[GP > 0 ? i : 0][GP > 0 ? j : 0][jj];
+                a.C[m * a.ldc + n] = to_act_bits<DT>(__builtin_fmaf(a.xs[m], v, bv));
+            }
+        }
+    }
+}
 }  // namespace
 
-W4a8Plan plan_w4a8(int64_t M, const Geometry& g) {
+W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16, int64_t ldq) {
     W4a8Plan p;
     p.MI = M <= 16 ? 1 : 2;
     const int64_t KTT = g.Kp / 128;
@@ -262,6 +484,21 @@ W4a8Plan plan_w4a8(int64_t M, const Geometry& g) {
     if (p.MI == 1 && p.kc > kA8DecodeChunk) p.kc = kA8DecodeChunk;
     p.ksplit = (KTT + p.kc - 1) / p.kc;
     p.partial_bytes = p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)g.Np * sizeof(float) : 0;
+
+    // The ring kernel, when its 128 x 256 tiles fill the chip at least once
+    // and its constraints hold: no K tail, one group per row (at most 131072
+    // k, so that the integer sums fit in 32 bits) or groups of 64 to 256 k,
+    // 16-byte aligned activation rows, and per-tile offsets below 2^31.
+    const int64_t m_tiles = (M + 127) / 128, n_blocks = (g.Np / 16 + 15) / 16;
+    const bool groups_ok = g.Kg == 1 ? g.Kp <= 131072 : (g.Ge >= 64 && g.Ge <= 256);
+    if (qa16 && g.Kp == g.K && groups_ok && m_tiles * n_blocks >= kCUs && m_tiles * n_blocks <= (1 << 22) &&
+        128 * ldq + g.K < ((int64_t)1 << 31) && 16 * (g.Kp / 128) * 1024 < ((int64_t)1 << 31)) {
+        p.ring = g.Kg == 1 ? 0 : (int)(g.Ge / 64);
+        p.m_tiles = m_tiles;
+        p.n_blocks = n_blocks;
+        p.ksplit = 1;
+        p.partial_bytes = 0;
+    }
     return p;
 }
 
@@ -296,6 +533,24 @@ hipError_t launch_w4a8(const int8_t* qa, const float* xs, int64_t M, int64_t ldq
     a.C = static_cast<uint16_t*>(C);
     a.ldc = ldc;
     a.partials = p.ksplit > 1 ? static_cast<float*>(workspace) : nullptr;
+    a.n_blocks = p.n_blocks;
+    if (p.ring >= 0) {
+        const dim3 rgrid((unsigned)(p.m_tiles * p.n_blocks));
+#define W4A8_RING(D, G) hipLaunchKernelGGL((w4a8_ring_kernel<D, G>), rgrid, dim3(512), 0, stream, a)
+        if (dtype == 0) {
+            if (p.ring == 0) W4A8_RING(0, 0);
+            else if (p.ring == 1) W4A8_RING(0, 1);
+            else if (p.ring == 2) W4A8_RING(0, 2);
+            else W4A8_RING(0, 4);
+        } else {
+            if (p.ring == 0) W4A8_RING(1, 0);
+            else if (p.ring == 1) W4A8_RING(1, 1);
+            else if (p.ring == 2) W4A8_RING(1, 2);
+            else W4A8_RING(1, 4);
+        }
+#undef W4A8_RING
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)p.blocks_n, (unsigned)p.blocks_m, (unsigned)p.ksplit);
     if (dtype == 0) {
         if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<0, 1, kA8DecodeChunk>), grid, dim3(256), 0, stream, a);

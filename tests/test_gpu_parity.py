@@ -822,6 +822,12 @@ W4A8_GEMM = [
     (2048, 4096, 4096, 128, "f16"),
     (2048, 14336, 4096, -1, "bf16"),
     (600, 2880, 1216, 32, "f16"),
+    # 128 x 256 ring tiles (at least one per CU): groups of 64, 128, 256 k
+    # and one group, with ragged M and a ragged last column block.
+    (2000, 4104, 4096, 64, "bf16"),
+    (1100, 14336, 2048, 128, "bf16"),
+    (2048, 4096, 14336, 256, "f16"),
+    (1999, 4232, 2944, -1, "f16"),
 ]
 
 
@@ -853,3 +859,21 @@ def test_w4a8_zero_row_gives_bias_and_no_store_past_n():
     torch.cuda.synchronize()
     assert torch.all(big[:, N:] == 77.0)
     assert torch.equal(C[2].cpu(), case.bias)
+
+
+@pytest.mark.parametrize("M,N,K,G", [(2048, 4096, 4096, 128), (1100, 8200, 2048, 256), (2000, 4096, 4096, -1),
+                                     (2048, 4096, 2048, 64)])
+def test_w4a8_ring_equals_register_kernel(M, N, K, G):
+    """The tiled ring kernel (16-byte aligned codes, ldq % 16 == 0) and the
+    register kernel (ldq % 16 == 8) form the same exact integer group sums
+    and fold them identically, so their results agree bit for bit."""
+    case = _case(54, M, N, K, G, UINT4B8, "bf16", with_bias=True)
+    wq, ws, _, A, bias = to_dev(case)
+    packed = w4.repack(wq, ws, None, G, UINT4B8)
+    qa, xs = w4.quantize_a8(A)
+    padded = torch.zeros((M, K + 8), dtype=torch.int8, device=DEV)
+    padded[:, :K] = qa
+    C_ring = w4.gemm_w4a8(qa, xs, packed, N, K, G, torch.bfloat16, bias=bias)
+    C_reg = w4.gemm_w4a8(padded[:, :K], xs, packed, N, K, G, torch.bfloat16, bias=bias)
+    torch.cuda.synchronize()
+    assert torch.equal(C_ring, C_reg)
