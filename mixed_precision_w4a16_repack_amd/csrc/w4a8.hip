@@ -84,6 +84,18 @@ struct A8Args {
     int64_t n_blocks;            // ring kernel: 256-column blocks of C
 };
 
+// 64 wait states between the int8 MFMAs issued before this point and the
+// VALU instructions after it. This compiler spaces a VALU read of a
+// v_mfma_i32_16x16x64_i8 result only 8 wait states from the MFMA (16 or more
+// for v_mfma_f32_16x16x32_bf16). On MI355X such reads returned stale sums,
+// now and then, with 8, 19 and 32 wait states; with 64 they did not. The
+// scheduling barriers keep every instruction on its side.
+__device__ __forceinline__ void mfma_i8_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Bytes of one activation chunk (k .. k+7 of a row) in the order the packed
 // weight word gives its codes after the nibble split below: 0,4,1,5 | 2,6,3,7.
 __device__ __forceinline__ int64_t a_operand(uint2 v) {
@@ -272,8 +284,7 @@ template <int DT, int GP>
 __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     static_assert(GP == 0 || GP == 1 || GP == 2 || GP == 4, "groups of 64, 128 or 256 k, or one group");
     constexpr int MI = 4, NJ = 4;
-    constexpr int NSC = GP == 0 ? 0 : (GP == 1 ? 2 : 1) * NJ;  // scale loads per wave and step
-    constexpr int STAGE_LOADS = 4 + NSC;
+    constexpr int NSC = GP == 0 ? 1 : (GP == 1 ? 2 : 1) * NJ;  // scale registers per stage
     __shared__ __attribute__((aligned(1024))) unsigned char a0[16 * 1024];
     __shared__ __attribute__((aligned(1024))) unsigned char a1[16 * 1024];
     __shared__ __attribute__((aligned(1024))) unsigned char a2[16 * 1024];
@@ -328,26 +339,31 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     };
 
     // Part h (0, 1) of the loads of step st: activation block h and weight
-    // tile h of the wave, and with h == 1 the scales of the step's groups.
-    auto issue = [&](int64_t st, int h, unsigned char* abuf, unsigned char* bbuf, uint32_t (&sb)[NSC > 0 ? NSC : 1]) {
+    // tile h of the wave.
+    auto issue = [&](int64_t st, int h, unsigned char* abuf, unsigned char* bbuf) {
         const bool live = st < steps;
         load_lds16(rsrc(abase, a_bytes, live), abuf + (2 * wave + h) * 1024, a_off, (uint32_t)(st * 128 + 64 * h));
         load_lds16(rsrc(cbase, c_bytes, live), bbuf + (2 * wave + h) * 1024, lane16,
                    (uint32_t)((b_tile[h] * a.KTT + st) * 1024));
-        if (GP > 0 && h == 1) {
-            const __amdgpu_buffer_rsrc_t rs = rsrc(sbase, s_bytes, live);
-            constexpr int NG = GP == 1 ? 2 : 1;
+    };
+    // The scales of the groups that end in step st (GP = 4: only odd steps
+    // end a group), for the wave's four columns.
+    auto issue_scales = [&](int64_t st, uint32_t (&sb)[NSC]) {
+        if (GP == 0) return;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(sbase, s_bytes, st < steps);
+        constexpr int NG = GP == 1 ? 2 : 1;
 #pragma unroll
-            for (int q = 0; q < NG; ++q) {
-                const int64_t g = GP == 1 ? 2 * st + q : (GP == 2 ? st : st / 2);
+        for (int q = 0; q < NG; ++q) {
+            const int64_t g = GP == 1 ? 2 * st + q : (GP == 2 ? st : st / 2);
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const uint32_t so = (uint32_t)(((nt_ld(j) - ntb) * a.Kg + g) * 16);
-                    sb[q * NJ + j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)r * 2, so * 2, 0);
-                }
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t so = (uint32_t)(((nt_ld(j) - ntb) * a.Kg + g) * 16);
+                sb[q * NJ + j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)r * 2, so * 2, 0);
             }
         }
     };
+    // Scale loads per step, over two consecutive steps.
+    constexpr int SC2 = GP == 0 ? 0 : (GP == 4 ? NSC : 2 * NSC);
 
     i32x4 acc[MI][NJ];
     floatx4 accf[GP > 0 ? MI : 1][GP > 0 ? NJ : 1];
@@ -361,16 +377,19 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     const i32x4 zero4 = {0, 0, 0, 0};
 
     // Step st (u = st % 4, known at compile time after inlining) reads stage
-    // u and issues the loads of step st + 3 into stage (u + 3) % 4.
-    auto step = [&](int64_t st, int u, unsigned char* abuf, unsigned char* bbuf,
-                    const uint32_t (&sb)[NSC > 0 ? NSC : 1], unsigned char* nabuf, unsigned char* nbbuf,
-                    uint32_t (&nsb)[NSC > 0 ? NSC : 1]) {
+    // u, loads the scales of step st + 2 (into the registers of stage
+    // (u + 2) % 4) and then the operands of step st + 3 (into stage
+    // (u + 3) % 4). A step's scales are loaded before the operands of the
+    // step after it, so waiting for them never waits for later operands.
+    auto step = [&](int64_t st, int u, unsigned char* abuf, unsigned char* bbuf, const uint32_t (&sb)[NSC],
+                    uint32_t (&ssb)[NSC], unsigned char* nabuf, unsigned char* nbbuf) {
+        if (GP == 1 || GP == 2 || (GP == 4 && (u & 1))) issue_scales(st + 2, ssb);
         u32x4 raw[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) raw[j] = *reinterpret_cast<const u32x4*>(bbuf + (4 * wn + j) * 1024 + lane16);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            issue(st + 3, h, nabuf, nbbuf, nsb);
+            issue(st + 3, h, nabuf, nbbuf);
             // Weight operands of slice h: words 2h and 2h + 1 (k = 64 h + 8 g4
             // and 64 h + 32 + 8 g4), low nibbles then high nibbles of each.
             i32x4 B[NJ];
@@ -405,6 +424,7 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
             // A slice ends a group: fold the integer sums with s / 16.
             if (GP > 0 && ((2 * u + h + 1) % (GP > 0 ? GP : 1)) == 0) {
                 const int q = GP == 1 ? h : 0;
+                mfma_i8_drain();
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const float sc = 0.0625f * act_to_float<DT>((uint16_t)sb[q * NJ + j]);
@@ -417,35 +437,40 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
                 }
             }
         }
-        // Stage st + 1 has landed once only the loads of steps st + 2 and
-        // st + 3 may be outstanding; the barrier then also frees stage u for
-        // step st + 4.
-        wait_vmcnt<2 * STAGE_LOADS>();
+        // Stage st + 1 has landed once only the loads issued in steps st - 1
+        // and st (operands of steps st + 2, st + 3 and their scales) may be
+        // outstanding; the barrier then also frees stage u for step st + 4.
+        wait_vmcnt<8 + SC2>();
         stage_barrier();
     };
 
-    uint32_t sb0[NSC > 0 ? NSC : 1], sb1[NSC > 0 ? NSC : 1], sb2[NSC > 0 ? NSC : 1], sb3[NSC > 0 ? NSC : 1];
+    uint32_t sb0[NSC], sb1[NSC], sb2[NSC], sb3[NSC];
+    // Operands of steps 0 .. 2 and scales of steps 0 and 1, in the order the
+    // steps keep (the scales of step k before the operands of step k + 1).
 #pragma unroll
-    for (int h = 0; h < 2; ++h) issue(0, h, a0, b0, sb0);
+    for (int h = 0; h < 2; ++h) issue(0, h, a0, b0);
+    if (GP == 1 || GP == 2) issue_scales(0, sb0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) issue(1, h, a1, b1, sb1);
+    for (int h = 0; h < 2; ++h) issue(1, h, a1, b1);
+    if (GP != 0) issue_scales(1, sb1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) issue(2, h, a2, b2, sb2);
-    wait_vmcnt<2 * STAGE_LOADS>();
+    for (int h = 0; h < 2; ++h) issue(2, h, a2, b2);
+    wait_vmcnt<8 + SC2>();
     stage_barrier();
     int64_t st = 0;
     for (; st + 4 <= steps; st += 4) {
-        step(st, 0, a0, b0, sb0, a3, b3, sb3);
-        step(st + 1, 1, a1, b1, sb1, a0, b0, sb0);
-        step(st + 2, 2, a2, b2, sb2, a1, b1, sb1);
-        step(st + 3, 3, a3, b3, sb3, a2, b2, sb2);
+        step(st, 0, a0, b0, sb0, sb2, a3, b3);
+        step(st + 1, 1, a1, b1, sb1, sb3, a0, b0);
+        step(st + 2, 2, a2, b2, sb2, sb0, a1, b1);
+        step(st + 3, 3, a3, b3, sb3, sb1, a2, b2);
     }
-    if (st < steps) step(st, 0, a0, b0, sb0, a3, b3, sb3);
-    if (st + 1 < steps) step(st + 1, 1, a1, b1, sb1, a0, b0, sb0);
-    if (st + 2 < steps) step(st + 2, 2, a2, b2, sb2, a1, b1, sb1);
+    if (st < steps) step(st, 0, a0, b0, sb0, sb2, a3, b3);
+    if (st + 1 < steps) step(st + 1, 1, a1, b1, sb1, sb3, a0, b0);
+    if (st + 2 < steps) step(st + 2, 2, a2, b2, sb2, sb0, a1, b1);
     wait_vmcnt<0>();
 
     // Epilogue: lane l holds rows 4 (l / 16) .. +3 of column l % 16 of each block.
+    if (GP == 0) mfma_i8_drain();
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int64_t nt = ntb + 4 * wn + j;
