@@ -91,9 +91,10 @@ struct W4a8Plan {
     int ring = -1;
     int64_t m_tiles = 0, n_blocks = 0;
 };
-// qa16: the activation codes are 16-byte aligned with ldq % 16 == 0 (the
-// ring kernel's loads need it; the workspace size assumes it is not).
-W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16 = false, int64_t ldq = 0);
+// qa16: the activation codes are 16-byte aligned with ldq % 16 == 0; c16: C
+// is 16-byte aligned with ldc % 8 == 0 (the ring kernel's loads and stores
+// need both; the workspace size assumes they do not hold).
+W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16 = false, int64_t ldq = 0, bool c16 = false);
 
 // Launchers; each returns hipSuccess or the launch error. Shapes are already
 // validated by the caller.

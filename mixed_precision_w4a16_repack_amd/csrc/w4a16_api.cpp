@@ -335,7 +335,8 @@ w4a16_status w4a8_gemm(const int8_t* qa, const float* xs, int64_t M, int64_t ldq
         (reinterpret_cast<uintptr_t>(bias) & 1u))
         return fail(W4A16_ERR_INVALID_ARG, "xs must be 4-byte and C, bias 2-byte aligned");
     const bool qa16 = (reinterpret_cast<uintptr_t>(qa) & 15u) == 0 && ldq % 16 == 0;
-    const W4a8Plan p = plan_w4a8(M, g, qa16, ldq);
+    const bool c16 = (reinterpret_cast<uintptr_t>(C) & 15u) == 0 && ldc % 8 == 0;
+    const W4a8Plan p = plan_w4a8(M, g, qa16, ldq, c16);
     if (p.blocks_m > 65535 || p.ksplit > 65535)
         return fail(W4A16_ERR_UNSUPPORTED, "M=%lld is too large for one W4A8 launch", (long long)M);
     if (p.partial_bytes > 0) {

@@ -469,31 +469,53 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     if (st + 2 < steps) step(st + 2, 2, a2, b2, sb2, sb0, a1, b1);
     wait_vmcnt<0>();
 
-    // Epilogue: lane l holds rows 4 (l / 16) .. +3 of column l % 16 of each block.
+    // Epilogue. The tile goes through LDS so that C is written in whole
+    // 16-byte row chunks: once every wave's loads have landed (the steps past
+    // K load zeros into the stages), rows 32 q .. 32 q + 31 of the tile go to
+    // stage buffer a_q, 512 bytes per row. Chunk c (8 columns) of tile row m
+    // sits at chunk c ^ 2 ((m / 4) % 4), which puts the four row groups of a
+    // 16 x 16 block on different LDS banks.
+    stage_barrier();
     if (GP == 0) mfma_i8_drain();
+    // Lane l holds rows 4 (l / 16) .. +3 of column l % 16 of each block.
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int64_t nt = ntb + 4 * wn + j;
-        if (nt >= a.NT) continue;
+        int64_t nt = ntb + 4 * wn + j;
+        nt = nt < a.NT ? nt : a.NT - 1;
         const int64_t n = nt * 16 + r;
-        if (n >= a.N) continue;
-        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+        const float bv = a.bias && n < a.N ? act_to_float<DT>(a.bias[n]) : 0.f;
         const float sc = GP == 0 ? 0.0625f * act_to_float<DT>(a.scales[nt * a.Kg * 16 + r]) : 0.f;
+        const uint32_t col = (uint32_t)(16 * (4 * wn + j) + r);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
+            unsigned char* rows = wm ? (i < 2 ? a2 : a3) : (i < 2 ? a0 : a1);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int64_t m = m0 + 64 * wm + 16 * i + 4 * g4 + jj;
-                if (m >= a.M) continue;
+                int64_t m = m0 + 64 * wm + 16 * i + 4 * g4 + jj;
+                m = m < a.M ? m : a.M - 1;
                 const float v = GP == 0 ? sc * (float)acc[i][j][jj] : accf[GP > 0 ? i : 0][GP > 0 ? j : 0][jj];
-                a.C[m * a.ldc + n] = to_act_bits<DT>(__builtin_fmaf(a.xs[m], v, bv));
+                const uint32_t row = (uint32_t)(16 * (i & 1) + 4 * g4 + jj);
+                const uint32_t off = row * 512 + ((((col >> 3) ^ (2u * (uint32_t)g4)) << 4) | ((col & 7) << 1));
+                *reinterpret_cast<uint16_t*>(rows + off) = to_act_bits<DT>(__builtin_fmaf(a.xs[m], v, bv));
             }
         }
+    }
+    stage_barrier();
+    // Thread t stores chunk t % 32 of tile rows 16 p + t / 32, p = 0 .. 7.
+    const uint32_t ch = threadIdx.x & 31;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const uint32_t row = 16 * (p & 1) + (threadIdx.x >> 5);  // row within a_q, q = p / 2
+        const unsigned char* rows = p < 2 ? a0 : (p < 4 ? a1 : (p < 6 ? a2 : a3));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(rows + row * 512 + ((ch ^ (2u * ((row >> 2) & 3u))) << 4));
+        const int64_t m = m0 + 16 * p + (threadIdx.x >> 5);
+        const int64_t n = ntb * 16 + 8 * ch;
+        if (m < a.M && n < a.N) *reinterpret_cast<u32x4*>(a.C + m * a.ldc + n) = v;
     }
 }
 }  // namespace
 
-W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16, int64_t ldq) {
+W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16, int64_t ldq, bool c16) {
     W4a8Plan p;
     p.MI = M <= 16 ? 1 : 2;
     const int64_t KTT = g.Kp / 128;
@@ -513,10 +535,11 @@ W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16, int64_t ldq) {
     // The ring kernel, when its 128 x 256 tiles fill the chip at least once
     // and its constraints hold: no K tail, one group per row (at most 131072
     // k, so that the integer sums fit in 32 bits) or groups of 64 to 256 k,
-    // 16-byte aligned activation rows, and per-tile offsets below 2^31.
+    // 16-byte aligned activation and output rows, and per-tile offsets below
+    // 2^31.
     const int64_t m_tiles = (M + 127) / 128, n_blocks = (g.Np / 16 + 15) / 16;
     const bool groups_ok = g.Kg == 1 ? g.Kp <= 131072 : (g.Ge >= 64 && g.Ge <= 256);
-    if (qa16 && g.Kp == g.K && groups_ok && m_tiles * n_blocks >= kCUs && m_tiles * n_blocks <= (1 << 22) &&
+    if (qa16 && c16 && g.Kp == g.K && groups_ok && m_tiles * n_blocks >= kCUs && m_tiles * n_blocks <= (1 << 22) &&
         128 * ldq + g.K < ((int64_t)1 << 31) && 16 * (g.Kp / 128) * 1024 < ((int64_t)1 << 31)) {
         p.ring = g.Kg == 1 ? 0 : (int)(g.Ge / 64);
         p.m_tiles = m_tiles;
