@@ -18,7 +18,9 @@ namespace w4a16 {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-constexpr int kA8DecodeChunk = 4;  // k-tiles per K chunk (and register stages) for up to 16 rows
+constexpr int kA8DecodeChunk = 4;      // k-tiles per K chunk (and register stages) for up to 16 rows
+constexpr int64_t kA8RingMinM = 64;     // the ring kernel from this many rows ...
+constexpr int64_t kA8RingMinTiles = 48; // ... and this many 128 x 256 tiles
 
 // ---------------------------------------------------------------- quantiser
 
@@ -532,14 +534,16 @@ W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16, int64_t ldq, bool c1
     p.ksplit = (KTT + p.kc - 1) / p.kc;
     p.partial_bytes = p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)g.Np * sizeof(float) : 0;
 
-    // The ring kernel, when its 128 x 256 tiles fill the chip at least once
-    // and its constraints hold: no K tail, one group per row (at most 131072
+    // The ring kernel when it has enough tiles of 128 x 256 (at M >= 64 and 48
+    // tiles it beat this kernel on every decode-layer shape measured, by up
+    // to 4x at a few hundred rows) and its constraints hold: no K tail, one
+    // group per row (at most 131072
     // k, so that the integer sums fit in 32 bits) or groups of 64 to 256 k,
     // 16-byte aligned activation and output rows, and per-tile offsets below
     // 2^31.
     const int64_t m_tiles = (M + 127) / 128, n_blocks = (g.Np / 16 + 15) / 16;
     const bool groups_ok = g.Kg == 1 ? g.Kp <= 131072 : (g.Ge >= 64 && g.Ge <= 256);
-    if (qa16 && c16 && g.Kp == g.K && groups_ok && m_tiles * n_blocks >= kCUs && m_tiles * n_blocks <= (1 << 22) &&
+    if (qa16 && c16 && g.Kp == g.K && groups_ok && M >= kA8RingMinM && m_tiles * n_blocks >= kA8RingMinTiles && m_tiles * n_blocks <= (1 << 22) &&
         128 * ldq + g.K < ((int64_t)1 << 31) && 16 * (g.Kp / 128) * 1024 < ((int64_t)1 << 31)) {
         p.ring = g.Kg == 1 ? 0 : (int)(g.Ge / 64);
         p.m_tiles = m_tiles;
