@@ -308,7 +308,11 @@ w4a16_status w4a8_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_
     Geometry g;
     w4a16_status st = make_geometry(N, K, group_size, W4A16_UINT4B8, &g);
     if (st != W4A16_OK) return st;
-    *out_bytes = M > 0 ? plan_w4a8(M, g).partial_bytes : 0;
+    // The larger of the two kernels' needs: the call picks the ring kernel
+    // only for 16-byte aligned activation and output rows.
+    const size_t reg = M > 0 ? plan_w4a8(M, g).partial_bytes : 0;
+    const size_t ring = M > 0 ? plan_w4a8(M, g, true, K, true).partial_bytes : 0;
+    *out_bytes = reg > ring ? reg : ring;
     return W4A16_OK;
 }
 

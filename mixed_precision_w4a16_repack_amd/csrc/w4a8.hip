@@ -20,7 +20,9 @@ namespace {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kA8DecodeChunk = 4;      // k-tiles per K chunk (and register stages) for up to 16 rows
 constexpr int64_t kA8RingMinM = 64;     // the ring kernel from this many rows ...
-constexpr int64_t kA8RingMinTiles = 48; // ... and this many 128 x 256 tiles
+constexpr int64_t kA8RingMinTiles = 48; // ... and this many 128 x 256 tiles or
+constexpr int64_t kA8RingMinK = 8192;   // ... this long a K (split into chunks)
+constexpr int64_t kA8RingMinChunk = 8;  // k-tiles per K chunk of the ring kernel, at least
 
 // ---------------------------------------------------------------- quantiser
 
@@ -304,7 +306,10 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     const int64_t ty = lin / a.n_blocks, tx = lin - ty * a.n_blocks;
     const int64_t m0 = ty * 128;
     const int64_t ntb = tx * 16;  // first n-tile of the workgroup
-    const int64_t steps = a.KTT;
+    // K chunk blockIdx.y: k-tiles [kt0, kt0 + steps) (one chunk unless the
+    // tiles are too few for the chip; chunks start at group boundaries).
+    const int64_t kt0 = (int64_t)blockIdx.y * a.kc;
+    const int64_t steps = (a.KTT - kt0 < a.kc ? a.KTT - kt0 : a.kc);
 
     // The workgroup's operands as buffers based at its tile: rows
     // [mb, mb + mr) of the activation codes (rows past M clamp to M - 1) and
@@ -344,9 +349,10 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     // tile h of the wave.
     auto issue = [&](int64_t st, int h, unsigned char* abuf, unsigned char* bbuf) {
         const bool live = st < steps;
-        load_lds16(rsrc(abase, a_bytes, live), abuf + (2 * wave + h) * 1024, a_off, (uint32_t)(st * 128 + 64 * h));
+        load_lds16(rsrc(abase, a_bytes, live), abuf + (2 * wave + h) * 1024, a_off,
+                   (uint32_t)((kt0 + st) * 128 + 64 * h));
         load_lds16(rsrc(cbase, c_bytes, live), bbuf + (2 * wave + h) * 1024, lane16,
-                   (uint32_t)((b_tile[h] * a.KTT + st) * 1024));
+                   (uint32_t)((b_tile[h] * a.KTT + kt0 + st) * 1024));
     };
     // The scales of the groups that end in step st (GP = 4: only odd steps
     // end a group), for the wave's four columns.
@@ -356,7 +362,8 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
         constexpr int NG = GP == 1 ? 2 : 1;
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
-            const int64_t g = GP == 1 ? 2 * st + q : (GP == 2 ? st : st / 2);
+            const int64_t kt = kt0 + st;
+            const int64_t g = GP == 1 ? 2 * kt + q : (GP == 2 ? kt : kt / 2);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const uint32_t so = (uint32_t)(((nt_ld(j) - ntb) * a.Kg + g) * 16);
@@ -471,6 +478,30 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     if (st + 2 < steps) step(st + 2, 2, a2, b2, sb2, sb0, a1, b1);
     wait_vmcnt<0>();
 
+    // With K in chunks: this chunk's fp32 results (the row scale and bias
+    // follow in w4a8_reduce_kernel).
+    if (a.partials != nullptr) {
+        if (GP == 0) mfma_i8_drain();
+        const int64_t ldp = a.NT * 16;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int64_t nt = ntb + 4 * wn + j;
+            if (nt >= a.NT) continue;
+            const int64_t n = nt * 16 + r;
+            const float sc = GP == 0 ? 0.0625f * act_to_float<DT>(a.scales[nt * a.Kg * 16 + r]) : 0.f;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int64_t m = m0 + 64 * wm + 16 * i + 4 * g4 + jj;
+                    if (m >= a.M || n >= a.N) continue;
+                    a.partials[((int64_t)blockIdx.y * a.M + m) * ldp + n] =
+                        GP == 0 ? sc * (float)acc[i][j][jj] : accf[GP > 0 ? i : 0][GP > 0 ? j : 0][jj];
+                }
+        }
+        return;
+    }
+
     // Epilogue. The tile goes through LDS so that C is written in whole
     // 16-byte row chunks: once every wave's loads have landed (the steps past
     // K load zeros into the stages), rows 32 q .. 32 q + 31 of the tile go to
@@ -534,22 +565,33 @@ W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16, int64_t ldq, bool c1
     p.ksplit = (KTT + p.kc - 1) / p.kc;
     p.partial_bytes = p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)g.Np * sizeof(float) : 0;
 
-    // The ring kernel when it has enough tiles of 128 x 256 (at M >= 64 and 48
-    // tiles it beat this kernel on every decode-layer shape measured, by up
-    // to 4x at a few hundred rows) and its constraints hold: no K tail, one
-    // group per row (at most 131072
+    // The ring kernel from 64 rows when it has 48 tiles of 128 x 256 or K is
+    // long enough to split well (on the decode-layer shapes measured it beat
+    // this kernel there, by up to 4x at a few hundred rows) and its
+    // constraints hold: no K tail, one group per row (at most 131072
     // k, so that the integer sums fit in 32 bits) or groups of 64 to 256 k,
     // 16-byte aligned activation and output rows, and per-tile offsets below
     // 2^31.
     const int64_t m_tiles = (M + 127) / 128, n_blocks = (g.Np / 16 + 15) / 16;
     const bool groups_ok = g.Kg == 1 ? g.Kp <= 131072 : (g.Ge >= 64 && g.Ge <= 256);
-    if (qa16 && c16 && g.Kp == g.K && groups_ok && M >= kA8RingMinM && m_tiles * n_blocks >= kA8RingMinTiles && m_tiles * n_blocks <= (1 << 22) &&
-        128 * ldq + g.K < ((int64_t)1 << 31) && 16 * (g.Kp / 128) * 1024 < ((int64_t)1 << 31)) {
+    const int64_t rtiles = m_tiles * n_blocks;
+    const bool big_enough = M >= kA8RingMinM && (rtiles >= kA8RingMinTiles || g.K >= kA8RingMinK);
+    const bool offsets_ok = rtiles <= (1 << 22) && 128 * ldq + g.K < ((int64_t)1 << 31) &&
+                            16 * (g.Kp / 128) * 1024 < ((int64_t)1 << 31);
+    if (qa16 && c16 && g.Kp == g.K && groups_ok && big_enough && offsets_ok) {
         p.ring = g.Kg == 1 ? 0 : (int)(g.Ge / 64);
         p.m_tiles = m_tiles;
         p.n_blocks = n_blocks;
-        p.ksplit = 1;
-        p.partial_bytes = 0;
+        // Fewer tiles than CUs: K in chunks of at least kA8RingMinChunk k-tiles
+        // (whole groups of 256 k), up to about one workgroup per CU.
+        int64_t ks = (kCUs + rtiles - 1) / rtiles;
+        if (ks > KTT / kA8RingMinChunk) ks = KTT / kA8RingMinChunk;
+        if (ks < 1) ks = 1;
+        int64_t kc = (KTT + ks - 1) / ks;
+        if (p.ring == 4 && (kc & 1)) ++kc;
+        p.kc = kc;
+        p.ksplit = (KTT + kc - 1) / kc;
+        p.partial_bytes = p.ksplit > 1 ? (size_t)p.ksplit * (size_t)M * (size_t)g.Np * sizeof(float) : 0;
     }
     return p;
 }
@@ -587,7 +629,7 @@ hipError_t launch_w4a8(const int8_t* qa, const float* xs, int64_t M, int64_t ldq
     a.partials = p.ksplit > 1 ? static_cast<float*>(workspace) : nullptr;
     a.n_blocks = p.n_blocks;
     if (p.ring >= 0) {
-        const dim3 rgrid((unsigned)(p.m_tiles * p.n_blocks));
+        const dim3 rgrid((unsigned)(p.m_tiles * p.n_blocks), (unsigned)p.ksplit);
 #define W4A8_RING(D, G) hipLaunchKernelGGL((w4a8_ring_kernel<D, G>), rgrid, dim3(512), 0, stream, a)
         if (dtype == 0) {
             if (p.ring == 0) W4A8_RING(0, 0);
@@ -601,15 +643,15 @@ hipError_t launch_w4a8(const int8_t* qa, const float* xs, int64_t M, int64_t ldq
             else W4A8_RING(1, 4);
         }
 #undef W4A8_RING
-        return hipGetLastError();
-    }
-    const dim3 grid((unsigned)p.blocks_n, (unsigned)p.blocks_m, (unsigned)p.ksplit);
-    if (dtype == 0) {
-        if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<0, 1, kA8DecodeChunk>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((w4a8_kernel<0, 2, 2>), grid, dim3(256), 0, stream, a);
     } else {
-        if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<1, 1, kA8DecodeChunk>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((w4a8_kernel<1, 2, 2>), grid, dim3(256), 0, stream, a);
+        const dim3 grid((unsigned)p.blocks_n, (unsigned)p.blocks_m, (unsigned)p.ksplit);
+        if (dtype == 0) {
+            if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<0, 1, kA8DecodeChunk>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((w4a8_kernel<0, 2, 2>), grid, dim3(256), 0, stream, a);
+        } else {
+            if (p.MI == 1) hipLaunchKernelGGL((w4a8_kernel<1, 1, kA8DecodeChunk>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((w4a8_kernel<1, 2, 2>), grid, dim3(256), 0, stream, a);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.ksplit == 1) return e;

@@ -828,7 +828,10 @@ W4A8_GEMM = [
     (1100, 14336, 2048, 128, "bf16"),
     (2048, 4096, 14336, 256, "f16"),
     (1999, 4232, 2944, -1, "f16"),
-    (300, 14336, 2048, 128, "f16"),  # fewer ring tiles than CUs, ragged M
+    # Fewer ring tiles than CUs: K in chunks (fp32 partials, second kernel).
+    (300, 14336, 2048, 128, "f16"),
+    (384, 4096, 14336, 256, "bf16"),
+    (200, 14336, 4096, -1, "bf16"),
 ]
 
 
@@ -863,7 +866,7 @@ def test_w4a8_zero_row_gives_bias_and_no_store_past_n():
 
 
 @pytest.mark.parametrize("M,N,K,G", [(2048, 4096, 4096, 128), (1100, 8200, 2048, 256), (2000, 4096, 4096, -1),
-                                     (2048, 4096, 2048, 64), (320, 14336, 4096, 128)])
+                                     (2048, 4096, 2048, 64), (640, 14336, 4096, 128)])
 def test_w4a8_ring_equals_register_kernel(M, N, K, G):
     """The tiled ring kernel (16-byte aligned codes, ldq % 16 == 0) and the
     register kernel (ldq % 16 == 8) form the same exact integer group sums
