@@ -267,8 +267,12 @@ w4a16_status w4a8_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_
  *   workspace, workspace_bytes  at least w4a8_workspace_size() bytes (may
  *            be NULL when that is 0); calls that share one must be ordered
  * The integer group sums are exact (int8 MFMA, int32 accumulation); each
- * group's sum is scaled in fp32. Shapes as for w4a16_repack. M == 0 is a
- * no-op. W4A16_ERR_SIZE if the workspace is too small. */
+ * group's sum is scaled in fp32. Shapes as for w4a16_repack. qa must be
+ * 8-byte aligned with ldq % 8 == 0. At M >= 64, with qa 16-byte aligned,
+ * ldq % 16 == 0, C 16-byte aligned and ldc % 8 == 0, a tiled kernel runs;
+ * other calls take a kernel that works in registers. Both give the same
+ * result when neither splits K. M == 0 is a no-op. W4A16_ERR_SIZE if the
+ * workspace is too small. */
 w4a16_status w4a8_gemm(const int8_t *qa, const float *xs, int64_t M, int64_t ldq, const void *packed, int64_t N,
                        int64_t K, int32_t group_size, int32_t dtype, const void *bias, void *C, int64_t ldc,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
