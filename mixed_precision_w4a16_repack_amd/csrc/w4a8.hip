@@ -70,6 +70,54 @@ __global__ __launch_bounds__(256) void a8_quant_kernel(const uint16_t* __restric
     }
 }
 
+// The same quantiser with the row held in registers between its two
+// passes, so that it is read from memory once: CPT 16-byte chunks per
+// thread, for K <= 8 * 256 * CPT.
+template <int DT, int CPT>
+__global__ __launch_bounds__(256) void a8_quant_reg_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t K,
+                                                           int8_t* __restrict__ q, int64_t ldq, float* __restrict__ xs) {
+    const int64_t m = blockIdx.x;
+    const uint16_t* row = A + m * lda;
+    const int64_t chunks = K / 8;
+    u32x4 v[CPT];
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < CPT; ++t) {
+        const int64_t c = threadIdx.x + 256 * t;
+        v[t] = c < chunks ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            amax = fmaxf(amax, fabsf(act_to_float<DT>((uint16_t)(v[t][e] & 0xFFFFu))));
+            amax = fmaxf(amax, fabsf(act_to_float<DT>((uint16_t)(v[t][e] >> 16))));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) xs[m] = s;
+    int8_t* qrow = q + m * ldq;
+#pragma unroll
+    for (int t = 0; t < CPT; ++t) {
+        const int64_t c = threadIdx.x + 256 * t;
+        if (c >= chunks) break;
+        uint32_t out[2] = {0u, 0u};
+        if (amax > 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t bits = (uint16_t)(e & 1 ? v[t][e >> 1] >> 16 : v[t][e >> 1] & 0xFFFFu);
+                const float r = __builtin_rintf(act_to_float<DT>(bits) / s);
+                const int iv = r > 127.0f ? 127 : (r < -127.0f ? -127 : (int)r);
+                out[e >> 2] |= ((uint32_t)iv & 0xFFu) << (8 * (e & 3));
+            }
+        }
+        *reinterpret_cast<uint2*>(qrow + 8 * c) = make_uint2(out[0], out[1]);
+    }
+}
+
 // ---------------------------------------------------------------- GEMM
 
 struct A8Args {
@@ -599,8 +647,27 @@ W4a8Plan plan_w4a8(int64_t M, const Geometry& g, bool qa16, int64_t ldq, bool c1
 hipError_t launch_a8_quant(const void* A, int64_t M, int64_t K, int64_t lda, int dtype, int8_t* qa, int64_t ldq,
                            float* xs, hipStream_t stream) {
     const uint16_t* a = static_cast<const uint16_t*>(A);
-    if (dtype == 0) hipLaunchKernelGGL((a8_quant_kernel<0>), dim3((unsigned)M), dim3(256), 0, stream, a, lda, K, qa, ldq, xs);
-    else hipLaunchKernelGGL((a8_quant_kernel<1>), dim3((unsigned)M), dim3(256), 0, stream, a, lda, K, qa, ldq, xs);
+    const int64_t cpt = (K / 8 + 255) / 256;  // 16-byte chunks per thread
+    const dim3 grid((unsigned)M), block(256);
+#define A8Q(D, C) hipLaunchKernelGGL((a8_quant_reg_kernel<D, C>), grid, block, 0, stream, a, lda, K, qa, ldq, xs)
+    if (cpt <= 8) {
+        if (dtype == 0) {
+            if (cpt <= 1) A8Q(0, 1);
+            else if (cpt <= 2) A8Q(0, 2);
+            else if (cpt <= 4) A8Q(0, 4);
+            else A8Q(0, 8);
+        } else {
+            if (cpt <= 1) A8Q(1, 1);
+            else if (cpt <= 2) A8Q(1, 2);
+            else if (cpt <= 4) A8Q(1, 4);
+            else A8Q(1, 8);
+        }
+    } else if (dtype == 0) {
+        hipLaunchKernelGGL((a8_quant_kernel<0>), grid, block, 0, stream, a, lda, K, qa, ldq, xs);
+    } else {
+        hipLaunchKernelGGL((a8_quant_kernel<1>), grid, block, 0, stream, a, lda, K, qa, ldq, xs);
+    }
+#undef A8Q
     return hipGetLastError();
 }
 

@@ -795,7 +795,8 @@ def test_weights_beyond_2gib(M, path):
 # ------------------------------------------------------------------ W4A8
 
 
-A8_QUANT = [(1, 4096, "f16", 0), (16, 14336, "bf16", 0), (37, 2880, "bf16", 64), (300, 1216, "f16", 8)]
+A8_QUANT = [(1, 4096, "f16", 0), (16, 14336, "bf16", 0), (37, 2880, "bf16", 64), (300, 1216, "f16", 8),
+            (3, 20480, "bf16", 16)]  # the last: more than 8 chunks per thread, two reads of the row
 
 
 @pytest.mark.parametrize("M,K,dtype,pad", A8_QUANT, ids=[f"{c[0]}x{c[1]}{c[2]}p{c[3]}" for c in A8_QUANT])
