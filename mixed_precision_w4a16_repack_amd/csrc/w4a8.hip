@@ -446,7 +446,11 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
         for (int j = 0; j < NJ; ++j) raw[j] = *reinterpret_cast<const u32x4*>(bbuf + (4 * wn + j) * 1024 + lane16);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            // The loads stay at the start of their slice (measured 1-2% faster
+            // than letting the scheduler move them).
+            __builtin_amdgcn_sched_barrier(0);
             issue(st + 3, h, nabuf, nbbuf);
+            __builtin_amdgcn_sched_barrier(0);
             // Weight operands of slice h: words 2h and 2h + 1 (k = 64 h + 8 g4
             // and 64 h + 32 + 8 g4), low nibbles then high nibbles of each.
             i32x4 B[NJ];
