@@ -7,9 +7,15 @@
 // int8 rows are multiplied by the int4 weights (uint4b8, zero 8) with the row
 // scale and the weight's group scales:
 //     C[m, n] = xs[m] * sum_g s[n, g] * sum_{k in g} qa[m, k] * (q[n, k] - 8)
-// The integer sums run on v_mfma_i32_16x16x32_i8 and are exact; the group
+// The integer sums run on the int8 matrix cores and are exact; the group
 // scale is applied to each group's integer sum in fp32, the row scale and
-// bias at the end, and C is rounded once.
+// bias at the end, and C is rounded once. Two GEMM kernels:
+//  * w4a8_ring_kernel (M >= 64 with enough tiles or a long K): 128 x 256
+//    tiles, operands staged through a four-stage LDS ring,
+//    v_mfma_i32_16x16x64_i8 on signed weight bytes 16 (q - 8);
+//  * w4a8_kernel (the rest, decode included): operands straight into
+//    registers, v_mfma_i32_16x16x32_i8 on unsigned codes with a row-sum
+//    correction, K split across workgroups.
 #include "device_common.h"
 #include "internal.h"
 #include "lds_stage.h"
