@@ -323,3 +323,7 @@ def test_w4a8_workspace_size():
     assert w4.w4a8_workspace_size(1, 4096, 4096, 128) > 0
     assert w4.w4a8_workspace_size(4096, 4096, 4096, 128) == 0
     assert w4.w4a8_workspace_size(0, 4096, 4096, 128) == 0
+    # 256 x 4096 x 14336: the tiled kernel splits K into 8 chunks of 14
+    # k-tiles (32 tiles, about one workgroup per CU), more than the register
+    # kernel's 4; the size covers the larger.
+    assert w4.w4a8_workspace_size(256, 4096, 14336, 128) == 8 * 256 * 4096 * 4
