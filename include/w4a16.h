@@ -247,7 +247,11 @@ w4a16_status w4a16_gemm_dense(const void *A, int64_t M, int64_t lda, const void 
  *   qa[m, k]  = rint(A[m, k] / xs[m])         (round half to even; always in
  *               [-127, 127]); a row of zeros gets xs[m] = 0 and codes 0
  *   A   [M, lda] act dtype, lda >= K, 16-byte aligned with lda % 8 == 0
- *   qa  [M, ldq] int8, ldq >= K, 8-byte aligned with ldq % 8 == 0
+ *   qa  [M, ldq] int8, ldq >= K, 8-byte aligned with ldq % 8 == 0. Each
+ *       run of 8 codes (k = 8c .. 8c + 7) is stored in the order
+ *       k = 8c + 0, 4, 1, 5, 2, 6, 3, 7: the order in which a packed weight
+ *       word gives its codes to the int8 MFMA, so w4a8_gemm uses them as
+ *       stored. Codes from elsewhere must be stored the same way.
  *   xs  [M] fp32
  * K % 8 == 0. M == 0 is a no-op. */
 w4a16_status w4a8_quantize(const void *A, int64_t M, int64_t K, int64_t lda, int32_t dtype, int8_t *qa, int64_t ldq,

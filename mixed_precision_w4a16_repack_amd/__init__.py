@@ -284,7 +284,10 @@ def dequant(packed: torch.Tensor, N: int, K: int, group_size: int, qtype: int, d
 
 
 def quantize_a8(A: torch.Tensor, out: tuple[torch.Tensor, torch.Tensor] | None = None):
-    """Per-token symmetric int8 quantisation: A [M, K] -> (qa [M, K] int8, xs [M] fp32)."""
+    """Per-token symmetric int8 quantisation: A [M, K] -> (qa [M, K] int8, xs [M] fp32).
+
+    Each run of 8 codes of qa is stored in the order 0, 4, 1, 5, 2, 6, 3, 7
+    (the packed weight's code order, which ``gemm_w4a8`` expects)."""
     _need_cuda("A", A, (torch.float16, torch.bfloat16))
     if A.dim() != 2 or A.stride(1) != 1:
         raise ValueError("A must be 2-D with unit column stride")

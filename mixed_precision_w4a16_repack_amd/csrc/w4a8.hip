@@ -36,6 +36,9 @@ constexpr int64_t kA8RingMinChunk = 8;  // k-tiles per K chunk of the ring kerne
 // (IEEE division); each value becomes rint(x / scale) (half to even),
 // which stays within [-127, 127] because |x| <= max |x|; a row of zeros
 // gets scale 0 and codes 0. K % 8 == 0: each thread handles 8-element chunks.
+// Each chunk of 8 codes is stored in the order 0,4,1,5,2,6,3,7: the order in
+// which a packed weight word's two nibble masks give its codes, so that the
+// GEMM kernels use the bytes as they are.
 template <int DT>
 __global__ __launch_bounds__(256) void a8_quant_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t K,
                                                        int8_t* __restrict__ q, int64_t ldq, float* __restrict__ xs) {
@@ -69,7 +72,8 @@ __global__ __launch_bounds__(256) void a8_quant_kernel(const uint16_t* __restric
                 const uint16_t bits = (uint16_t)(e & 1 ? v[e >> 1] >> 16 : v[e >> 1] & 0xFFFFu);
                 const float t = __builtin_rintf(act_to_float<DT>(bits) / s);
                 const int iv = t > 127.0f ? 127 : (t < -127.0f ? -127 : (int)t);
-                out[e >> 2] |= ((uint32_t)iv & 0xFFu) << (8 * (e & 3));
+                const int pos = e < 4 ? 2 * e : 2 * e - 7;  // pair order 0,4,1,5,2,6,3,7
+                out[pos >> 2] |= ((uint32_t)iv & 0xFFu) << (8 * (pos & 3));
             }
         }
         *reinterpret_cast<uint2*>(qrow + 8 * c) = make_uint2(out[0], out[1]);
@@ -117,7 +121,8 @@ __global__ __launch_bounds__(256) void a8_quant_reg_kernel(const uint16_t* __res
                 const uint16_t bits = (uint16_t)(e & 1 ? v[t][e >> 1] >> 16 : v[t][e >> 1] & 0xFFFFu);
                 const float r = __builtin_rintf(act_to_float<DT>(bits) / s);
                 const int iv = r > 127.0f ? 127 : (r < -127.0f ? -127 : (int)r);
-                out[e >> 2] |= ((uint32_t)iv & 0xFFu) << (8 * (e & 3));
+                const int pos = e < 4 ? 2 * e : 2 * e - 7;  // pair order 0,4,1,5,2,6,3,7
+                out[pos >> 2] |= ((uint32_t)iv & 0xFFu) << (8 * (pos & 3));
             }
         }
         *reinterpret_cast<uint2*>(qrow + 8 * c) = make_uint2(out[0], out[1]);
@@ -154,12 +159,10 @@ __device__ __forceinline__ void mfma_i8_drain() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Bytes of one activation chunk (k .. k+7 of a row) in the order the packed
-// weight word gives its codes after the nibble split below: 0,4,1,5 | 2,6,3,7.
+// One activation chunk (k .. k+7 of a row, stored in pair order by the
+// quantiser) as the 8 bytes of an MFMA operand.
 __device__ __forceinline__ int64_t a_operand(uint2 v) {
-    const uint32_t lo = __builtin_amdgcn_perm(v.y, v.x, 0x05010400u);
-    const uint32_t hi = __builtin_amdgcn_perm(v.y, v.x, 0x07030602u);
-    return (int64_t)(((uint64_t)hi << 32) | lo);
+    return (int64_t)(((uint64_t)v.y << 32) | v.x);
 }
 
 // The eight codes of a packed word (pair order: code i at 4*(i/2) + 16*(i%2))
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(256) void w4a8_reduce_kernel(const float* __restric
 //    sign bit of each nibble flipped, a nibble is the 4-bit two's complement
 //    of q - 8, and placed in the high half of a byte it reads as 16 (q - 8).
 //    The low nibbles (codes 0, 4, 1, 5 in pair order) move up by a shift;
-//    two v_perm put each 8-byte activation chunk in the same order.
+//    the quantiser stores each 8-byte activation chunk in the same order.
 //  * Integer sums are exact (|16 (q - 8) qa| <= 16256; a chunk of at most
 //    131072 k stays below 2^31). GP = 0: one group per row, the scale is
 //    applied in the epilogue. GP > 0: a group spans GP slices of 64 k; at
@@ -486,11 +489,8 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const uint64_t v0 = av[h][i][0], v1 = av[h][i][1];
-                i32x4 A;
-                A[0] = (int32_t)__builtin_amdgcn_perm((uint32_t)(v0 >> 32), (uint32_t)v0, 0x05010400u);
-                A[1] = (int32_t)__builtin_amdgcn_perm((uint32_t)(v0 >> 32), (uint32_t)v0, 0x07030602u);
-                A[2] = (int32_t)__builtin_amdgcn_perm((uint32_t)(v1 >> 32), (uint32_t)v1, 0x05010400u);
-                A[3] = (int32_t)__builtin_amdgcn_perm((uint32_t)(v1 >> 32), (uint32_t)v1, 0x07030602u);
+                const i32x4 A = {(int32_t)(uint32_t)v0, (int32_t)(uint32_t)(v0 >> 32), (int32_t)(uint32_t)v1,
+                                 (int32_t)(uint32_t)(v1 >> 32)};
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B[j], start ? zero4 : acc[i][j], 0, 0, 0);

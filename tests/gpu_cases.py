@@ -54,3 +54,11 @@ def expected_codes_scales_zeros(case: wi.Case):
 
 def rel_err_rows(C_gpu: torch.Tensor, C_ref: np.ndarray, rows) -> float:
     return oracle.rel_err(C_gpu.cpu()[torch.as_tensor(rows)], C_ref)
+
+
+def pair_order_codes(q: np.ndarray) -> np.ndarray:
+    """Row-major int8 codes [..., K] in the stored order of w4a8_quantize:
+    each run of 8 columns as 0, 4, 1, 5, 2, 6, 3, 7 (K % 8 == 0)."""
+    shape = q.shape
+    r = q.reshape(shape[:-1] + (shape[-1] // 8, 8))
+    return r[..., [0, 4, 1, 5, 2, 6, 3, 7]].reshape(shape)
