@@ -883,3 +883,23 @@ def test_w4a8_ring_equals_register_kernel(M, N, K, G):
     C_reg = w4.gemm_w4a8(padded[:, :K], xs, packed, N, K, G, torch.bfloat16, bias=bias)
     torch.cuda.synchronize()
     assert torch.equal(C_ring, C_reg)
+
+
+def test_w4a8_unaligned_output_and_no_bias():
+    """C rows that are not 16-byte multiples (ldc % 8 != 0) take the register
+    kernel; bias None on the tiled kernel. Same exact sums, same results."""
+    M, N, K, G = 2048, 4096, 4096, 64
+    case = _case(55, M, N, K, G, UINT4B8, "f16", with_bias=False)
+    wq, ws, _, A, _ = to_dev(case)
+    packed = w4.repack(wq, ws, None, G, UINT4B8)
+    qa, xs = w4.quantize_a8(A)
+    C_ring = w4.gemm_w4a8(qa, xs, packed, N, K, G, torch.float16)
+    big = torch.full((M, N + 4), 5.0, dtype=torch.float16, device=DEV)
+    C_reg = w4.gemm_w4a8(qa, xs, packed, N, K, G, torch.float16, out=big[:, :N])
+    torch.cuda.synchronize()
+    assert torch.equal(C_ring, C_reg)
+    assert torch.all(big[:, N:] == 5.0)
+    rows = sample_rows(M)
+    q_ref, xs_ref = oracle.quant_rows_a8(case.A[torch.as_tensor(rows)])
+    ref = oracle.gemm_w4a8(q_ref, xs_ref, case.weight_packed, case.weight_scale, G, None)
+    assert rel_err_rows(C_ring, ref, rows) <= oracle.TOLERANCE["f16"]
