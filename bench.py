@@ -508,7 +508,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the W4A16 path here is a single-GPU kernel; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(the W4A16 path here is a single-GPU kernel; across GPUs the weight would be split along N or K)",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
