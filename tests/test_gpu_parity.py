@@ -834,6 +834,9 @@ W4A8_GEMM = [
     (300, 14336, 2048, 128, "f16"),
     (384, 4096, 14336, 256, "bf16"),
     (200, 14336, 4096, -1, "bf16"),
+    # The largest prefill shapes of the bench, sampled rows.
+    (8192, 14336, 4096, -1, "bf16"),
+    (8192, 4096, 14336, 256, "bf16"),
 ]
 
 
