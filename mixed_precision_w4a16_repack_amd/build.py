@@ -4,6 +4,9 @@
 
 Each source compiles to an object under ``_build/`` (in parallel), then one
 shared library is linked next to this file, where the binding loads it.
+The sources with staged GEMM kernels are also compiled to gfx950 assembly,
+and ``wait_check`` verifies their hand-counted memory waits against it; a
+mismatch fails the build.
 """
 
 from __future__ import annotations
@@ -19,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "w4a16")
 LIB = os.path.join(PKG, "libw4a16.so")
 SOURCES = ["w4a16_api.cpp", "repack.hip", "skinny.hip", "mfma.hip", "dense.hip", "w4a8.hip"]
+STAGED = ["mfma.hip", "w4a8.hip"]  # kernels with hand-counted waits (wait_check)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -50,11 +54,41 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _assembly(src: str) -> str:
+    out = os.path.join(BUILD, os.path.splitext(src)[0] + ".gfx950.s")
+    cmd = [HIPCC, "-x", "hip", *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{res.stdout}{res.stderr}")
+    return out
+
+
+def check_waits(asm_paths) -> None:
+    """Fails when a staged kernel's hand-counted wait does not match the
+    vector-memory instructions the compiler emitted (see wait_check)."""
+    from . import wait_check
+
+    problems, kernels = [], 0
+    for p in asm_paths:
+        with open(p) as f:
+            n, probs = wait_check.check_asm(f.read())
+        kernels += n
+        problems += probs
+    if kernels == 0:
+        raise RuntimeError("wait check: no staged kernel found in the assembly")
+    if problems:
+        raise RuntimeError("wait check failed:\n" + "\n".join(problems))
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libw4a16.so. Returns the library path."""
+    """Compile every source, check the staged kernels' waits and link
+    libw4a16.so. Returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        asm = [ex.submit(_assembly, s) for s in STAGED]
         objs = list(ex.map(_compile, SOURCES))
+        asm_paths = [f.result() for f in asm]
+    check_waits(asm_paths)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lhipblaslt"]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -108,6 +108,50 @@ struct Dequant<1> {
     }
 };
 
+// Offset-corrected B operand of the tiled kernels: code q becomes the exact
+// act value 1 + q/16, the nibble OR-ed into the top four mantissa bits of 1.0
+// (fp16 bits 6..9 of each half, bf16 bits 3..6). Pair p of a word (codes 2p
+// and 2p+1 at bits 4p and 16+4p) moves there with one shift by kPos - 4p and
+// one v_and_or_b32. A product sum P = sum A*(1 + q/16) then carries the
+// offset sum A with weight 1 against code steps of 1/16, so
+// sum A*(q - z) = 16*P - (16 + z)*S (S = sum A) cancels only a few bits even
+// when sum A grows with K (the magic 1024 + q of the skinny kernels would
+// carry the offset 1024 times one code step).
+template <int DT>
+struct TopNibble {
+    static constexpr int kPos = DT == 0 ? 6 : 3;  // lowest bit of the nibble in each half
+    static constexpr uint32_t kMask = (0xFu << kPos) * 0x00010001u;
+    static constexpr uint32_t kOne = DT == 0 ? 0x3C003C00u : 0x3F803F80u;  // 1.0 in both halves
+};
+
+// Word w shifted so that its pair P lands at the nibble position.
+template <int DT, int P>
+__device__ __forceinline__ uint32_t top_pair_shift(uint32_t w) {
+    constexpr int sh = TopNibble<DT>::kPos - 4 * P;
+    if constexpr (sh >= 0) {
+        return w << sh;
+    } else {
+        return w >> (-sh);
+    }
+}
+
+// The same shift of two consecutive words held as one 64-bit value (word 0
+// low): one v_lshlrev_b64 / v_lshrrev_b64 serves both. The bits that cross
+// between the halves land outside the nibble masks.
+template <int DT, int P>
+__device__ __forceinline__ uint64_t top_pair_shift64(uint64_t x) {
+    constexpr int sh = TopNibble<DT>::kPos - 4 * P;
+    uint64_t y;
+    if constexpr (sh > 0) {
+        asm("v_lshlrev_b64 %0, %2, %1" : "=v"(y) : "v"(x), "n"(sh));
+    } else if constexpr (sh < 0) {
+        asm("v_lshrrev_b64 %0, %2, %1" : "=v"(y) : "v"(x), "n"(-sh));
+    } else {
+        y = x;
+    }
+    return y;
+}
+
 // acc += A_frag (16 rows x 32 k) * B_frag (32 k x 16 cols), fp32 accumulate.
 // Lane l holds A[l%16][8(l/16) .. +7] and B[8(l/16) .. +7][l%16]; the result
 // lane l holds rows 4(l/16) .. +3 of column l%16.

@@ -12,8 +12,9 @@
 //    workgroup per CU, for one group per row or groups of 128 k or more.
 //    Activation and weight tiles go from HBM/L2 straight into a three-stage
 //    LDS ring (direct 16-byte buffer loads), and the weights are
-//    dequantised offset-corrected: exact magic values m + q into the MFMA,
-//    the scale applied once per group.
+//    dequantised offset-corrected: exact values 1 + q/16 into the MFMA
+//    (TopNibble), the offset removed with row sums and the scale applied
+//    once per group.
 //  * mfma_lds_kernel: the other tile shapes (64-column tiles at small and
 //    medium M) and groups of 32 or 64 k (scale first, per weight, as the
 //    pages do); activation tiles go straight into two LDS buffers, the
@@ -105,7 +106,7 @@ __device__ __forceinline__ TileBufs tile_bufs(const MfmaArgs& a, int64_t m0, int
 // whose per-wave part of the offset is scalar, which keeps the vector
 // registers for the accumulators.
 // OCM: 0 scale-first dequantisation; 1 offset-corrected with one group per
-// row (scales applied in the epilogue).
+// row (operand 1 + q/16, offset and scale applied in the epilogue).
 template <int DT, int QT, int SPT, int BM, int WM, int NJ, int KS, int OCM, int KT = 0>
 __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
     static_assert(OCM == 0 || OCM == 1, "scale first, or one group per row");
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         }
     };
 
-    uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
+    uint32_t dq_mask = OC ? TopNibble<DT>::kMask : 0x000F000Fu, dq_magic = OC ? TopNibble<DT>::kOne : kMagic<DT>;
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
 
     floatx4 acc[MI][NJ];
@@ -216,13 +217,13 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // OC (one group per row): offset-corrected dequantisation, as in the
-    // skinny kernels. The B operand is the exact magic value m + q (one
-    // v_and_or_b32 per pair of codes), acc sums A*(m + q) over all of K, S
-    // sums A over K (one MFMA against an all-ones B per activation
+    // OC (one group per row): offset-corrected dequantisation. The B
+    // operand is the exact value 1 + q/16 (TopNibble: a shift and one
+    // v_and_or_b32 per pair of codes), acc sums A*(1 + q/16) over all of K,
+    // S sums A over K (one MFMA against an all-ones B per activation
     // fragment, shared by the NJ n-tiles), and the epilogue applies
-    // C = s * (acc - (m + z) * S): the scale multiplies an exact-integer-
-    // weight sum once instead of every weight.
+    // C = 16*s * (acc - (1 + z/16) * S): the scale multiplies an
+    // exact-weight sum once instead of every weight.
     floatx4 S[OC ? MI : 1];
 #pragma unroll
     for (int i = 0; i < (OC ? MI : 1); ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -230,13 +231,19 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
     const u32x4 ones = {one2, one2, one2, one2};
 
     // One step on LDS buffer `buf` with the weights in (raw, sb, zb); the
-    // next step's activation tile and weights are requested first.
+    // next step's activation tile and then its weights are requested first
+    // (in that order: the wait at the end counts the weight loads). The
+    // last step (a compile-time flag at each call) requests nothing and
+    // needs no wait: no step reads what it would load.
     auto step = [&](int64_t st, int buf, const u32x4 (&raw)[NJ][KS], const uint32_t (&sb)[NJ][KS][SPT],
                     const uint32_t (&zb)[NJ][KS][SPT], u32x4 (&nraw)[NJ][KS], uint32_t (&nsb)[NJ][KS][SPT],
-                    uint32_t (&nzb)[NJ][KS][SPT]) {
-        const bool more = st + 1 < steps;
-        stage_a(st + 1, buf ^ 1, more);
-        load_b(st + 1, nraw, nsb, nzb, more);
+                    uint32_t (&nzb)[NJ][KS][SPT], bool last) {
+        if (!last) {
+            const bool more = st + 1 < steps;
+            stage_a(st + 1, buf ^ 1, more);
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(st + 1, nraw, nsb, nzb, more);
+        }
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char* abase = (buf ? abuf1 : abuf0) + lane * 16;
 #pragma unroll
@@ -248,8 +255,10 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
                 for (int j = 0; j < NJ; ++j) {
                     if (OC) {
                         const uint32_t w = raw[j][kk][s];
-                        bq[j] = u32x4{and_or(w, dq_mask, dq_magic), and_or(w >> 4, dq_mask, dq_magic),
-                                      and_or(w >> 8, dq_mask, dq_magic), and_or(w >> 12, dq_mask, dq_magic)};
+                        bq[j] = u32x4{and_or(top_pair_shift<DT, 0>(w), dq_mask, dq_magic),
+                                      and_or(top_pair_shift<DT, 1>(w), dq_mask, dq_magic),
+                                      and_or(top_pair_shift<DT, 2>(w), dq_mask, dq_magic),
+                                      and_or(top_pair_shift<DT, 3>(w), dq_mask, dq_magic)};
                     } else {
                         const int u = s / (4 / SPT);
                         bq[j] = Dequant<DT>::apply(
@@ -270,20 +279,24 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         // The next activation tile has landed once only the weight loads
         // issued after it may be outstanding; then every wave is done with
         // this buffer and sees the next one.
-        wait_vmcnt<NB_LOADS>();
-        stage_barrier();
+        if (!last) {
+            wait_vmcnt<NB_LOADS>();
+            stage_barrier();
+        }
     };
 
     stage_a(0, 0, true);
+    __builtin_amdgcn_sched_barrier(0);
     load_b(0, raw0, sb0, zb0, true);
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<NB_LOADS>();
     stage_barrier();
     int64_t st = 0;
     for (; st + 1 < steps; st += 2) {
-        step(st, 0, raw0, sb0, zb0, raw1, sb1, zb1);
-        step(st + 1, 1, raw1, sb1, zb1, raw0, sb0, zb0);
+        step(st, 0, raw0, sb0, zb0, raw1, sb1, zb1, false);
+        step(st + 1, 1, raw1, sb1, zb1, raw0, sb0, zb0, false);
     }
-    if (st < steps) step(st, 0, raw0, sb0, zb0, raw1, sb1, zb1);
+    if (st < steps) step(st, 0, raw0, sb0, zb0, raw1, sb1, zb1, true);
 
     // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l%16 of each block.
 #pragma unroll
@@ -292,9 +305,9 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
         const int64_t n = (nt0 + j) * 16 + r;
         const float bv = a.bias && n < a.Nst ? act_to_float<DT>(a.bias[n]) : 0.f;
         float sf = 1.f, zf = 0.f;
-        if (OCM == 1) {  // the row's only scale and zero
-            sf = act_to_float<DT>(a.scales[n]);
-            zf = -((DT == 0 ? 1024.0f : 128.0f) + (QT ? (float)a.zeros[n] : 8.0f));
+        if (OCM == 1) {  // the row's only scale and zero (exact in fp32)
+            sf = 16.0f * act_to_float<DT>(a.scales[n]);
+            zf = -(1.0f + (QT ? (float)a.zeros[n] : 8.0f) * 0.0625f);
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -322,12 +335,16 @@ __global__ __launch_bounds__(512) void mfma_lds_kernel(MfmaArgs a) {
 //    B) are split over the four waves that share a row half: wave wn sums
 //    row block wn of the half (one extra fragment read per K slice), and
 //    the sums meet in LDS.
-//  * P = sum A*(m+q) runs over all of K. OCM 1 (one group per row): the
-//    epilogue applies C = s * (P - (m+z) * S). OCM 2 (groups of G >= 128):
-//    each group end adds (s_g - s_{g+1}) * P to the result, which sums to
-//    sum_g s_g * P_g without ever clearing P, and the correction
-//    -s_g * (m+z_g) * S_g is applied one step later, once the row sums of
-//    the group have passed the step's barrier.
+//  * The B operand is the exact value 1 + q/16 (TopNibble), and
+//    P = sum A*(1 + q/16) runs over all of K. OCM 1 (one group per row):
+//    the epilogue applies C = 16*s * (P - (1 + z/16) * S). OCM 2 (groups of
+//    G >= 128): each group end adds (s_g - s_{g+1}) * P to the result, which
+//    sums to sum_g s_g * P_g without ever clearing P, the correction
+//    -s_g * (1 + z_g/16) * S_g is applied one step later, once the row sums
+//    of the group have passed the step's barrier, and the epilogue scales
+//    the whole by 16. With the offset at 16 code steps (not 1024 as with
+//    the magic 1024 + q), P stays within a small factor of the result even
+//    when sum A grows with K.
 template <int DT, int QT, int OCM, int BM, int KT>
 __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     static_assert(OCM == 1 || OCM == 2, "offset-corrected modes only");
@@ -423,23 +440,27 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     };
     static_assert(APW <= 4 && BPW <= 2, "at most one activation block per K slice");
 
-    uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
+    uint32_t dq_mask = TopNibble<DT>::kMask, dq_magic = TopNibble<DT>::kOne;
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
-    // Magic values of two consecutive words: b0 from w0, b1 from w1.
+    // Two slices' operands at once (one 64-bit shift per pair position for
+    // both words) except in the grouped mode with zero points, which has no
+    // registers for the second slice's operands: one slice at a time there.
+    constexpr bool kPairs = !(OCM == 2 && QT);
+    // Operand values 1 + q/16 of two consecutive words: b0 from w0, b1 from
+    // w1 (one 64-bit shift per pair position serves both words).
     auto dequant_pair = [&](uint32_t w0, uint32_t w1, u32x4& b0, u32x4& b1) {
         const uint64_t x = ((uint64_t)w1 << 32) | w0;
-        uint64_t x4, x8, x12;
-        asm("v_lshrrev_b64 %0, 4, %1" : "=v"(x4) : "v"(x));
-        asm("v_lshrrev_b64 %0, 8, %1" : "=v"(x8) : "v"(x));
-        asm("v_lshrrev_b64 %0, 12, %1" : "=v"(x12) : "v"(x));
-        b0 = u32x4{and_or((uint32_t)x, dq_mask, dq_magic), and_or((uint32_t)x4, dq_mask, dq_magic),
-                   and_or((uint32_t)x8, dq_mask, dq_magic), and_or((uint32_t)x12, dq_mask, dq_magic)};
-        b1 = u32x4{and_or((uint32_t)(x >> 32), dq_mask, dq_magic), and_or((uint32_t)(x4 >> 32), dq_mask, dq_magic),
-                   and_or((uint32_t)(x8 >> 32), dq_mask, dq_magic), and_or((uint32_t)(x12 >> 32), dq_mask, dq_magic)};
+        auto put = [&](int p, uint64_t xp) {
+            b0[p] = and_or((uint32_t)xp, dq_mask, dq_magic);
+            b1[p] = and_or((uint32_t)(xp >> 32), dq_mask, dq_magic);
+        };
+        put(0, top_pair_shift64<DT, 0>(x));
+        put(1, top_pair_shift64<DT, 1>(x));
+        put(2, top_pair_shift64<DT, 2>(x));
+        put(3, top_pair_shift64<DT, 3>(x));
     };
     const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
     const u32x4 ones = {one2, one2, one2, one2};
-    constexpr float kM = DT == 0 ? 1024.0f : 128.0f;
 
     // S: row block wn % MI of the wave's half (with half tiles two waves
     // sum each row block; the sums read back are those of waves 0..MI-1).
@@ -452,7 +473,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
 #pragma unroll
         for (int j = 0; j < (OCM == 2 ? NJ : 1); ++j) P[OCM == 2 ? i : 0][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    // Pending group correction (OCM 2): -s*(m+z) per n column of the wave.
+    // Pending group correction (OCM 2): -s*(1 + z/16) per n column of the wave.
     float cz[NJ];
     int par = 0;          // parity of the group whose S partials are written next
     bool pending = false; // a group ended in the previous step
@@ -470,10 +491,14 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     };
 
     // sb, zb: scales and zeros of step st; sbn: scales of step st + 1 (0
-    // past the last step, whose loads use zero-size descriptors).
+    // past the last step). A tail step (one of the at most two after the
+    // loop; a compile-time flag at each call) requests nothing, since the
+    // step two ahead does not exist, and waits for every load before its
+    // barrier. (Requesting loads whose registers no step reads would let
+    // the compiler drop them and break the count of the wait.)
     auto step = [&](int64_t st, unsigned char* abuf, unsigned char* bbuf, const uint32_t (&sb)[NJ],
                     const uint32_t (&zb)[NJ], const uint32_t (&sbn)[NJ], unsigned char* nabuf, unsigned char* nbbuf,
-                    uint32_t (&nsb)[NJ], uint32_t (&nzb)[NJ]) {
+                    uint32_t (&nsb)[NJ], uint32_t (&nzb)[NJ], bool tail) {
         if (OCM == 2 && pending) {
             floatx4 Sf[MI];
             get_s(par ^ 1, Sf);
@@ -498,13 +523,22 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
             // current MFMAs; with groups the register budget is spent and the
             // point is a full scheduling barrier.
             __builtin_amdgcn_sched_barrier(OCM == 1 ? 0x18F : 0);
-            issue(st + 2, s, nabuf, nbbuf, nsb, nzb);
+            if (!tail) issue(st + 2, s, nabuf, nbbuf, nsb, nzb);
             __builtin_amdgcn_sched_barrier(OCM == 1 ? 0x18F : 0);
-            if ((s & 1) == 0) {
+            if (kPairs && (s & 1) == 0) {
                 // Slices s and s + 1 together: their words are adjacent
                 // registers, so one 64-bit shift serves both.
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) dequant_pair(raw[j][s], raw[j][s + 1], bq2[0][j], bq2[1][j]);
+            } else if (!kPairs) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const uint32_t w = raw[j][s];
+                    bq2[s & 1][j] = u32x4{and_or(top_pair_shift<DT, 0>(w), dq_mask, dq_magic),
+                                          and_or(top_pair_shift<DT, 1>(w), dq_mask, dq_magic),
+                                          and_or(top_pair_shift<DT, 2>(w), dq_mask, dq_magic),
+                                          and_or(top_pair_shift<DT, 3>(w), dq_mask, dq_magic)};
+                }
             }
             const u32x4 (&bq)[NJ] = bq2[s & 1];
             const u32x4 as = *reinterpret_cast<const u32x4*>(abase + ((wm * MI + wn % MI) * 4 + s) * 1024);
@@ -528,7 +562,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
             for (int j = 0; j < NJ; ++j) {
                 const float sf = act_to_float<DT>((uint16_t)sb[j]);
                 const float d = sf - act_to_float<DT>((uint16_t)sbn[j]);
-                cz[j] = -sf * (kM + (QT ? (float)zb[j] : 8.0f));
+                cz[j] = -sf * (1.0f + (QT ? (float)zb[j] : 8.0f) * 0.0625f);
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     const floatx4& p = P[OCM == 2 ? i : 0][OCM == 2 ? j : 0];
@@ -542,7 +576,8 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
         }
         // Stage st + 1 has landed once only the loads of step st + 2 may be
         // outstanding; the barrier then also frees stage st for step st + 3.
-        wait_vmcnt<STAGE_LOADS>();
+        if (tail) wait_vmcnt<0>();
+        else wait_vmcnt<STAGE_LOADS>();
         stage_barrier();
     };
 
@@ -554,12 +589,16 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     stage_barrier();
     int64_t st = 0;
     for (; st + 3 <= steps; st += 3) {
-        step(st, a0, b0, sb0, zb0, sb1, a2, b2, sb2, zb2);
-        step(st + 1, a1, b1, sb1, zb1, sb2, a0, b0, sb0, zb0);
-        step(st + 2, a2, b2, sb2, zb2, sb0, a1, b1, sb1, zb1);
+        step(st, a0, b0, sb0, zb0, sb1, a2, b2, sb2, zb2, false);
+        step(st + 1, a1, b1, sb1, zb1, sb2, a0, b0, sb0, zb0, false);
+        step(st + 2, a2, b2, sb2, zb2, sb0, a1, b1, sb1, zb1, false);
     }
-    if (st < steps) step(st, a0, b0, sb0, zb0, sb1, a2, b2, sb2, zb2);
-    if (st + 1 < steps) step(st + 1, a1, b1, sb1, zb1, sb2, a0, b0, sb0, zb0);
+    // Tail: the scales of the first tail step's successor were requested
+    // by the loop (or the prologue); the second tail step is the last, and
+    // its successor's scale is 0.
+    const uint32_t no_scale[NJ] = {};
+    if (st < steps) step(st, a0, b0, sb0, zb0, sb1, a2, b2, sb2, zb2, true);
+    if (st + 1 < steps) step(st + 1, a1, b1, sb1, zb1, no_scale, a0, b0, sb0, zb0, true);
     wait_vmcnt<0>();
 
     floatx4 Sf[MI];
@@ -584,10 +623,12 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
         if (nt_of(j) >= NT) continue;
         const int64_t n = nt_of(j) * 16 + r;
         const float bv = a.bias && n < a.Nst ? act_to_float<DT>(a.bias[n]) : 0.f;
-        float sf = 1.f, zf = 0.f;
-        if (OCM == 1) {  // the row's only scale and zero
-            sf = act_to_float<DT>(a.scales[n]);
-            zf = -(kM + (QT ? (float)a.zeros[n] : 8.0f));
+        // OCM 1: the row's only scale and zero; OCM 2: the folded sum is in
+        // units of 1/16 code step. Both factors are exact in fp32.
+        float sf = 16.0f, zf = 0.f;
+        if (OCM == 1) {
+            sf = 16.0f * act_to_float<DT>(a.scales[n]);
+            zf = -(1.0f + (QT ? (float)a.zeros[n] : 8.0f) * 0.0625f);
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -595,7 +636,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
             for (int jj = 0; jj < 4; ++jj) {
                 const int64_t m = m0 + wm * (BM / 2) + 16 * i + 4 * g4 + jj;
                 float v = acc[i][j][jj];
-                if (OCM == 1) v = sf * __builtin_fmaf(zf, Sf[i][jj], v);
+                v = OCM == 1 ? sf * __builtin_fmaf(zf, Sf[i][jj], v) : sf * v;
                 if (m < a.M && n < a.Nst) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
             }
         }

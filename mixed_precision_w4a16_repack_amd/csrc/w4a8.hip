@@ -147,18 +147,6 @@ struct A8Args {
     int64_t n_blocks;            // ring kernel: 256-column blocks of C
 };
 
-// 64 wait states between the int8 MFMAs issued before this point and the
-// VALU instructions after it. This compiler spaces a VALU read of a
-// v_mfma_i32_16x16x64_i8 result only 8 wait states from the MFMA (16 or more
-// for v_mfma_f32_16x16x32_bf16). On MI355X such reads returned stale sums,
-// now and then, with 8, 19 and 32 wait states; with 64 they did not. The
-// scheduling barriers keep every instruction on its side.
-__device__ __forceinline__ void mfma_i8_drain() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // One activation chunk (k .. k+7 of a row, stored in pair order by the
 // quantiser) as the 8 bytes of an MFMA operand.
 __device__ __forceinline__ int64_t a_operand(uint2 v) {
@@ -447,9 +435,15 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     // (u + 2) % 4) and then the operands of step st + 3 (into stage
     // (u + 3) % 4). A step's scales are loaded before the operands of the
     // step after it, so waiting for them never waits for later operands.
+    // tail (a compile-time value at each call): 0 in the loop; in the at
+    // most three steps after it, 1 for the first (it requests only the
+    // scales of the third, which that step reads if it runs) and 2 for the
+    // others (nothing to request). Tail steps wait for every load before
+    // their barrier. (Requesting loads whose registers no step reads would
+    // let the compiler drop them and break the count of the wait.)
     auto step = [&](int64_t st, int u, unsigned char* abuf, unsigned char* bbuf, const uint32_t (&sb)[NSC],
-                    uint32_t (&ssb)[NSC], unsigned char* nabuf, unsigned char* nbbuf) {
-        if (GP == 1 || GP == 2 || (GP == 4 && (u & 1))) issue_scales(st + 2, ssb);
+                    uint32_t (&ssb)[NSC], unsigned char* nabuf, unsigned char* nbbuf, int tail) {
+        if (tail <= 1 && (GP == 1 || GP == 2 || (GP == 4 && (u & 1)))) issue_scales(st + 2, ssb);
         u32x4 raw[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) raw[j] = *reinterpret_cast<const u32x4*>(bbuf + (4 * wn + j) * 1024 + lane16);
@@ -465,7 +459,7 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             __builtin_amdgcn_sched_barrier(0);
-            issue(st + 3, h, nabuf, nbbuf);
+            if (tail == 0) issue(st + 3, h, nabuf, nbbuf);
             __builtin_amdgcn_sched_barrier(0);
             if (h == 0) {
 #pragma unroll
@@ -498,7 +492,6 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
             // A slice ends a group: fold the integer sums with s / 16.
             if (GP > 0 && ((2 * u + h + 1) % (GP > 0 ? GP : 1)) == 0) {
                 const int q = GP == 1 ? h : 0;
-                mfma_i8_drain();
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const float sc = 0.0625f * act_to_float<DT>((uint16_t)sb[q * NJ + j]);
@@ -514,7 +507,8 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
         // Stage st + 1 has landed once only the loads issued in steps st - 1
         // and st (operands of steps st + 2, st + 3 and their scales) may be
         // outstanding; the barrier then also frees stage u for step st + 4.
-        wait_vmcnt<8 + SC2>();
+        if (tail) wait_vmcnt<0>();
+        else wait_vmcnt<8 + SC2>();
         stage_barrier();
     };
 
@@ -533,20 +527,19 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     stage_barrier();
     int64_t st = 0;
     for (; st + 4 <= steps; st += 4) {
-        step(st, 0, a0, b0, sb0, sb2, a3, b3);
-        step(st + 1, 1, a1, b1, sb1, sb3, a0, b0);
-        step(st + 2, 2, a2, b2, sb2, sb0, a1, b1);
-        step(st + 3, 3, a3, b3, sb3, sb1, a2, b2);
+        step(st, 0, a0, b0, sb0, sb2, a3, b3, 0);
+        step(st + 1, 1, a1, b1, sb1, sb3, a0, b0, 0);
+        step(st + 2, 2, a2, b2, sb2, sb0, a1, b1, 0);
+        step(st + 3, 3, a3, b3, sb3, sb1, a2, b2, 0);
     }
-    if (st < steps) step(st, 0, a0, b0, sb0, sb2, a3, b3);
-    if (st + 1 < steps) step(st + 1, 1, a1, b1, sb1, sb3, a0, b0);
-    if (st + 2 < steps) step(st + 2, 2, a2, b2, sb2, sb0, a1, b1);
+    if (st < steps) step(st, 0, a0, b0, sb0, sb2, a3, b3, 1);
+    if (st + 1 < steps) step(st + 1, 1, a1, b1, sb1, sb3, a0, b0, 2);
+    if (st + 2 < steps) step(st + 2, 2, a2, b2, sb2, sb0, a1, b1, 2);
     wait_vmcnt<0>();
 
     // With K in chunks: this chunk's fp32 results (the row scale and bias
     // follow in w4a8_reduce_kernel).
     if (a.partials != nullptr) {
-        if (GP == 0) mfma_i8_drain();
         const int64_t ldp = a.NT * 16;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -574,7 +567,6 @@ __global__ __launch_bounds__(512) void w4a8_ring_kernel(A8Args a) {
     // sits at chunk c ^ 2 ((m / 4) % 4), which puts the four row groups of a
     // 16 x 16 block on different LDS banks.
     stage_barrier();
-    if (GP == 0) mfma_i8_drain();
     // Lane l holds rows 4 (l / 16) .. +3 of column l % 16 of each block.
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {

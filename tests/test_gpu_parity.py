@@ -613,6 +613,12 @@ RING = [
     (1930, 14336, 256, 128, UINT4, "f16", True),    # a half tile lies wholly past M
     (2048, 4096, 1024, 64, UINT4, "bf16", True),    # G = 64: staged tiles, scale first
     (1000, 8192, 512, 32, UINT4B8, "f16", False),   # G = 32: staged tiles, scale first, ragged M
+    # Two tail steps after the loop (steps % 3 == 2) in the grouped mode:
+    # the tail requests no loads and waits for every one (the last step's
+    # successor scale is zero).
+    (2048, 4096, 640, 128, UINT4, "f16", True),     # 5 steps, a group per step, zero points
+    (2048, 4096, 1024, 256, UINT4B8, "bf16", False),# 8 steps, two steps per group
+    (2048, 4096, 4096, 256, UINT4, "f16", True),    # 32 steps, the K of the 14336 x 4096 prefill weight
 ]
 
 
@@ -628,6 +634,64 @@ def test_ring_tiles(M, N, K, G, qtype, dtype, bias):
     rows = sample_rows(M)
     err = rel_err_rows(C, oracle_ref(case, rows=rows), rows)
     assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
+
+
+# Long sums of non-zero-mean activations. The offset-corrected kernels feed
+# the MFMA exact operand values with a constant offset (b = c0 + c1*q) and
+# take the offset back out with row sums S = sum A; with A ~ N(mu, 1) the
+# partial sums grow like mu*K, which is the one input property that fp32
+# rounding of those sums is sensitive to. Codes "centred" on the zero
+# (q = clip(round(N(z, 2.5)))) make C itself small, the hardest case for the
+# relative error. K = 14336 is the deepest decode/prefill shape.
+SHIFTED = [
+    # (M, N, K, G, qtype, dtype, mean, codes, path): the kernel each reaches
+    (2048, 4096, 14336, -1, UINT4B8, "f16", 1.0, "uniform", MFMA),   # ring, one group per row
+    (2048, 4096, 14336, -1, UINT4B8, "f16", 3.0, "centred", MFMA),
+    (2048, 4096, 14336, 256, UINT4B8, "f16", 1.0, "uniform", MFMA),  # ring, folded groups
+    (2048, 4096, 14336, 256, UINT4B8, "f16", 3.0, "centred", MFMA),
+    (2048, 4096, 14336, 256, UINT4, "f16", 3.0, "centred", MFMA),    # ring, zero points, codes around each zero
+    (2048, 4096, 14272, -1, UINT4B8, "f16", 3.0, "centred", MFMA),   # ring with a K tail
+    (64, 4096, 14336, -1, UINT4B8, "f16", 1.0, "uniform", MFMA),     # staged tiles, one group per row
+    (64, 4096, 14336, -1, UINT4B8, "f16", 3.0, "centred", MFMA),
+    (64, 4096, 14272, -1, UINT4, "f16", 3.0, "centred", MFMA),       # staged tiles with a K tail
+    (128, 14336, 4096, 64, UINT4B8, "f16", 3.0, "centred", MFMA),    # staged tiles, scale first (G = 64)
+    (2048, 4096, 14336, -1, UINT4, "bf16", 3.0, "centred", MFMA),
+    (2048, 4096, 14336, 256, UINT4B8, "bf16", 3.0, "centred", MFMA),
+    (16, 4096, 14336, -1, UINT4B8, "f16", 3.0, "centred", SKINNY),   # skinny fold blocks, K split in chunks
+    (16, 14336, 4096, 128, UINT4, "f16", 3.0, "centred", SKINNY),
+    (8, 1024, 14336, 256, UINT4B8, "f16", 3.0, "centred", SKINNY),   # split-K kernel
+]
+
+
+def _centred_case(cfg, M, N, K, G, qtype, dtype, mean):
+    """A case whose codes are drawn around their zero (8, or each group's
+    zero point), packed by the oracle's packer."""
+    case = _case(cfg, M, N, K, G, qtype, dtype, mean=mean)
+    Ge = wi.effective_group(K, G)
+    if qtype == UINT4:
+        z = oracle.unpack_zeros(case.weight_zero_point, N).astype(np.float64)
+        centre = np.repeat(z, Ge, axis=1)
+    else:
+        centre = np.full((N, K), 8.0)
+    codes = wi.centred_codes(cfg * 7919 + K, centre)
+    case.weight_packed = oracle.pack_codes(codes)
+    return case
+
+
+@pytest.mark.parametrize("M,N,K,G,qtype,dtype,mean,codes,path", SHIFTED,
+                         ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-G{c[3]}-q{c[4]}-{c[5]}-mu{c[6]:g}-{c[7]}" for c in SHIFTED])
+def test_shifted_activations_long_k(M, N, K, G, qtype, dtype, mean, codes, path):
+    print(f"[case] shifted M={M} N={N} K={K} G={G} qtype={qtype} {dtype} mean={mean} {codes} path={path}",
+          flush=True)
+    case = (_centred_case(27, M, N, K, G, qtype, dtype, mean) if codes == "centred"
+            else _case(27, M, N, K, G, qtype, dtype, mean=mean))
+    packed = repack(case)
+    C = w4.gemm(case.A.to(DEV), packed, N, K, G, qtype, path=path)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    err = rel_err_rows(C, oracle_ref(case, rows=rows), rows)
+    print(f"[result] rel err {err:.3e}", flush=True)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e} > {oracle.TOLERANCE[dtype]}"
 
 
 # Full-K skinny kernels (N >= 3072): activations in registers or staged in
@@ -830,6 +894,12 @@ W4A8_GEMM = [
     (1100, 14336, 2048, 128, "bf16"),
     (2048, 4096, 14336, 256, "f16"),
     (1999, 4232, 2944, -1, "f16"),
+    # Tail steps after the 4-step loop with folded groups: 11 steps (three
+    # tail steps, the third reads the stage the loop's last step loaded) and
+    # 10 steps (two).
+    (2048, 4096, 1408, 64, "bf16"),
+    (2048, 4096, 1408, 128, "f16"),
+    (2048, 4096, 1280, 256, "bf16"),
     # Fewer ring tiles than CUs: K in chunks (fp32 partials, second kernel).
     (300, 14336, 2048, 128, "f16"),
     (384, 4096, 14336, 256, "bf16"),

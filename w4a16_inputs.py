@@ -87,11 +87,14 @@ def make_case(
     dtype: str,
     *,
     sigma: float = 1.0,
+    mean: float = 0.0,
     with_zero_point: bool | None = None,
     with_bias: bool = False,
     extra: int = 0,
 ) -> Case:
-    """Draw one case. ``with_zero_point`` defaults to ``qtype == UINT4``."""
+    """Draw one case. ``with_zero_point`` defaults to ``qtype == UINT4``.
+    ``mean`` shifts the activations, A ~ N(mean, sigma) (0 everywhere except
+    the tests of sums over long K of non-zero-mean activations)."""
     if with_zero_point is None:
         with_zero_point = qtype == UINT4
     Ge = effective_group(K, G)
@@ -106,7 +109,7 @@ def make_case(
         if N % 8:
             raise ValueError(f"zero points need N % 8 == 0, got N={N}")
         zp = rng.integers(0, 2**32, size=(N // 8, Kg), dtype=np.uint64).astype(np.uint32).view(np.int32)
-    A = _to_act(rng.normal(0.0, sigma, size=(M, K)), dtype)
+    A = _to_act(rng.normal(mean, sigma, size=(M, K)), dtype)
     bias = _to_act(rng.normal(0.0, 1.0, size=(N,)), dtype) if with_bias else None
     return Case(M, N, K, G, qtype, dtype, words.view(np.int32), scales, zp, A, bias)
 
@@ -158,6 +161,16 @@ def make_layout_weights(cfg_id: int, N: int, K: int, G: int, qtype: int, dtype: 
         zp = rng.integers(0, 2**32, size=zdims, dtype=np.uint64).astype(np.uint32).view(np.int32)
     return LayoutWeights(N, K, G, qtype, dtype, weight_output_dim, weight_packed_dim, scale_output_dim,
                          zero_output_dim, words, scales, zp)
+
+
+def centred_codes(seed: int, centre: np.ndarray, sd: float = 2.5) -> np.ndarray:
+    """Integer codes in [0, 15] drawn around a per-element centre: round a
+    N(centre, sd) draw to the nearest integer and clip it to the code range.
+    ``centre`` has the shape of the codes (e.g. [N, K], the zero of each
+    weight). Returns uint8 codes; packing them is left to the caller."""
+    rng = np.random.default_rng([seed, 4242])
+    x = rng.normal(0.0, sd, size=centre.shape) + centre
+    return np.clip(np.rint(x), 0, 15).astype(np.uint8)
 
 
 def random_activations(cfg_id: int, M: int, K: int, dtype: str, sigma: float = 1.0, extra: int = 0) -> torch.Tensor:
