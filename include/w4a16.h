@@ -269,7 +269,11 @@ w4a16_status w4a8_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group_
  *            pages; the call cannot check this)
  *   bias     [N] act dtype, or NULL; C [M, ldc] act dtype, ldc >= N
  *   workspace, workspace_bytes  at least w4a8_workspace_size() bytes (may
- *            be NULL when that is 0); calls that share one must be ordered
+ *            be NULL when that is 0); calls that share one must be ordered.
+ *            The call writes partial results from the start of the
+ *            workspace: a buffer it shares with w4a16_gemm must have its
+ *            first w4a16_workspace_counter_bytes() bytes zeroed again before
+ *            the next w4a16_gemm call
  * The integer group sums are exact (int8 MFMA, int32 accumulation); each
  * group's sum is scaled in fp32. Shapes as for w4a16_repack. qa must be
  * 8-byte aligned with ldq % 8 == 0. At M >= 64, with qa 16-byte aligned,

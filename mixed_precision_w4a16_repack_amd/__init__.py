@@ -233,8 +233,12 @@ class Workspace:
 _workspaces: dict = {}
 
 
-def _default_workspace(device) -> Workspace:
-    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+def _default_workspace(device, kind: str = "w4a16") -> Workspace:
+    """The default workspace of one kind of call on a device and stream.
+    w4a16_gemm and w4a8_gemm get separate ones: w4a16_gemm needs the counter
+    region at the start of its workspace to be zero, and w4a8_gemm writes its
+    partial results from the start of its own."""
+    key = (kind, torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None:
         ws = _workspaces[key] = Workspace(device)
@@ -335,7 +339,7 @@ def gemm_w4a8(qa: torch.Tensor, xs: torch.Tensor, packed: torch.Tensor, N: int, 
     if bias is not None and (bias.dim() != 1 or bias.shape[0] != N or not bias.is_contiguous()):
         raise ValueError(f"bias must be a contiguous [N={N}] tensor")
     ws_bytes = w4a8_workspace_size(M, N, K, group_size) if M > 0 else 0
-    ws = (workspace or _default_workspace(qa.device)).get(ws_bytes)
+    ws = (workspace or _default_workspace(qa.device, "w4a8")).get(ws_bytes)
     _check(load_library().w4a8_gemm(
         _ptr(qa), _ptr(xs), M, qa.stride(0), _ptr(packed), N, K, group_size, _DTYPE_CODE[dtype], _ptr(bias),
         _ptr(out), out.stride(0), _ptr(ws) if ws_bytes else None, ws.numel() if (ws is not None and ws_bytes) else 0,

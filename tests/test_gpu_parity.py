@@ -958,6 +958,25 @@ def test_w4a8_ring_equals_register_kernel(M, N, K, G):
     assert torch.equal(C_ring, C_reg)
 
 
+def test_w4a8_then_w4a16_with_default_workspaces():
+    """A W4A8 call that splits K writes partial results into its workspace;
+    a following W4A16 split-K call on the binding's default workspace must
+    still find its arrival counters at zero (the two kinds of call get
+    separate default workspaces)."""
+    M, N, K, G = 300, 14336, 2048, 128
+    case = _case(56, M, N, K, G, UINT4B8, "f16")
+    wq, ws, _, A, _ = to_dev(case)
+    packed = w4.repack(wq, ws, None, G, UINT4B8)
+    assert w4.w4a8_workspace_size(M, N, K, G) > 0
+    qa, xs = w4.quantize_a8(A)
+    w4.gemm_w4a8(qa, xs, packed, N, K, G, torch.float16)
+    case2 = _case(57, 16, 4096, 14336, 128, UINT4B8, "f16")
+    assert w4.workspace_size(16, 4096, 14336, 128) > 0
+    C = w4.gemm(case2.A.to(DEV), repack(case2), 4096, 14336, 128, UINT4B8)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(C.cpu(), oracle_ref(case2)) <= oracle.TOLERANCE["f16"]
+
+
 def test_w4a8_unaligned_output_and_no_bias():
     """C rows that are not 16-byte multiples (ldc % 8 != 0) take the register
     kernel; bias None on the tiled kernel. Same exact sums, same results."""
