@@ -37,6 +37,19 @@ w4a16_status hip_fail(const char* what, hipError_t e) {
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Bounds that keep every size and offset computation of the calls within
+// 64-bit arithmetic: N and K (the packed sizes are products of the two) and
+// row strides in elements.
+constexpr int64_t kMaxDim = (int64_t)1 << 32;
+constexpr int64_t kMaxStride = (int64_t)1 << 40;
+
+w4a16_status check_stride(const char* name, int64_t ld) {
+    if (ld > kMaxStride)
+        return fail(W4A16_ERR_UNSUPPORTED, "%s=%lld is too large: row strides must be at most 2^40 elements", name,
+                    (long long)ld);
+    return W4A16_OK;
+}
+
 int ilog2(int64_t x) {
     int l = 0;
     while ((int64_t(1) << l) < x) ++l;
@@ -46,6 +59,8 @@ int ilog2(int64_t x) {
 // Shape and type rules shared by every call that takes a weight.
 w4a16_status make_geometry(int64_t N, int64_t K, int32_t group_size, int32_t qtype, Geometry* g) {
     if (N <= 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "N=%lld and K=%lld must be positive", (long long)N, (long long)K);
+    if (N > kMaxDim || K > kMaxDim)
+        return fail(W4A16_ERR_UNSUPPORTED, "N=%lld and K=%lld must be at most 2^32", (long long)N, (long long)K);
     if (qtype != W4A16_UINT4B8 && qtype != W4A16_UINT4)
         return fail(W4A16_ERR_INVALID_ARG, "qtype=%d is not a w4a16_qtype (0 uint4b8, 1 uint4)", qtype);
     if (N % 8 != 0) return fail(W4A16_ERR_UNSUPPORTED, "N=%lld must be divisible by 8", (long long)N);
@@ -228,6 +243,7 @@ w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packe
         return fail(W4A16_ERR_INVALID_ARG, "A, packed and C must not be NULL");
     if (lda < K) return fail(W4A16_ERR_INVALID_ARG, "lda=%lld must be >= K=%lld", (long long)lda, (long long)K);
     if (ldc < N) return fail(W4A16_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc, (long long)N);
+    if ((st = check_stride("lda", lda)) != W4A16_OK || (st = check_stride("ldc", ldc)) != W4A16_OK) return st;
     if (!aligned16(A) || lda % 8 != 0)
         return fail(W4A16_ERR_UNSUPPORTED, "A must be 16-byte aligned with lda %% 8 == 0 (lda=%lld)", (long long)lda);
     if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
@@ -288,6 +304,9 @@ w4a16_status w4a8_quantize(const void* A, int64_t M, int64_t K, int64_t lda, int
     if (K % 8 != 0) return fail(W4A16_ERR_UNSUPPORTED, "K=%lld must be divisible by 8", (long long)K);
     if (lda < K) return fail(W4A16_ERR_INVALID_ARG, "lda=%lld must be >= K=%lld", (long long)lda, (long long)K);
     if (ldq < K) return fail(W4A16_ERR_INVALID_ARG, "ldq=%lld must be >= K=%lld", (long long)ldq, (long long)K);
+    if (K > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "K=%lld must be at most 2^32", (long long)K);
+    w4a16_status st = check_stride("lda", lda);
+    if (st != W4A16_OK || (st = check_stride("ldq", ldq)) != W4A16_OK) return st;
     if (M >= ((int64_t)1 << 31)) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld is too large (one workgroup per row)", (long long)M);
     if (M == 0) return W4A16_OK;
     if (A == nullptr || qa == nullptr || xs == nullptr) return fail(W4A16_ERR_INVALID_ARG, "A, qa and xs must not be NULL");
@@ -329,6 +348,7 @@ w4a16_status w4a8_gemm(const int8_t* qa, const float* xs, int64_t M, int64_t ldq
         return fail(W4A16_ERR_INVALID_ARG, "dtype=%d is not a w4a16_dtype (0 fp16, 1 bf16)", dtype);
     if (ldq < K) return fail(W4A16_ERR_INVALID_ARG, "ldq=%lld must be >= K=%lld", (long long)ldq, (long long)K);
     if (ldc < N) return fail(W4A16_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc, (long long)N);
+    if ((st = check_stride("ldq", ldq)) != W4A16_OK || (st = check_stride("ldc", ldc)) != W4A16_OK) return st;
     if (M == 0) return W4A16_OK;
     if (qa == nullptr || xs == nullptr || packed == nullptr || C == nullptr)
         return fail(W4A16_ERR_INVALID_ARG, "qa, xs, packed and C must not be NULL");
@@ -365,6 +385,7 @@ w4a16_status w4a16_dequant(const void* packed, int64_t N, int64_t K, int32_t gro
     if (packed == nullptr || dense == nullptr) return fail(W4A16_ERR_INVALID_ARG, "packed and dense must not be NULL");
     if (reinterpret_cast<uintptr_t>(packed) & 255u) return fail(W4A16_ERR_INVALID_ARG, "packed must be 256-byte aligned");
     if (ldw < K) return fail(W4A16_ERR_INVALID_ARG, "ldw=%lld must be >= K=%lld", (long long)ldw, (long long)K);
+    if ((st = check_stride("ldw", ldw)) != W4A16_OK) return st;
     if (!aligned16(dense) || ldw % 8 != 0)
         return fail(W4A16_ERR_UNSUPPORTED, "dense must be 16-byte aligned with ldw %% 8 == 0 (ldw=%lld)", (long long)ldw);
     hipError_t e = launch_dequant(packed, g, dtype, dense, ldw, stream);
@@ -386,6 +407,9 @@ w4a16_status w4a16_gemm_dense(const void* A, int64_t M, int64_t lda, const void*
     if (lda < K) return fail(W4A16_ERR_INVALID_ARG, "lda=%lld must be >= K=%lld", (long long)lda, (long long)K);
     if (ldw < K) return fail(W4A16_ERR_INVALID_ARG, "ldw=%lld must be >= K=%lld", (long long)ldw, (long long)K);
     if (ldc < N) return fail(W4A16_ERR_INVALID_ARG, "ldc=%lld must be >= N=%lld", (long long)ldc, (long long)N);
+    w4a16_status st = check_stride("lda", lda);
+    if (st != W4A16_OK || (st = check_stride("ldw", ldw)) != W4A16_OK || (st = check_stride("ldc", ldc)) != W4A16_OK)
+        return st;
     if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(dense) | reinterpret_cast<uintptr_t>(C) |
          reinterpret_cast<uintptr_t>(bias)) & 1u)
         return fail(W4A16_ERR_INVALID_ARG, "A, dense, C and bias must be 2-byte aligned");
