@@ -202,6 +202,27 @@ w4a16_status w4a16_gemm(const void *A, int64_t M, int64_t lda, const void *packe
                         int32_t path, int32_t skinny_max_m, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
+/* w4a16_gemm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, result and errors as w4a16_gemm, without the workspace:
+ * the split-K partial sums and arrival counters of the skinny kernels live
+ * in a static device array of the library, W4A16_NOALLOC_MAX_WORKSPACE_BYTES
+ * bytes (64 KiB of counters + 8 MiB of partial sums) per GPU, held until the
+ * process ends. A call that needs more workspace than that (a larger
+ * w4a16_workspace_size()) returns W4A16_ERR_SIZE without launching anything;
+ * use w4a16_gemm with a caller workspace for it. The call allocates nothing:
+ * no hipMalloc, hipFree or allocating library routine. On the first call
+ * that needs the array on a device (that device current), the library looks
+ * up its address and clears its counters with a small kernel on `stream`;
+ * every later call on that device uses the same array, whose counters every
+ * completed call leaves at zero. All calls on one GPU share the array: calls
+ * that overlap in time on one GPU (different streams, or threads without
+ * ordering) race and must be serialised by the caller. */
+#define W4A16_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)(64 * 1024) + ((size_t)8 << 20))
+w4a16_status w4a16_gemm_noalloc(const void *A, int64_t M, int64_t lda, const void *packed, int64_t N, int64_t K,
+                                int32_t group_size, int32_t qtype, int32_t dtype, const void *bias, void *C,
+                                int64_t ldc, int32_t path, int32_t skinny_max_m, hipStream_t stream);
+
 /* Dense dequantisation of the packed buffer, the first half of the pages'
  * second prefill strategy ("rdna_hybrid_w4a16" page, build 61746:
  * `dequantize_w4a16` and `_cache_dequant_weight`, which keep a dense copy of

@@ -49,6 +49,10 @@ SIGNATURES = {
         ctypes.c_int,
         [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _P, _SZ, _P],
     ),
+    "w4a16_gemm_noalloc": (
+        ctypes.c_int,
+        [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _P],
+    ),
     "w4a16_dequant": (ctypes.c_int, [_P, _I64, _I64, _I32, _I32, _I32, _P, _I64, _P]),
     "w4a8_quantize": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _P, _I64, _P, _P]),
     "w4a8_workspace_size": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.POINTER(_SZ)]),
@@ -268,6 +272,31 @@ def gemm(A: torch.Tensor, packed: torch.Tensor, N: int, K: int, group_size: int,
         _ptr(A), M, A.stride(0), _ptr(packed), N, K, group_size, qtype, _DTYPE_CODE[A.dtype], _ptr(bias),
         _ptr(out), out.stride(0), path, skinny_max_m, _ptr(ws) if ws_bytes else None,
         ws.numel() if (ws is not None and ws_bytes) else 0, _stream(A)))
+    return out
+
+
+def gemm_noalloc(A: torch.Tensor, packed: torch.Tensor, N: int, K: int, group_size: int, qtype: int,
+                 bias: torch.Tensor | None = None, out: torch.Tensor | None = None, path: int = PATH_AUTO,
+                 skinny_max_m: int = 0) -> torch.Tensor:
+    """``gemm`` through w4a16_gemm_noalloc: the split-K workspace is the
+    library's static device scratch (no workspace argument). With ``out``
+    given, the call allocates nothing, here or in the library."""
+    _need_cuda("A", A, (torch.float16, torch.bfloat16))
+    _need_cuda("packed", packed)
+    _need_cuda("bias", bias, A.dtype)
+    if A.dim() != 2 or A.shape[1] != K or A.stride(1) != 1:
+        raise ValueError(f"A must be [M, K={K}] with unit column stride, got {tuple(A.shape)} {A.stride()}")
+    M = A.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    _need_cuda("out", out, A.dtype)
+    if out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError(f"out must be [M={M}, N={N}] with unit column stride")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != N or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous [N={N}] tensor")
+    _check(load_library().w4a16_gemm_noalloc(
+        _ptr(A), M, A.stride(0), _ptr(packed), N, K, group_size, qtype, _DTYPE_CODE[A.dtype], _ptr(bias),
+        _ptr(out), out.stride(0), path, skinny_max_m, _stream(A)))
     return out
 
 

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "w4a16")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["w4a16_api.cpp", "repack.hip", "skinny.hip", "mfma.hip", "dense.hip", "w4a8.hip"]
+SOURCES = ["w4a16_api.cpp", "repack.hip", "skinny.hip", "mfma.hip", "dense.hip", "w4a8.hip", "scratch.hip"]
 STAGED = ["mfma.hip", "w4a8.hip"]  # kernels with hand-counted waits (wait_check)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -75,6 +75,13 @@ constexpr int64_t kMaxTilesPerWG = 16; // full-K: n-tiles per workgroup (LDS for
 
 constexpr size_t kCounterRegionBytes = 64 * 1024;  // 16384 u32 arrival counters
 
+// The static device scratch of w4a16_gemm_noalloc: the counter region and
+// up to 8 MiB of split-K partial sums.
+constexpr size_t kScratchBytes = kCounterRegionBytes + ((size_t)8 << 20);
+// Device address of the current device's scratch (set up on the first call
+// on that device: its counters cleared by a fill kernel on `stream`).
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 SkinnyPlan plan_skinny(int64_t M, const Geometry& g);
 MfmaPlan plan_mfma(int64_t M, const Geometry& g);
 

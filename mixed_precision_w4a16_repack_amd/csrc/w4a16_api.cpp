@@ -16,6 +16,8 @@
 #include "internal.h"
 #include "w4a16.h"
 
+static_assert(W4A16_NOALLOC_MAX_WORKSPACE_BYTES == w4a16::kScratchBytes, "header and library agree on the scratch");
+
 namespace w4a16 {
 namespace {
 
@@ -225,11 +227,18 @@ w4a16_status w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group
     return W4A16_OK;
 }
 
-w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packed, int64_t N, int64_t K,
-                        int32_t group_size, int32_t qtype, int32_t dtype, const void* bias, void* C, int64_t ldc,
-                        int32_t path, int32_t skinny_max_m, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
-    clear_error();
+}  // extern "C"
+
+namespace w4a16 {
+namespace {
+
+// w4a16_gemm and w4a16_gemm_noalloc. With from_scratch, the workspace is the
+// library's static device scratch, fetched only once every argument has
+// passed validation and the call is known to need it.
+w4a16_status gemm_impl(const void* A, int64_t M, int64_t lda, const void* packed, int64_t N, int64_t K,
+                       int32_t group_size, int32_t qtype, int32_t dtype, const void* bias, void* C, int64_t ldc,
+                       int32_t path, int32_t skinny_max_m, void* workspace, size_t workspace_bytes,
+                       bool from_scratch, hipStream_t stream) {
     Geometry g;
     w4a16_status st = make_geometry(N, K, group_size, qtype, &g);
     if (st != W4A16_OK) return st;
@@ -274,6 +283,16 @@ w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packe
     if (p.n_groups * (int64_t)sizeof(uint32_t) > (int64_t)kCounterRegionBytes)
         return fail(W4A16_ERR_UNSUPPORTED, "N=%lld needs more split-K counters than the workspace holds", (long long)N);
     const size_t need = skinny_workspace(p);
+    if (need > 0 && from_scratch) {
+        if (need > kScratchBytes)
+            return fail(W4A16_ERR_SIZE,
+                        "this call needs %zu bytes of split-K workspace, more than the %zu bytes of the static "
+                        "scratch; use w4a16_gemm with a caller workspace",
+                        need, kScratchBytes);
+        hipError_t e = noalloc_scratch(stream, &workspace);
+        if (e != hipSuccess) return hip_fail("static scratch set-up", e);
+        workspace_bytes = kScratchBytes;
+    }
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < need)
             return fail(W4A16_ERR_SIZE, "workspace of %zu bytes is smaller than the %zu bytes this call needs",
@@ -291,6 +310,28 @@ w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packe
         if (e != hipSuccess) return hip_fail("skinny kernel launch", e);
     }
     return W4A16_OK;
+}
+
+}  // namespace
+}  // namespace w4a16
+
+extern "C" {
+
+w4a16_status w4a16_gemm(const void* A, int64_t M, int64_t lda, const void* packed, int64_t N, int64_t K,
+                        int32_t group_size, int32_t qtype, int32_t dtype, const void* bias, void* C, int64_t ldc,
+                        int32_t path, int32_t skinny_max_m, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    clear_error();
+    return gemm_impl(A, M, lda, packed, N, K, group_size, qtype, dtype, bias, C, ldc, path, skinny_max_m, workspace,
+                     workspace_bytes, false, stream);
+}
+
+w4a16_status w4a16_gemm_noalloc(const void* A, int64_t M, int64_t lda, const void* packed, int64_t N, int64_t K,
+                                int32_t group_size, int32_t qtype, int32_t dtype, const void* bias, void* C,
+                                int64_t ldc, int32_t path, int32_t skinny_max_m, hipStream_t stream) {
+    clear_error();
+    return gemm_impl(A, M, lda, packed, N, K, group_size, qtype, dtype, bias, C, ldc, path, skinny_max_m, nullptr, 0,
+                     true, stream);
 }
 
 

@@ -56,6 +56,10 @@ int main(void) {
                                        NULL), W4A16_ERR_UNSUPPORTED);
     expect("gemm workspace", w4a16_gemm(p, 1, 4096, p, 1024, 4096, 128, 0, 0, NULL, p, 1024, 0, 0, NULL, 0, NULL),
            W4A16_ERR_SIZE);
+    expect("gemm_noalloc M=0", w4a16_gemm_noalloc(p, 0, 4096, p, 4096, 4096, 128, 0, 0, NULL, p, 4096, 0, 0, NULL),
+           0);
+    expect("gemm_noalloc too big", w4a16_gemm_noalloc(p, 1, 131072, p, 2048, 131072, 128, 0, 0, NULL, p, 2048, 0, 0,
+                                                      NULL), W4A16_ERR_SIZE);
     expect("dequant ldw", w4a16_dequant(p, 4096, 4096, 128, 0, 0, p, 100, NULL), W4A16_ERR_INVALID_ARG);
     expect("gemm_dense M=0", w4a16_gemm_dense(p, 0, 64, p, 64, 64, 64, 0, NULL, p, 64, NULL, 0, NULL), 0);
     expect("gemm_dense dtype", w4a16_gemm_dense(p, 4, 64, p, 64, 64, 64, 3, NULL, p, 64, NULL, 0, NULL),

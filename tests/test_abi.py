@@ -131,6 +131,45 @@ def test_gemm_rejects_before_any_hip_call(lib, kw, status, needle):
     assert needle in w4.last_error()
 
 
+def _gemm_noalloc(lib, **kw):
+    args = dict(A=ctypes.c_void_p(4096), M=4, lda=4096, packed=ctypes.c_void_p(4096), N=4096, K=4096, G=128,
+                qtype=0, dtype=0, bias=None, C=ctypes.c_void_p(4096), ldc=4096, path=0, smax=0)
+    args.update(kw)
+    return lib.w4a16_gemm_noalloc(args["A"], args["M"], args["lda"], args["packed"], args["N"], args["K"],
+                                  args["G"], args["qtype"], args["dtype"], args["bias"], args["C"], args["ldc"],
+                                  args["path"], args["smax"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,status,needle",
+    [
+        (dict(dtype=2), INVALID, "dtype=2"),
+        (dict(lda=4000), INVALID, "lda=4000 must be >= K=4096"),
+        (dict(A=ctypes.c_void_p(4104)), UNSUPPORTED, "16-byte aligned"),
+        (dict(K=4100, lda=4104), UNSUPPORTED, "must be divisible by"),
+        # 128 n-tiles with K = 131072 split over 256 chunks: 33.5 MB of partial sums
+        (dict(M=1, N=2048, ldc=2048, K=131072, lda=131072), SIZE, "more than the 8454144 bytes of the static scratch"),
+    ],
+)
+def test_gemm_noalloc_rejects_before_any_hip_call(lib, kw, status, needle):
+    assert _gemm_noalloc(lib, **kw) == status
+    assert needle in w4.last_error()
+
+
+def test_gemm_noalloc_m_zero_is_a_noop(lib):
+    assert _gemm_noalloc(lib, M=0) == OK
+    assert w4.last_error() == ""
+
+
+def test_gemm_noalloc_scratch_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define W4A16_NOALLOC_MAX_WORKSPACE_BYTES \(\(size_t\)\(64 \* 1024\) \+ \(\(size_t\)8 << 20\)\)", text)
+    assert m, "the documented scratch size changed"
+    # the largest workspace of the decode shapes fits
+    for (M, N, K) in [(16, 4096, 14336), (16, 14336, 4096), (16, 4096, 4096), (16, 1024, 14336)]:
+        assert w4.workspace_size(M, N, K, 128, w4.PATH_AUTO) <= 64 * 1024 + (8 << 20)
+
+
 def test_gemm_m_zero_is_a_noop(lib):
     # Pointers are never dereferenced for M == 0.
     assert _gemm(lib, M=0) == OK
