@@ -228,6 +228,18 @@ def per_case_spread(g: Gemm, reps=30, min_launches=64):
     return {"p10_us": round(pick(0.1), 2), "p50_us": round(pick(0.5), 2), "p90_us": round(pick(0.9), 2)}
 
 
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (fp64, all host threads) on the decode workload's GEMMs,
     repeated until about budget_s seconds of CPU work."""
@@ -252,6 +264,7 @@ def cpu_baseline(budget_s=12.0):
         "value": round(done_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": int(used),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{done_gemms} decode GEMMs (the step's 12 shapes in order, fp64 C oracle, all of each output) "
                   f"in {dt:.1f} s; weight-stream bytes / time",
@@ -423,8 +436,54 @@ def prefill_dense_rates():
     }
 
 
+def read_ceiling():
+    """HBM read ceiling of one launch: a plain streaming-read kernel
+    (libw4a16_ceiling.so) reads buffers of the decode weight sizes, replayed
+    like the decode launches (graphs of >= 64 launches over >= 1 GB of
+    rotating buffers), over a few launch shapes; the fastest per size."""
+    import ctypes
+
+    from mixed_precision_w4a16_repack_amd import build as lib_build
+
+    lib = ctypes.CDLL(lib_build.CEILING_LIB)
+    fn = lib.w4a16_ceiling_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p]
+    sink = torch.zeros(4096, dtype=torch.int32, device=DEV)
+    shapes = [(256, 512, 8), (512, 512, 4), (1024, 256, 8), (2048, 256, 4)]
+    rows = []
+    sizes = {"empty": 16, "decode 4096x4096 G=128": weight_stream_bytes(4096, 4096, 128, wi.UINT4B8, False),
+             "decode 14336x4096 G=128": weight_stream_bytes(14336, 4096, 128, wi.UINT4B8, False),
+             "decode-asym 6144x4096 G=32": weight_stream_bytes(6144, 4096, 32, wi.UINT4, True)}
+    for name, nbytes in sizes.items():
+        copies = copies_for(nbytes) if nbytes > 16 else 2
+        bufs = [torch.randint(-2**31, 2**31 - 1, (max(4, nbytes // 4),), dtype=torch.int32, device=DEV)
+                for _ in range(copies)]
+        n = max(64, copies)
+        best = None
+        for (grid, threads, unroll) in (shapes if nbytes > 16 else shapes[:1]):
+            def launch(c, grid=grid, threads=threads, unroll=unroll):
+                rc = fn(ctypes.c_void_p(bufs[c % copies].data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                        grid, threads, unroll, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"ceiling kernel launch failed: {rc}")
+            graphs = capture_graphs([[(lambda c=c: launch(c)) for c in range(n)]])
+            warm_up(graphs, 5.0)
+            us = time_graphs(graphs, 10, 2) * 1e3 / (10 * n)
+            if best is None or us < best["us"]:
+                best = {"grid": grid, "threads": threads, "loads_per_thread": unroll, "us": round(us, 3)}
+            del graphs
+        rows.append({"size": name, "bytes": nbytes, **best,
+                     "GBps": round(nbytes / best["us"] / 1e3, 1) if nbytes > 16 else None})
+        del bufs
+        torch.cuda.empty_cache()
+    return {"kernel": "plain streaming read (16-byte nontemporal loads, XOR-folded)", "rows": rows}
+
+
 def extras(warmup):
     out = {}
+    out["read_ceiling"] = read_ceiling()
     # Crossover workload: skinny (16-row slices) vs MFMA at M = 32..256.
     wl = wi.WORKLOADS["crossover"]
     cross = []
@@ -607,6 +666,20 @@ def main():
     del graphs
     if not args.no_extras:
         result["extras"] = extras(args.warmup)
+        pre = result["extras"]["prefill"]
+        # The other half of the metric: the tiled MFMA kernel on the prefill
+        # workload, 2*M*N*K per GEMM over its measured duration, summed over
+        # the 16 prefill GEMMs, against the dense fp16/bf16 MFMA peak.
+        result["roofline_prefill"] = {
+            "kernel": "tiled MFMA GEMM (three-stage ring), prefill workload",
+            "bound": "mfma",
+            "achieved": pre["tflops"],
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": pre["frac_of_peak"],
+            "traffic": None,
+            "algorithmic_flops": sum(2.0 * r["M"] * r["N"] * r["K"] for r in pre["rows"]),
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
