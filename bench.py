@@ -293,14 +293,15 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def prefill_rates():
-    """Prefill workload on the MFMA kernel: TFLOP/s per shape and in total."""
+def prefill_rates(quick=False):
+    """Prefill workload on the MFMA kernel: TFLOP/s per shape and in total.
+    quick: no warm-up and 3 replays (for counter runs under a profiler)."""
     wl = wi.WORKLOADS["prefill"]
     rows, tot_flop, tot_us = [], 0.0, 0.0
     for (G, qt) in wl["variants"]:
         for (M, N, K) in wl["shapes"]:
             g = Gemm(wl["cfg_id"], M, N, K, G, qt, wl["dtype"], wl["sigma"], 2)
-            us = per_case_rate(g, launches=2, reps=10, warm_ms=PREFILL_WARM_MS)
+            us = per_case_rate(g, launches=2, reps=3 if quick else 10, warm_ms=0.0 if quick else PREFILL_WARM_MS)
             tf = g.flops / us / 1e6
             rows.append({"M": M, "N": N, "K": K, "G": G, "qtype": qt, "us": round(us, 1), "tflops": round(tf, 1),
                          "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4)})
@@ -481,26 +482,30 @@ def read_ceiling():
     return {"kernel": "plain streaming read (16-byte nontemporal loads, XOR-folded)", "rows": rows}
 
 
-def extras(warmup):
-    out = {}
-    out["read_ceiling"] = read_ceiling()
-    # Crossover workload: skinny (16-row slices) vs MFMA at M = 32..256.
+def crossover_rates(paths=(("skinny_us", w4.PATH_SKINNY), ("mfma_us", w4.PATH_MFMA)), ms=None):
+    """Crossover workload: skinny (16-row slices) vs MFMA at M = 32..256
+    (or the rows ``ms`` of the same weight)."""
     wl = wi.WORKLOADS["crossover"]
     cross = []
-    for (M, N, K) in wl["shapes"]:
+    shapes = wl["shapes"] if ms is None else [(m, wl["shapes"][0][1], wl["shapes"][0][2]) for m in ms]
+    for (M, N, K) in shapes:
         row = {"M": M}
-        for name, path in (("skinny_us", w4.PATH_SKINNY), ("mfma_us", w4.PATH_MFMA)):
+        for name, path in paths:
             g = Gemm(wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], wl["sigma"],
                      copies_for(weight_stream_bytes(N, K, wl["G"], wl["qtype"], False)), path=path)
             row[name] = round(per_case_rate(g, reps=10), 2)
             del g
-        row["mfma_tflops"] = round(2.0 * M * N * K / row["mfma_us"] / 1e6, 1)
+        if "mfma_us" in row:
+            row["mfma_tflops"] = round(2.0 * M * N * K / row["mfma_us"] / 1e6, 1)
         cross.append(row)
-    out["crossover"] = {"workload": "N=14336, K=4096, G=64, uint4b8, fp16", "rows": cross,
-                        "crossover_M": next((r["M"] for r in cross if r["mfma_us"] < r["skinny_us"]), None)}
-    out["prefill"] = prefill_rates()
-    out["prefill_dense"] = prefill_dense_rates()
-    # Decode asymmetric bf16 workload and the tiny case.
+    out = {"workload": "N=14336, K=4096, G=64, uint4b8, fp16", "rows": cross}
+    if all("skinny_us" in r and "mfma_us" in r for r in cross):
+        out["crossover_M"] = next((r["M"] for r in cross if r["mfma_us"] < r["skinny_us"]), None)
+    return out
+
+
+def decode_asym_rates():
+    """Decode asymmetric bf16 workload: N=6144, K=4096, G=32, uint4 + zero points."""
     wl = wi.WORKLOADS["decode_asym"]
     asym = []
     for (M, N, K) in wl["shapes"]:
@@ -508,7 +513,17 @@ def extras(warmup):
                  copies_for(weight_stream_bytes(N, K, wl["G"], wl["qtype"], True)))
         us = per_case_rate(g)
         asym.append({"M": M, "N": N, "K": K, "us": round(us, 2), "weight_GBps": round(g.weight_bytes / us / 1e3, 1)})
-    out["decode_asym"] = {"workload": "N=6144, K=4096, G=32, uint4 + zero points, bf16", "rows": asym}
+        del g
+    return {"workload": "N=6144, K=4096, G=32, uint4 + zero points, bf16", "rows": asym}
+
+
+def extras(warmup):
+    out = {}
+    out["read_ceiling"] = read_ceiling()
+    out["crossover"] = crossover_rates()
+    out["prefill"] = prefill_rates()
+    out["prefill_dense"] = prefill_dense_rates()
+    out["decode_asym"] = decode_asym_rates()
     wl = wi.WORKLOADS["tiny"]
     (M, N, K) = wl["shapes"][0]
     g = Gemm(wl["cfg_id"], M, N, K, wl["G"], wl["qtype"], wl["dtype"], wl["sigma"], 4)
@@ -559,6 +574,9 @@ def main():
                     help="only time the W4A8 variant (int8 activations) on the decode and prefill shapes")
     ap.add_argument("--strides-only", action="store_true",
                     help="only time prefill GEMMs with padded and unpadded activation/output row strides")
+    ap.add_argument("--only", choices=["crossover", "crossover-mfma", "crossover-fine", "decode-asym", "read-ceiling",
+                                       "prefill", "prefill-quick"],
+                    help="only time one extra workload and print its JSON (the commands the profiles use)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time the prefill workload (MFMA kernel, and the dense variant) and print its JSON")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -589,6 +607,13 @@ def main():
         return
     if args.strides_only:
         print(json.dumps({"row_strides": row_stride_rates()}), flush=True)
+        return
+    if args.only:
+        fn = {"crossover": crossover_rates, "crossover-mfma": lambda: crossover_rates((("mfma_us", w4.PATH_MFMA),)),
+              "crossover-fine": lambda: crossover_rates(ms=(16, 17, 20, 24, 28, 32, 48)),
+              "decode-asym": decode_asym_rates, "read-ceiling": read_ceiling, "prefill": prefill_rates,
+              "prefill-quick": lambda: prefill_rates(quick=True)}[args.only]
+        print(json.dumps({args.only: fn()}), flush=True)
         return
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_rates(), "prefill_dense": prefill_dense_rates()}), flush=True)

@@ -710,6 +710,11 @@ FULL_K = [
     (4096, 16384, 12, -1, UINT4B8, "f16", False), # K split in 4 chunks, one group per row
     (14336, 4096, 7, 32, UINT4, "bf16", True),    # streamed: 4 n-tiles per workgroup, a scale per word
     (6144, 4096, 16, 32, UINT4, "bf16", True),    # 2 n-tiles per workgroup, a scale per word
+    # Long K with K split over workgroups (partials through the workspace).
+    (4096, 14336, 1, 128, UINT4B8, "f16", False),
+    (4096, 14336, 4, 128, UINT4, "bf16", True),
+    (3072, 13952, 3, 128, UINT4B8, "f16", True),  # 109 k-tiles
+    (4096, 16384, 2, -1, UINT4, "f16", False),    # one group per row
 ]
 
 
