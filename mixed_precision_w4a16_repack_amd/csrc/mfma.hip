@@ -88,6 +88,25 @@ __device__ __forceinline__ TileBufs tile_bufs(const MfmaArgs& a, int64_t m0, int
     return t;
 }
 
+// Tile (ty, tx) of workgroup b of a launch over all m_tiles x n_blocks
+// tiles. Workgroups go to the 8 XCDs round-robin (b % 8); each XCD takes a
+// contiguous eighth of the tile order, and that order runs over groups of
+// 4 m-tiles with the n-blocks inside a group, so that the workgroups one XCD
+// runs at a time share 4 activation row blocks and about 8 weight column
+// blocks in its L2.
+__device__ __forceinline__ void xcd_tile(const MfmaArgs& a, int64_t& ty, int64_t& tx) {
+    // 32-bit arithmetic (a launch has fewer than 2^31 tiles) made explicitly
+    // wave-uniform, so that the tile's buffer descriptors stay scalar.
+    const uint32_t b = blockIdx.x, nb = (uint32_t)a.n_blocks, mt = (uint32_t)a.m_tiles;
+    const uint32_t grid = mt * nb;
+    const uint32_t idx = grid % 8 == 0 ? (b % 8) * (grid / 8) + b / 8 : b;
+    constexpr uint32_t GM = 4;
+    const uint32_t grp = idx / (GM * nb), off = idx - grp * GM * nb;
+    const uint32_t rows = mt - grp * GM < GM ? mt - grp * GM : GM;
+    ty = (int64_t)__builtin_amdgcn_readfirstlane(grp * GM + off % rows);
+    tx = (int64_t)__builtin_amdgcn_readfirstlane(off / rows);
+}
+
 // Tiled variant with the activation tile loaded straight into LDS.
 // A workgroup of 8 waves computes a BM x BN tile of C, the waves in a
 // WM x (8/WM) grid; wave (wm, wn) owns MI = BM/(16*WM) row blocks and NJ
@@ -643,6 +662,197 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     }
 }
 
+// 128 x 512 tiles for one group per row, for large M and N: twice the
+// columns per activation tile of the ring kernel, so every activation byte
+// brought from L2 serves twice the MFMA work. On MI355X the shader clock of
+// these GEMMs is set by the power limit, and the activation traffic from L2
+// into the CUs is what lowers it (with half of it the clock rises from about
+// 2.05 to 2.27 GHz); the wider tile cuts the bytes moved per MFMA by a
+// quarter.
+//  * 8 waves side by side: wave w computes all 128 rows of n-tiles
+//    4*w .. 4*w + 3 (32 accumulators of 16 x 16), so each weight word is
+//    dequantised once per workgroup and serves 8 row blocks.
+//  * Per K step of 128 both operands go straight into LDS (32 activation
+//    blocks and 32 weight tiles of 1 KB), double-buffered: the step's loads
+//    are requested in its first two slices and waited for at its end, a
+//    whole step (33 MFMAs per wave and slice) later.
+//  * Same offset-corrected arithmetic as the ring kernel with one group per
+//    row: operand 1 + q/16 (TopNibble), row sums S by MFMA against ones
+//    (wave w sums row block w), C = 16*s * (P - (1 + z/16) * S) in the
+//    epilogue.
+template <int DT, int QT, int KT>
+__global__ __launch_bounds__(512) void mfma_wide_kernel(MfmaArgs a) {
+    constexpr int MI = 8, NJ = 4;
+    constexpr int ABLK = 32, BBLK = 32;  // 1 KB blocks per stage
+    constexpr int APW = ABLK / 8, BPW = BBLK / 8;
+    __shared__ __attribute__((aligned(1024))) unsigned char a0[ABLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char a1[ABLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b0[BBLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b1[BBLK * 1024];
+    __shared__ float sx[MI][16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g4 = lane >> 4;
+    int64_t ty, tx;
+    xcd_tile(a, ty, tx);
+    const int64_t m0 = ty * 128;
+    const int64_t NT = a.N / 16;
+    const int64_t steps = a.KTT;
+    const int64_t ntb = tx * 32;  // first n-tile of the workgroup
+    const TileBufs tb = tile_bufs(a, m0, 128, ntb, 32);
+
+    auto rsrc = [&](const void* base, uint32_t bytes, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
+    };
+    // Activation block b = wave*APW + t: row block b/4, K slice b%4.
+    uint32_t a_off[APW];
+#pragma unroll
+    for (int t = 0; t < APW; ++t) {
+        const int b = wave * APW + t;
+        int64_t row = m0 + 16 * (b >> 2) + r;
+        if (row > a.M - 1) row = a.M - 1;
+        a_off[t] = (uint32_t)(((row - tb.mb) * a.lda + 8 * g4) * 2);
+    }
+    // Weight block b = wave*BPW + t: n-tile ntb + b (clamped; never stored).
+    uint32_t b_tile[BPW];
+#pragma unroll
+    for (int t = 0; t < BPW; ++t) {
+        const int64_t nt = ntb + wave * BPW + t;
+        b_tile[t] = (uint32_t)((nt < NT ? nt : NT - 1) - ntb);
+    }
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    const int32_t k_end = (int32_t)a.K - 8 * g4;
+    auto nt_of = [&](int j) { return ntb + wave * NJ + j; };
+
+    // Requests half h (0, 1) of step st: two activation blocks and two
+    // weight tiles of the wave.
+    auto issue = [&](int64_t st, int h, unsigned char* abuf, unsigned char* bbuf) {
+        const bool live = st < steps;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int p = 2 * h + u;
+            const int b = wave * APW + p;
+            const uint32_t kcol = (uint32_t)(st * 128 + 32 * (b & 3));
+            load_lds16(rsrc(tb.A, tb.a_bytes, live), abuf + b * 1024,
+                       KT && (int32_t)kcol >= k_end ? 0x80000000u : a_off[p], kcol * 2);
+            load_lds16(rsrc(tb.codes, tb.codes_bytes, live), bbuf + (wave * BPW + p) * 1024, lane16,
+                       (uint32_t)((b_tile[p] * a.KTT + st) * 1024));
+        }
+    };
+
+    uint32_t dq_mask = TopNibble<DT>::kMask, dq_magic = TopNibble<DT>::kOne;
+    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
+    const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
+    const u32x4 ones = {one2, one2, one2, one2};
+
+    floatx4 acc[MI][NJ], S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Step st multiplies stage (abuf, bbuf) and fills the other stage with
+    // step st + 1 (past the last step the descriptors have size 0: the loads
+    // write zeros without a memory access, and no step reads them).
+    auto step = [&](int64_t st, const unsigned char* abuf, const unsigned char* bbuf, unsigned char* nabuf,
+                    unsigned char* nbbuf) {
+        const unsigned char* abase = abuf + lane16;
+        u32x4 bq2[2][NJ];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < 2) issue(st + 1, s, nabuf, nbbuf);
+            if ((s & 1) == 0) {
+                // Words s and s + 1 of each n-tile (k 32*s .. 32*s + 63 of the
+                // step): adjacent, so one 64-bit shift per pair position
+                // serves both.
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const uint64_t x =
+                        *reinterpret_cast<const uint64_t*>(bbuf + (wave * NJ + j) * 1024 + lane16 + 4 * s);
+                    auto put = [&](int p, uint64_t xp) {
+                        bq2[0][j][p] = and_or((uint32_t)xp, dq_mask, dq_magic);
+                        bq2[1][j][p] = and_or((uint32_t)(xp >> 32), dq_mask, dq_magic);
+                    };
+                    put(0, top_pair_shift64<DT, 0>(x));
+                    put(1, top_pair_shift64<DT, 1>(x));
+                    put(2, top_pair_shift64<DT, 2>(x));
+                    put(3, top_pair_shift64<DT, 3>(x));
+                }
+            }
+            const u32x4 (&bq)[NJ] = bq2[s & 1];
+            // Transposed products (weights as the first operand): lane l
+            // ends with C[row l%16][columns 4*(l/16) .. +3] of each tile,
+            // four adjacent outputs, and the row sum of row l%16.
+            const u32x4 as = *reinterpret_cast<const u32x4*>(abase + (wave * 4 + s) * 1024);
+            S = mfma16x16x32<DT>(ones, as, S);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const u32x4 av = *reinterpret_cast<const u32x4*>(abase + (i * 4 + s) * 1024);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32<DT>(bq[j], av, acc[i][j]);
+            }
+        }
+        // The next stage has landed once no load is outstanding; the barrier
+        // also frees this stage for the step after next.
+        wait_vmcnt<0>();
+        stage_barrier();
+    };
+
+    issue(0, 0, a0, b0);
+    issue(0, 1, a0, b0);
+    wait_vmcnt<0>();
+    stage_barrier();
+    int64_t st = 0;
+    for (; st + 2 <= steps; st += 2) {
+        step(st, a0, b0, a1, b1);
+        step(st + 1, a1, b1, a0, b0);
+    }
+    if (st < steps) step(st, a0, b0, a1, b1);
+
+    // Row sums: wave w summed row block w (every lane holds the sum of its
+    // row l%16).
+    if (g4 == 0) sx[wave][r] = S[0];
+    stage_barrier();
+
+    // Epilogue: per tile, lane l writes row 16*i + l%16, columns
+    // 4*(l/16) .. +3 of the n-tile: one 8-byte store where the four columns
+    // exist and C's rows keep them 8-byte aligned.
+    const bool vec = ((a.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 7) == 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if (nt_of(j) >= NT) continue;
+        const int64_t n0 = nt_of(j) * 16 + 4 * g4;
+        float sf[4], zf[4], bv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int64_t n = n0 + jj;
+            bv[jj] = a.bias && n < a.Nst ? act_to_float<DT>(a.bias[n]) : 0.f;
+            sf[jj] = 16.0f * act_to_float<DT>(a.scales[n]);
+            zf[jj] = -(1.0f + (QT ? (float)a.zeros[n] : 8.0f) * 0.0625f);
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int64_t m = m0 + 16 * i + r;
+            if (m >= a.M) continue;
+            const float Sr = sx[i][r];
+            uint16_t o[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) o[jj] = to_act_bits<DT>(sf[jj] * __builtin_fmaf(zf[jj], Sr, acc[i][j][jj]) + bv[jj]);
+            uint16_t* dst = a.C + m * a.ldc + n0;
+            if (vec && n0 + 3 < a.Nst) {
+                *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                       (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if (n0 + jj < a.Nst) dst[jj] = o[jj];
+            }
+        }
+    }
+}
+
 template <int DT, int QT, int OCM, int KT>
 hipError_t launch_ring_ocm(MfmaArgs a, hipStream_t stream) {
     // 128 x 256 tiles, row-major over m-tiles x n-blocks, one workgroup per
@@ -667,6 +877,18 @@ hipError_t launch_ring_ocm(MfmaArgs a, hipStream_t stream) {
 template <int DT, int QT>
 hipError_t launch_ring_t(MfmaArgs a, hipStream_t stream) {
     a.m_tiles = (a.M + 127) / 128;
+    if (a.one_group) {
+        // 128 x 512 tiles when they fill whole rounds of the CUs (or the
+        // last, partial round is at most a fifth of the work).
+        const int64_t wide = a.m_tiles * ((a.N + 511) / 512);
+        if (wide >= kCUs && (wide % kCUs == 0 || wide >= 4 * kCUs)) {
+            a.n_blocks = (a.N + 511) / 512;
+            a.tile0 = 0;
+            if (a.K % 128) hipLaunchKernelGGL((mfma_wide_kernel<DT, QT, 1>), dim3((unsigned)wide), dim3(512), 0, stream, a);
+            else hipLaunchKernelGGL((mfma_wide_kernel<DT, QT, 0>), dim3((unsigned)wide), dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     a.n_blocks = (a.N + 255) / 256;
     if (!a.one_group) return launch_ring_ocm<DT, QT, 2, 0>(a, stream);
     return a.K % 128 ? launch_ring_ocm<DT, QT, 1, 1>(a, stream) : launch_ring_ocm<DT, QT, 1, 0>(a, stream);

@@ -619,6 +619,14 @@ RING = [
     (2048, 4096, 640, 128, UINT4, "f16", True),     # 5 steps, a group per step, zero points
     (2048, 4096, 1024, 256, UINT4B8, "bf16", False),# 8 steps, two steps per group
     (2048, 4096, 4096, 256, UINT4, "f16", True),    # 32 steps, the K of the 14336 x 4096 prefill weight
+    # 128 x 512 tiles (one group per row, whole rounds of 256 tiles or at
+    # least 1024 tiles): two LDS stages, tiles ordered per XCD.
+    (4096, 4096, 1024, -1, UINT4B8, "bf16", False), # 256 tiles, 8 steps
+    (4096, 4000, 896, -1, UINT4, "f16", True),      # ragged N (250 n-tiles), 7 steps: odd tail step
+    (4000, 4096, 1000, -1, UINT4B8, "f16", False),  # ragged M, K tail
+    (8192, 4096, 256, -1, UINT4, "bf16", True),     # 512 tiles: two rounds
+    (8192, 14336, 128, -1, UINT4B8, "bf16", False), # 1792 tiles, a single K step
+    (4470, 15872, 128, -1, UINT4B8, "f16", True),   # 1085 tiles: not a multiple of 8 (no XCD grouping)
 ]
 
 
@@ -651,6 +659,8 @@ SHIFTED = [
     (2048, 4096, 14336, 256, UINT4B8, "f16", 3.0, "centred", MFMA),
     (2048, 4096, 14336, 256, UINT4, "f16", 3.0, "centred", MFMA),    # ring, zero points, codes around each zero
     (2048, 4096, 14272, -1, UINT4B8, "f16", 3.0, "centred", MFMA),   # ring with a K tail
+    (4096, 4096, 14336, -1, UINT4B8, "f16", 3.0, "centred", MFMA),   # 128 x 512 tiles
+    (4096, 4096, 14336, -1, UINT4, "bf16", 3.0, "centred", MFMA),
     (64, 4096, 14336, -1, UINT4B8, "f16", 1.0, "uniform", MFMA),     # staged tiles, one group per row
     (64, 4096, 14336, -1, UINT4B8, "f16", 3.0, "centred", MFMA),
     (64, 4096, 14272, -1, UINT4, "f16", 3.0, "centred", MFMA),       # staged tiles with a K tail
