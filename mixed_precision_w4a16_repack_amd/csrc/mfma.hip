@@ -88,18 +88,18 @@ __device__ __forceinline__ TileBufs tile_bufs(const MfmaArgs& a, int64_t m0, int
     return t;
 }
 
-// Tile (ty, tx) of workgroup b of a launch over all m_tiles x n_blocks
-// tiles. Workgroups go to the 8 XCDs round-robin (b % 8); each XCD takes a
-// contiguous eighth of the tile order, and that order runs over groups of
-// 4 m-tiles with the n-blocks inside a group, so that the workgroups one XCD
-// runs at a time share 4 activation row blocks and about 8 weight column
-// blocks in its L2.
-__device__ __forceinline__ void xcd_tile(const MfmaArgs& a, int64_t& ty, int64_t& tx) {
-    // 32-bit arithmetic (a launch has fewer than 2^31 tiles) made explicitly
-    // wave-uniform, so that the tile's buffer descriptors stay scalar.
-    const uint32_t b = blockIdx.x, nb = (uint32_t)a.n_blocks, mt = (uint32_t)a.m_tiles;
-    const uint32_t grid = mt * nb;
-    const uint32_t idx = grid % 8 == 0 ? (b % 8) * (grid / 8) + b / 8 : b;
+// Tile (ty, tx) of tile `local` of a launch of `count` tiles that covers
+// positions tile0 .. tile0 + count - 1 of the tile order. Workgroups go to
+// the 8 XCDs round-robin (blockIdx % 8); each XCD takes a contiguous eighth
+// of the launch's positions, and the order runs over groups of 4 m-tiles
+// with the n-blocks inside a group, so that the workgroups one XCD runs at a
+// time share 4 activation row blocks and about 8 weight column blocks in its
+// L2. 32-bit arithmetic (fewer than 2^31 tiles) made explicitly wave-uniform,
+// so that the tile's buffer descriptors stay scalar.
+__device__ __forceinline__ void xcd_tile(const MfmaArgs& a, uint32_t local, uint32_t count, int64_t& ty,
+                                         int64_t& tx) {
+    const uint32_t nb = (uint32_t)a.n_blocks, mt = (uint32_t)a.m_tiles;
+    const uint32_t idx = (uint32_t)a.tile0 + (count % 8 == 0 ? (local % 8) * (count / 8) + local / 8 : local);
     constexpr uint32_t GM = 4;
     const uint32_t grp = idx / (GM * nb), off = idx - grp * GM * nb;
     const uint32_t rows = mt - grp * GM < GM ? mt - grp * GM : GM;
@@ -382,17 +382,18 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char b0[BBLK * 1024];
     __shared__ __attribute__((aligned(1024))) unsigned char b1[BBLK * 1024];
     __shared__ __attribute__((aligned(1024))) unsigned char b2[BBLK * 1024];
-    // Row sums: [group parity][wm][row block wn][4 row groups] of floatx4.
-    __shared__ floatx4 sx[2][2][WN][4];
+    // Row sums: [group parity][wm][row block wn][row].
+    __shared__ float sx[2][2][WN][16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave - wm * WN;
     const int r = lane & 15, g4 = lane >> 4;
-    // Tile of the workgroup: 128 x 256 tile a.tile0 + blockIdx.x, or with
-    // BM = 64 half (blockIdx.x & 1) of tile a.tile0 + blockIdx.x / 2.
-    const int64_t lin = a.tile0 + (BM == 128 ? (int64_t)blockIdx.x : (int64_t)(blockIdx.x >> 1));
-    const int64_t ty = lin / a.n_blocks, tx = lin - ty * a.n_blocks;
+    // Tile of the workgroup: tile blockIdx.x of the launch, or with BM = 64
+    // half (blockIdx.x & 1) of tile blockIdx.x / 2.
+    int64_t ty, tx;
+    if (BM == 128) xcd_tile(a, blockIdx.x, gridDim.x, ty, tx);
+    else xcd_tile(a, blockIdx.x >> 1, gridDim.x >> 1, ty, tx);
     const int64_t m0 = ty * 128 + (BM == 64 ? (int64_t)(blockIdx.x & 1) * 64 : 0);
     const int64_t NT = a.N / 16;
     const int64_t steps = a.KTT;
@@ -427,12 +428,15 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     auto nt_of = [&](int j) { return ntb + wn * NJ + j; };
     auto nt_ld = [&](int j) { return nt_of(j) < NT ? nt_of(j) : NT - 1; };
 
-    uint32_t sb0[NJ], sb1[NJ], sb2[NJ], zb0[NJ], zb1[NJ], zb2[NJ];
+    // Per n-tile of the wave: the scales (4 x 16 bits) and zero points
+    // (4 x 8 bits) of the lane's four columns 4*(l/16) .. +3.
+    uint2 sb0[NJ], sb1[NJ], sb2[NJ];
+    uint32_t zb0[NJ], zb1[NJ], zb2[NJ];
     // Requests part p (0..3) of step st: activation block p of the wave,
     // weight block p (p < BPW), and with p == 2 the scales and zeros of the
     // step's group. A step's loads are spread over its four K slices so that
     // the waves do not all queue their requests at the barrier.
-    auto issue = [&](int64_t st, int p, unsigned char* abuf, unsigned char* bbuf, uint32_t (&sb)[NJ],
+    auto issue = [&](int64_t st, int p, unsigned char* abuf, unsigned char* bbuf, uint2 (&sb)[NJ],
                      uint32_t (&zb)[NJ]) {
         const bool live = st < steps;
         const int b = wave * APW + p;
@@ -452,8 +456,8 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const uint32_t so = (uint32_t)(((nt_ld(j) - ntb) * a.Kg + g) * 16);
-                sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)r * 2, so * 2, 0);
-                if (QT) zb[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, (uint32_t)r, so, 0);
+                sb[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs_s, (uint32_t)g4 * 8, so * 2, 0));
+                if (QT) zb[j] = __builtin_amdgcn_raw_buffer_load_b32(rs_z, (uint32_t)g4 * 4, so, 0);
             }
         }
     };
@@ -492,21 +496,21 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
 #pragma unroll
         for (int j = 0; j < (OCM == 2 ? NJ : 1); ++j) P[OCM == 2 ? i : 0][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    // Pending group correction (OCM 2): -s*(1 + z/16) per n column of the wave.
-    float cz[NJ];
+    // Pending group correction (OCM 2): -s*(1 + z/16) per n column of the lane.
+    float cz[NJ][4];
     int par = 0;          // parity of the group whose S partials are written next
     bool pending = false; // a group ended in the previous step
 
-    // Writes this wave's row sums for parity p: lanes with l%16 == 0 hold
-    // the 16 distinct values (4 each) of the 16 x 16 result.
+    // Writes this wave's row sums for parity p: with the transposed products
+    // every lane holds the sum of row l%16 of its row block.
     auto put_s = [&](int p) {
-        if (r == 0) sx[p][wm][wn][g4] = S;
+        if (g4 == 0) sx[p][wm][wn][r] = S[0];
         S = floatx4{0.f, 0.f, 0.f, 0.f};
     };
-    // Row sums of the wave's row blocks, in accumulator layout.
-    auto get_s = [&](int p, floatx4 (&Sf)[MI]) {
+    // Row sums of the lane's row (l%16) in each of the wave's row blocks.
+    auto get_s = [&](int p, float (&Sf)[MI]) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) Sf[i] = sx[p][wm][i][g4];
+        for (int i = 0; i < MI; ++i) Sf[i] = sx[p][wm][i][r];
     };
 
     // sb, zb: scales and zeros of step st; sbn: scales of step st + 1 (0
@@ -515,18 +519,18 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     // step two ahead does not exist, and waits for every load before its
     // barrier. (Requesting loads whose registers no step reads would let
     // the compiler drop them and break the count of the wait.)
-    auto step = [&](int64_t st, unsigned char* abuf, unsigned char* bbuf, const uint32_t (&sb)[NJ],
-                    const uint32_t (&zb)[NJ], const uint32_t (&sbn)[NJ], unsigned char* nabuf, unsigned char* nbbuf,
-                    uint32_t (&nsb)[NJ], uint32_t (&nzb)[NJ], bool tail) {
+    auto step = [&](int64_t st, unsigned char* abuf, unsigned char* bbuf, const uint2 (&sb)[NJ],
+                    const uint32_t (&zb)[NJ], const uint2 (&sbn)[NJ], unsigned char* nabuf, unsigned char* nbbuf,
+                    uint2 (&nsb)[NJ], uint32_t (&nzb)[NJ], bool tail) {
         if (OCM == 2 && pending) {
-            floatx4 Sf[MI];
+            float Sf[MI];
             get_s(par ^ 1, Sf);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j], Sf[i][jj], acc[i][j][jj]);
+                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j][jj], Sf[i], acc[i][j][jj]);
             pending = false;
         }
         u32x4 raw[NJ];
@@ -560,15 +564,18 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
                 }
             }
             const u32x4 (&bq)[NJ] = bq2[s & 1];
+            // Transposed products (weights as the first operand): lane l
+            // ends with row l%16, columns 4*(l/16) .. +3 of each tile, and
+            // the row sum of row l%16.
             const u32x4 as = *reinterpret_cast<const u32x4*>(abase + ((wm * MI + wn % MI) * 4 + s) * 1024);
-            S = mfma16x16x32<DT>(as, ones, S);
+            S = mfma16x16x32<DT>(ones, as, S);
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const u32x4 av = *reinterpret_cast<const u32x4*>(abase + ((wm * MI + i) * 4 + s) * 1024);
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    if (OCM == 2) P[OCM == 2 ? i : 0][OCM == 2 ? j : 0] = mfma16x16x32<DT>(av, bq[j], P[OCM == 2 ? i : 0][OCM == 2 ? j : 0]);
-                    else acc[i][j] = mfma16x16x32<DT>(av, bq[j], acc[i][j]);
+                    if (OCM == 2) P[OCM == 2 ? i : 0][OCM == 2 ? j : 0] = mfma16x16x32<DT>(bq[j], av, P[OCM == 2 ? i : 0][OCM == 2 ? j : 0]);
+                    else acc[i][j] = mfma16x16x32<DT>(bq[j], av, acc[i][j]);
                 }
             }
         }
@@ -579,14 +586,18 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
             // row sums of the other waves (next step, after the barrier).
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const float sf = act_to_float<DT>((uint16_t)sb[j]);
-                const float d = sf - act_to_float<DT>((uint16_t)sbn[j]);
-                cz[j] = -sf * (1.0f + (QT ? (float)zb[j] : 8.0f) * 0.0625f);
 #pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const floatx4& p = P[OCM == 2 ? i : 0][OCM == 2 ? j : 0];
+                for (int jj = 0; jj < 4; ++jj) {
+                    const uint32_t sw = jj < 2 ? sb[j].x : sb[j].y, nw = jj < 2 ? sbn[j].x : sbn[j].y;
+                    const float sf = act_to_float<DT>((uint16_t)(sw >> (16 * (jj & 1))));
+                    const float d = sf - act_to_float<DT>((uint16_t)(nw >> (16 * (jj & 1))));
+                    const float z = QT ? (float)((zb[j] >> (8 * jj)) & 0xFFu) : 8.0f;
+                    cz[j][jj] = -sf * (1.0f + z * 0.0625f);
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(d, p[jj], acc[i][j][jj]);
+                    for (int i = 0; i < MI; ++i) {
+                        const floatx4& p = P[OCM == 2 ? i : 0][OCM == 2 ? j : 0];
+                        acc[i][j][jj] = __builtin_fmaf(d, p[jj], acc[i][j][jj]);
+                    }
                 }
             }
             put_s(par);
@@ -615,12 +626,12 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
     // Tail: the scales of the first tail step's successor were requested
     // by the loop (or the prologue); the second tail step is the last, and
     // its successor's scale is 0.
-    const uint32_t no_scale[NJ] = {};
+    const uint2 no_scale[NJ] = {};
     if (st < steps) step(st, a0, b0, sb0, zb0, sb1, a2, b2, sb2, zb2, true);
     if (st + 1 < steps) step(st + 1, a1, b1, sb1, zb1, no_scale, a0, b0, sb0, zb0, true);
     wait_vmcnt<0>();
 
-    floatx4 Sf[MI];
+    float Sf[MI];
     if (OCM == 1) {
         put_s(0);
         stage_barrier();
@@ -633,30 +644,49 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j], Sf[i][jj], acc[i][j][jj]);
+                for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j][jj], Sf[i], acc[i][j][jj]);
     }
 
-    // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l%16 of each block.
+    // Epilogue: per tile, lane l writes row l%16 of the row block, columns
+    // 4*(l/16) .. +3 of the n-tile: one 8-byte store where the four columns
+    // exist and C's rows keep them 8-byte aligned.
+    const bool vec = ((a.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 7) == 0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         if (nt_of(j) >= NT) continue;
-        const int64_t n = nt_of(j) * 16 + r;
-        const float bv = a.bias && n < a.Nst ? act_to_float<DT>(a.bias[n]) : 0.f;
-        // OCM 1: the row's only scale and zero; OCM 2: the folded sum is in
-        // units of 1/16 code step. Both factors are exact in fp32.
-        float sf = 16.0f, zf = 0.f;
-        if (OCM == 1) {
-            sf = 16.0f * act_to_float<DT>(a.scales[n]);
-            zf = -(1.0f + (QT ? (float)a.zeros[n] : 8.0f) * 0.0625f);
+        const int64_t n0 = nt_of(j) * 16 + 4 * g4;
+        // OCM 1: the column's only scale and zero; OCM 2: the folded sum is
+        // in units of 1/16 code step. Both factors are exact in fp32.
+        float sf[4], zf[4], bv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int64_t n = n0 + jj;
+            bv[jj] = a.bias && n < a.Nst ? act_to_float<DT>(a.bias[n]) : 0.f;
+            sf[jj] = 16.0f;
+            zf[jj] = 0.f;
+            if (OCM == 1) {
+                sf[jj] = 16.0f * act_to_float<DT>(a.scales[n]);
+                zf[jj] = -(1.0f + (QT ? (float)a.zeros[n] : 8.0f) * 0.0625f);
+            }
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
+            const int64_t m = m0 + wm * (BM / 2) + 16 * i + r;
+            if (m >= a.M) continue;
+            uint16_t o[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int64_t m = m0 + wm * (BM / 2) + 16 * i + 4 * g4 + jj;
-                float v = acc[i][j][jj];
-                v = OCM == 1 ? sf * __builtin_fmaf(zf, Sf[i][jj], v) : sf * v;
-                if (m < a.M && n < a.Nst) a.C[m * a.ldc + n] = to_act_bits<DT>(v + bv);
+                const float v = acc[i][j][jj];
+                o[jj] = to_act_bits<DT>((OCM == 1 ? sf[jj] * __builtin_fmaf(zf[jj], Sf[i], v) : sf[jj] * v) + bv[jj]);
+            }
+            uint16_t* dst = a.C + m * a.ldc + n0;
+            if (vec && n0 + 3 < a.Nst) {
+                *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                       (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if (n0 + jj < a.Nst) dst[jj] = o[jj];
             }
         }
     }
@@ -695,7 +725,7 @@ __global__ __launch_bounds__(512) void mfma_wide_kernel(MfmaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g4 = lane >> 4;
     int64_t ty, tx;
-    xcd_tile(a, ty, tx);
+    xcd_tile(a, blockIdx.x, gridDim.x, ty, tx);
     const int64_t m0 = ty * 128;
     const int64_t NT = a.N / 16;
     const int64_t steps = a.KTT;

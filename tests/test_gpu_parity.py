@@ -644,6 +644,36 @@ def test_ring_tiles(M, N, K, G, qtype, dtype, bias):
     assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
 
 
+# The 128 x 256 and 128 x 512 tiles store four adjacent outputs of a row with
+# one 8-byte store when C's row stride keeps them aligned; an odd stride takes
+# the element-wise stores. Sentinels past column N must survive.
+ODD_LDC = [
+    # (M, N, K, G, qtype, dtype): kernel reached
+    (2048, 4096, 256, -1, UINT4B8, "bf16"),  # ring, one group per row
+    (2048, 4096, 512, 256, UINT4, "f16"),    # ring, groups of 256
+    (4096, 4096, 256, -1, UINT4, "f16"),     # 128 x 512 tiles
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,qtype,dtype", ODD_LDC,
+                         ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-G{c[3]}-q{c[4]}-{c[5]}" for c in ODD_LDC])
+@pytest.mark.parametrize("pad", [3, 4])
+def test_tiled_output_strides(M, N, K, G, qtype, dtype, pad):
+    print(f"[case] tiled stride M={M} N={N} K={K} G={G} qtype={qtype} {dtype} pad={pad}", flush=True)
+    case = _case(29, M, N, K, G, qtype, dtype, with_bias=True)
+    packed = repack(case)
+    _, _, _, A, b = to_dev(case)
+    big = torch.full((M, N + pad), 1234.0, dtype=case.torch_dtype, device=DEV)
+    C = w4.gemm(A, packed, N, K, G, qtype, bias=b, out=big[:, :N], path=MFMA)
+    torch.cuda.synchronize()
+    assert torch.all(big[:, N:] == 1234.0), "a store landed past column N"
+    rows = sample_rows(M)
+    err = rel_err_rows(C, oracle_ref(case, rows=rows), rows)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
+    C2 = w4.gemm(A, packed, N, K, G, qtype, bias=b, path=MFMA)
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "strided and contiguous outputs differ"
+
+
 # Long sums of non-zero-mean activations. The offset-corrected kernels feed
 # the MFMA exact operand values with a constant offset (b = c0 + c1*q) and
 # take the offset back out with row sums S = sum A; with A ~ N(mu, 1) the
