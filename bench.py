@@ -293,6 +293,51 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(run_dir):
+    """{dispatch id: (kernel name, {counter: value})} from a rocprofv3 --pmc
+    csv directory (run_counter_collection.csv)."""
+    import csv
+    out = {}
+    with open(os.path.join(run_dir, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            d = out.setdefault(int(r["Dispatch_Id"]), (r["Kernel_Name"], {}))
+            d[1][r["Counter_Name"]] = d[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, copy_mib, commands):
+    """The HBM traffic of the skinny decode kernels from four rocprofv3 runs:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of every skinny dispatch of
+    the decode step, each scaled by what the same counter reads for a plain
+    copy of known size (only the copy dispatches of the calibration run: those
+    that read; the fill that creates the buffer reads nothing)."""
+    copy_kib = copy_mib * 1024.0
+    fetch = [v["FETCH_SIZE"] for k, v in _counter_rows(fetch_dir).values() if "skinny" in k]
+    write = [v["WRITE_SIZE"] for k, v in _counter_rows(write_dir).values() if "skinny" in k]
+    cal_f = [v["FETCH_SIZE"] for _, v in _counter_rows(cal_fetch_dir).values() if v["FETCH_SIZE"] > 0.25 * copy_kib]
+    cal_w = [v["WRITE_SIZE"] for _, v in _counter_rows(cal_write_dir).values() if v["WRITE_SIZE"] > 0.25 * copy_kib]
+    ff = copy_kib / (sum(cal_f) / len(cal_f))
+    wf = copy_kib / (sum(cal_w) / len(cal_w))
+    f_mean, w_mean = sum(fetch) / len(fetch), sum(write) / len(write)
+    wl = wi.WORKLOADS["decode_sym"]
+    algo = sum(algorithmic_bytes(M, N, K, wl["G"], wl["qtype"], False) for (M, N, K) in wl["shapes"]) / len(wl["shapes"])
+    return {
+        "kernel": "skinny decode kernels (all variants the 12-GEMM decode step launches)",
+        "kernel_source_hash": kernel_source_hash(),
+        "commands": commands,
+        "calibration": {"copy_bytes": int(copy_kib * 1024), "copy_dispatches": len(cal_f),
+                        "FETCH_SIZE_KB": sum(cal_f) / len(cal_f), "WRITE_SIZE_KB": sum(cal_w) / len(cal_w),
+                        "fetch_factor": ff, "write_factor": wf},
+        "dispatches": len(fetch),
+        "FETCH_SIZE_KB_mean": f_mean,
+        "WRITE_SIZE_KB_mean": w_mean,
+        "hbm_bytes_per_launch": int(round((f_mean * ff + w_mean * wf) * 1024)),
+        "algorithmic_bytes_per_launch": algo,
+        "note": "mean over every skinny dispatch of the commands above (the step's 12 shapes in equal numbers); "
+                "each counter scaled by its factor from the copy dispatches of the calibration run",
+    }
+
+
 def prefill_rates(quick=False):
     """Prefill workload on the MFMA kernel: TFLOP/s per shape and in total.
     quick: no warm-up and 3 replays (for counter runs under a profiler)."""
@@ -579,6 +624,9 @@ def main():
                     help="only time one extra workload and print its JSON (the commands the profiles use)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time the prefill workload (MFMA kernel, and the dense variant) and print its JSON")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="write profiles/skinny_decode_counters.json from four rocprofv3 --pmc csv directories "
+                         "(FETCH_SIZE and WRITE_SIZE of the decode step, then of --calibration-copy 256)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer 10 times (a known-size workload that calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -588,6 +636,19 @@ def main():
               "(the W4A16 path here is a single-GPU kernel; across GPUs the weight would be split along N or K)",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_counters:
+        fd, wd, cfd, cwd = args.summarize_counters
+        cmds = [f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex skinny -f csv -d {fd} -o run -- python3 bench.py "
+                "--no-extras --no-cpu-baseline --no-breakdown --steps 4 --warmup 1",
+                f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex skinny -f csv -d {wd} -o run -- python3 bench.py "
+                "--no-extras --no-cpu-baseline --no-breakdown --steps 4 --warmup 1",
+                f"rocprofv3 --pmc FETCH_SIZE -f csv -d {cfd} -o run -- python3 bench.py --calibration-copy 256",
+                f"rocprofv3 --pmc WRITE_SIZE -f csv -d {cwd} -o run -- python3 bench.py --calibration-copy 256"]
+        rec = summarize_counters(fd, wd, cfd, cwd, 256, cmds)
+        with open(os.path.join(ROOT, "profiles", "skinny_decode_counters.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec), flush=True)
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -696,7 +757,7 @@ def main():
         # workload, 2*M*N*K per GEMM over its measured duration, summed over
         # the 16 prefill GEMMs, against the dense fp16/bf16 MFMA peak.
         result["roofline_prefill"] = {
-            "kernel": "tiled MFMA GEMM (three-stage ring), prefill workload",
+            "kernel": "tiled MFMA GEMM (128 x 512 and 128 x 256 tiles), prefill workload",
             "bound": "mfma",
             "achieved": pre["tflops"],
             "peak": MFMA_PEAK_TFLOPS,

@@ -88,6 +88,35 @@ __device__ __forceinline__ TileBufs tile_bufs(const MfmaArgs& a, int64_t m0, int
     return t;
 }
 
+// Output staging of the tiled kernels' epilogues: a wave's rows x 64
+// columns of C in LDS, 128 bytes per row, the 16-byte chunks of a row
+// XOR-swizzled by row/2 so that the 16 rows one write instruction touches
+// (lane l: row l%16, 8 bytes at column 4*(l/16)) fall in distinct banks.
+__device__ __forceinline__ int stage_chunk(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
+
+// The four adjacent outputs (packed act values) of lane (r, g4) for row
+// `row` and n-tile j of the wave.
+__device__ __forceinline__ void stage_put(unsigned char* stage, int row, int j, int g4, uint2 packed) {
+    *reinterpret_cast<uint2*>(stage + stage_chunk(row, 2 * j + (g4 >> 1)) + 8 * (g4 & 1)) = packed;
+}
+
+// Stores the wave's ROWS x 64 staged outputs to C rows mrow0 + row, columns
+// n0 .. n0 + 63: per instruction 8 rows x 128 bytes, lane l chunk l%8 of row
+// l/8. N is a multiple of 8, so a 16-byte chunk lies wholly inside or wholly
+// past it; rows past M are not stored. The wave's own LDS writes complete in
+// order before these reads.
+template <int ROWS>
+__device__ __forceinline__ void stage_flush(const unsigned char* stage, int lane, uint16_t* C, int64_t ldc, int64_t M,
+                                            int64_t Nst, int64_t mrow0, int64_t n0) {
+#pragma unroll
+    for (int q = 0; q < ROWS / 8; ++q) {
+        const int row = 8 * q + (lane >> 3), c = lane & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + stage_chunk(row, c));
+        const int64_t m = mrow0 + row, n = n0 + 8 * c;
+        if (m < M && n < Nst) *reinterpret_cast<u32x4*>(C + m * ldc + n) = v;
+    }
+}
+
 // Tile (ty, tx) of tile `local` of a launch of `count` tiles that covers
 // positions tile0 .. tile0 + count - 1 of the tile order. Workgroups go to
 // the 8 XCDs round-robin (blockIdx % 8); each XCD takes a contiguous eighth
@@ -647,10 +676,16 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
                 for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j][jj], Sf[i], acc[i][j][jj]);
     }
 
-    // Epilogue: per tile, lane l writes row l%16 of the row block, columns
-    // 4*(l/16) .. +3 of the n-tile: one 8-byte store where the four columns
-    // exist and C's rows keep them 8-byte aligned.
-    const bool vec = ((a.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 7) == 0);
+    // Epilogue. Per tile, lane l holds row l%16 of the row block, columns
+    // 4*(l/16) .. +3 of the n-tile. Where C's rows are 16-byte aligned, the
+    // wave stages its BM/2 x 64 outputs in its own part of the (now idle)
+    // activation stages and writes whole 128-byte row segments; otherwise
+    // each lane stores its four outputs (one 8-byte store where C's rows
+    // keep them 8-byte aligned).
+    const uintptr_t cbase = reinterpret_cast<uintptr_t>(a.C);
+    const bool vec16 = ((a.ldc & 7) == 0) && ((cbase & 15) == 0);
+    const bool vec = ((a.ldc & 3) == 0) && ((cbase & 7) == 0);
+    unsigned char* stage = (wave < 4 ? a0 : a1) + (wave & 3) * (BM * 64);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         if (nt_of(j) >= NT) continue;
@@ -672,17 +707,21 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int64_t m = m0 + wm * (BM / 2) + 16 * i + r;
-            if (m >= a.M) continue;
             uint16_t o[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const float v = acc[i][j][jj];
                 o[jj] = to_act_bits<DT>((OCM == 1 ? sf[jj] * __builtin_fmaf(zf[jj], Sf[i], v) : sf[jj] * v) + bv[jj]);
             }
+            const uint2 packed = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+            if (vec16) {
+                stage_put(stage, 16 * i + r, j, g4, packed);
+                continue;
+            }
+            if (m >= a.M) continue;
             uint16_t* dst = a.C + m * a.ldc + n0;
             if (vec && n0 + 3 < a.Nst) {
-                *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
-                                                       (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+                *reinterpret_cast<uint2*>(dst) = packed;
             } else {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
@@ -690,6 +729,7 @@ __global__ __launch_bounds__(512) void mfma_ring_kernel(MfmaArgs a) {
             }
         }
     }
+    if (vec16) stage_flush<BM / 2>(stage, lane, a.C, a.ldc, a.M, a.Nst, m0 + wm * (BM / 2), nt_of(0) * 16);
 }
 
 // 128 x 512 tiles for one group per row, for large M and N: twice the
@@ -846,10 +886,16 @@ __global__ __launch_bounds__(512) void mfma_wide_kernel(MfmaArgs a) {
     if (g4 == 0) sx[wave][r] = S[0];
     stage_barrier();
 
-    // Epilogue: per tile, lane l writes row 16*i + l%16, columns
-    // 4*(l/16) .. +3 of the n-tile: one 8-byte store where the four columns
-    // exist and C's rows keep them 8-byte aligned.
-    const bool vec = ((a.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.C) & 7) == 0);
+    // Epilogue. Per tile, lane l holds row 16*i + l%16, columns
+    // 4*(l/16) .. +3 of the n-tile. Where C's rows are 16-byte aligned, the
+    // wave stages its 128 x 64 outputs in its own 16 KB of the (now idle)
+    // stage buffers, then writes whole 128-byte row segments: 16 stores of
+    // 8 rows x 128 bytes. Otherwise each lane stores its four outputs (one
+    // 8-byte store where C's rows keep them 8-byte aligned).
+    const uintptr_t cbase = reinterpret_cast<uintptr_t>(a.C);
+    const bool vec16 = ((a.ldc & 7) == 0) && ((cbase & 15) == 0);
+    const bool vec8 = ((a.ldc & 3) == 0) && ((cbase & 7) == 0);
+    unsigned char* stage = (wave < 2 ? a0 : wave < 4 ? a1 : wave < 6 ? b0 : b1) + (wave & 1) * 16384;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         if (nt_of(j) >= NT) continue;
@@ -865,15 +911,19 @@ __global__ __launch_bounds__(512) void mfma_wide_kernel(MfmaArgs a) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int64_t m = m0 + 16 * i + r;
-            if (m >= a.M) continue;
             const float Sr = sx[i][r];
             uint16_t o[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) o[jj] = to_act_bits<DT>(sf[jj] * __builtin_fmaf(zf[jj], Sr, acc[i][j][jj]) + bv[jj]);
+            const uint2 packed = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+            if (vec16) {
+                stage_put(stage, 16 * i + r, j, g4, packed);
+                continue;
+            }
+            if (m >= a.M) continue;
             uint16_t* dst = a.C + m * a.ldc + n0;
-            if (vec && n0 + 3 < a.Nst) {
-                *reinterpret_cast<uint2*>(dst) = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
-                                                       (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+            if (vec8 && n0 + 3 < a.Nst) {
+                *reinterpret_cast<uint2*>(dst) = packed;
             } else {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
@@ -881,6 +931,7 @@ __global__ __launch_bounds__(512) void mfma_wide_kernel(MfmaArgs a) {
             }
         }
     }
+    if (vec16) stage_flush<128>(stage, lane, a.C, a.ldc, a.M, a.Nst, m0, nt_of(0) * 16);
 }
 
 template <int DT, int QT, int OCM, int KT>

@@ -644,14 +644,17 @@ def test_ring_tiles(M, N, K, G, qtype, dtype, bias):
     assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
 
 
-# The 128 x 256 and 128 x 512 tiles store four adjacent outputs of a row with
-# one 8-byte store when C's row stride keeps them aligned; an odd stride takes
-# the element-wise stores. Sentinels past column N must survive.
+# The 128 x 256 tiles store four adjacent outputs of a row with one 8-byte
+# store when C's row stride keeps them aligned, the 128 x 512 tiles whole
+# 16-byte row chunks staged through LDS when the stride is a multiple of 8;
+# an odd stride takes the element-wise stores. Sentinels past column N must
+# survive.
 ODD_LDC = [
     # (M, N, K, G, qtype, dtype): kernel reached
     (2048, 4096, 256, -1, UINT4B8, "bf16"),  # ring, one group per row
     (2048, 4096, 512, 256, UINT4, "f16"),    # ring, groups of 256
     (4096, 4096, 256, -1, UINT4, "f16"),     # 128 x 512 tiles
+    (4096, 4008, 256, -1, UINT4B8, "bf16"),  # 128 x 512 tiles, N not a multiple of 16
 ]
 
 
