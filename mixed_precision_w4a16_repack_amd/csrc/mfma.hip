@@ -934,6 +934,244 @@ __global__ __launch_bounds__(512) void mfma_wide_kernel(MfmaArgs a) {
     if (vec16) stage_flush<128>(stage, lane, a.C, a.ldc, a.M, a.Nst, m0, nt_of(0) * 16);
 }
 
+// 128 x 512 tiles for groups of 128 k or more (G a power of two, K a
+// multiple of 128): the same tile, loads and dequantisation as the one-group
+// kernel, with the group scales applied by rescaling the accumulators.
+// With b = 1 + q/16 into the MFMA and c_g = 1 + z_g/16, the result is
+// C = 16 * sum_g s_g * (P_g - c_g * S_g), P_g and S_g the group's products and
+// row sums. The accumulators hold that sum in units of the current group's
+// scale u_g (u_g = s_g, or 1 for a zero scale): the MFMAs add P_g directly,
+// and at each group end every column is multiplied by u_g / u_{g+1}; the
+// zero-point term -c_g * S_g (times that ratio) follows one step later, once
+// the row sums of the group have met in LDS; the epilogue multiplies by
+// 16 * u of the last group. A group whose scale is zero contributes nothing:
+// its operand mask and magic are zero (b = 0) and its row-sum term is
+// dropped. Only one set of accumulators is needed (the ring kernel keeps a
+// second set for P), so the 128 x 512 tile fits. The products are not
+// transposed here: each lane owns one column per n-tile (n-tile row l%16),
+// so the per-column scale work is four values per lane and the operand mask
+// of that column is the lane's own.
+template <int DT, int QT>
+__global__ __launch_bounds__(512) void mfma_wide_grouped_kernel(MfmaArgs a) {
+    constexpr int MI = 8, NJ = 4;
+    constexpr int ABLK = 32, BBLK = 32;
+    constexpr int APW = ABLK / 8, BPW = BBLK / 8;
+    __shared__ __attribute__((aligned(1024))) unsigned char a0[ABLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char a1[ABLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b0[BBLK * 1024];
+    __shared__ __attribute__((aligned(1024))) unsigned char b1[BBLK * 1024];
+    // Row sums of a group: [parity][row block][4 row groups] of floatx4.
+    __shared__ floatx4 sx[2][MI][4];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g4 = lane >> 4;
+    int64_t ty, tx;
+    xcd_tile(a, blockIdx.x, gridDim.x, ty, tx);
+    const int64_t m0 = ty * 128;
+    const int64_t NT = a.N / 16;
+    const int64_t steps = a.KTT;
+    const int64_t ntb = tx * 32;
+    const TileBufs tb = tile_bufs(a, m0, 128, ntb, 32);
+    const int64_t gsteps = (int64_t)1 << (a.gshift - 7);  // K steps per group
+
+    auto rsrc = [&](const void* base, uint32_t bytes, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
+    };
+    uint32_t a_off[APW];
+#pragma unroll
+    for (int t = 0; t < APW; ++t) {
+        const int b = wave * APW + t;
+        int64_t row = m0 + 16 * (b >> 2) + r;
+        if (row > a.M - 1) row = a.M - 1;
+        a_off[t] = (uint32_t)(((row - tb.mb) * a.lda + 8 * g4) * 2);
+    }
+    uint32_t b_tile[BPW];
+#pragma unroll
+    for (int t = 0; t < BPW; ++t) {
+        const int64_t nt = ntb + wave * BPW + t;
+        b_tile[t] = (uint32_t)((nt < NT ? nt : NT - 1) - ntb);
+    }
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    auto nt_of = [&](int j) { return ntb + wave * NJ + j; };
+    auto nt_ld = [&](int j) { return nt_of(j) < NT ? nt_of(j) : NT - 1; };
+
+    auto issue = [&](int64_t st, int h, unsigned char* abuf, unsigned char* bbuf) {
+        const bool live = st < steps;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int p = 2 * h + u;
+            const int b = wave * APW + p;
+            const uint32_t kcol = (uint32_t)(st * 128 + 32 * (b & 3));
+            load_lds16(rsrc(tb.A, tb.a_bytes, live), abuf + b * 1024, a_off[p], kcol * 2);
+            load_lds16(rsrc(tb.codes, tb.codes_bytes, live), bbuf + (wave * BPW + p) * 1024, lane16,
+                       (uint32_t)((b_tile[p] * a.KTT + st) * 1024));
+        }
+    };
+    // The scale (and zero point) of group g for the lane's column of each
+    // n-tile (zero past the last group).
+    auto load_group = [&](int64_t g, uint32_t (&sraw)[NJ], uint32_t (&zraw)[NJ]) {
+        const bool live = g < a.Kg;
+        const __amdgpu_buffer_rsrc_t rs_s = rsrc(tb.scales, tb.scales_bytes, live);
+        const __amdgpu_buffer_rsrc_t rs_z = rsrc(tb.zeros, tb.zeros_bytes, live);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const uint32_t so = (uint32_t)(((nt_ld(j) - ntb) * a.Kg + g) * 16);
+            sraw[j] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)r * 2, so * 2, 0);
+            if (QT) zraw[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, (uint32_t)r, so, 0);
+        }
+    };
+
+    const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
+    const u32x4 ones = {one2, one2, one2, one2};
+
+    floatx4 acc[MI][NJ], S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Current group: scale and zero of the lane's column per n-tile, the
+    // operand mask and magic (zero for a zero scale); next group: raw loads.
+    float sc[NJ], zc[NJ], cz[NJ];
+    uint32_t msk[NJ], mag[NJ], sn[NJ], zn[NJ];
+    auto set_group = [&](const uint32_t (&sraw)[NJ], const uint32_t (&zraw)[NJ]) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            sc[j] = act_to_float<DT>((uint16_t)sraw[j]);
+            zc[j] = QT ? (float)(zraw[j] & 0xFFu) : 8.0f;
+            msk[j] = sc[j] != 0.0f ? TopNibble<DT>::kMask : 0u;
+            mag[j] = sc[j] != 0.0f ? TopNibble<DT>::kOne : 0u;
+        }
+    };
+    int par = 0;
+    bool pending = false;
+
+    auto step = [&](int64_t st, const unsigned char* abuf, const unsigned char* bbuf, unsigned char* nabuf,
+                    unsigned char* nbbuf) {
+        if (pending) {
+            // Zero-point term of the group that ended last step: its row sums
+            // passed that step's barrier.
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const floatx4 Sf = sx[par ^ 1][i][g4];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j], Sf[jj], acc[i][j][jj]);
+            }
+            pending = false;
+        }
+        const unsigned char* abase = abuf + lane16;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < 2) issue(st + 1, s, nabuf, nbbuf);
+            if (s == 0 && (st & (gsteps - 1)) == 0) load_group((st >> (a.gshift - 7)) + 1, sn, zn);
+            // Word s of each n-tile (one slice at a time: the group state
+            // takes the registers of a second slice).
+            u32x4 bq[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(bbuf + (wave * NJ + j) * 1024 + lane16 + 4 * s);
+                bq[j] = u32x4{and_or(top_pair_shift<DT, 0>(w), msk[j], mag[j]),
+                              and_or(top_pair_shift<DT, 1>(w), msk[j], mag[j]),
+                              and_or(top_pair_shift<DT, 2>(w), msk[j], mag[j]),
+                              and_or(top_pair_shift<DT, 3>(w), msk[j], mag[j])};
+            }
+            const u32x4 as = *reinterpret_cast<const u32x4*>(abase + (wave * 4 + s) * 1024);
+            S = mfma16x16x32<DT>(as, ones, S);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const u32x4 av = *reinterpret_cast<const u32x4*>(abase + (i * 4 + s) * 1024);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32<DT>(av, bq[j], acc[i][j]);
+            }
+        }
+        if (((st + 1) & (gsteps - 1)) == 0) {
+            // End of a group: hand its row sums over, move the accumulators to
+            // the next group's scale, and keep the zero-point factor.
+            if (r == 0) sx[par][wave][g4] = S;
+            S = floatx4{0.f, 0.f, 0.f, 0.f};
+            const bool last = st + 1 >= steps;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float s_next = last ? 0.0f : act_to_float<DT>((uint16_t)sn[j]);
+                const float u_cur = sc[j] != 0.0f ? sc[j] : 1.0f;
+                const float u_next = s_next != 0.0f ? s_next : 1.0f;
+                const float ratio = last ? 1.0f : u_cur / u_next;
+                cz[j] = sc[j] != 0.0f ? -(1.0f + zc[j] * 0.0625f) * ratio : 0.0f;
+                if (!last) {
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] *= ratio;
+                }
+            }
+            if (!last) set_group(sn, zn);
+            par ^= 1;
+            pending = true;
+        }
+        wait_vmcnt<0>();
+        stage_barrier();
+    };
+
+    {
+        uint32_t s0[NJ], z0[NJ];
+        load_group(0, s0, z0);
+        set_group(s0, z0);
+    }
+    issue(0, 0, a0, b0);
+    issue(0, 1, a0, b0);
+    wait_vmcnt<0>();
+    stage_barrier();
+    int64_t st = 0;
+    for (; st + 2 <= steps; st += 2) {
+        step(st, a0, b0, a1, b1);
+        step(st + 1, a1, b1, a0, b0);
+    }
+    if (st < steps) step(st, a0, b0, a1, b1);
+    if (pending) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const floatx4 Sf = sx[par ^ 1][i][g4];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[i][j][jj] = __builtin_fmaf(cz[j], Sf[jj], acc[i][j][jj]);
+        }
+    }
+
+    // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l%16 of each tile.
+    // Where C's rows are 16-byte aligned the wave stages its 128 x 64 outputs
+    // (2-byte writes) and stores whole 128-byte row segments.
+    const uintptr_t cbase = reinterpret_cast<uintptr_t>(a.C);
+    const bool vec16 = ((a.ldc & 7) == 0) && ((cbase & 15) == 0);
+    unsigned char* stage = (wave < 2 ? a0 : wave < 4 ? a1 : wave < 6 ? b0 : b1) + (wave & 1) * 16384;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if (nt_of(j) >= NT) continue;
+        const int64_t n = nt_of(j) * 16 + r;
+        const float bv = a.bias && n < a.Nst ? act_to_float<DT>(a.bias[n]) : 0.f;
+        const float sf = 16.0f * (sc[j] != 0.0f ? sc[j] : 1.0f);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int row = 16 * i + 4 * g4 + jj;
+                const uint16_t o = to_act_bits<DT>(sf * acc[i][j][jj] + bv);
+                if (vec16) {
+                    *reinterpret_cast<uint16_t*>(stage + stage_chunk(row, 2 * j + (r >> 3)) + 2 * (r & 7)) = o;
+                } else {
+                    const int64_t m = m0 + row;
+                    if (m < a.M && n < a.Nst) a.C[m * a.ldc + n] = o;
+                }
+            }
+        }
+    }
+    if (vec16) stage_flush<128>(stage, lane, a.C, a.ldc, a.M, a.Nst, m0, nt_of(0) * 16);
+}
+
 template <int DT, int QT, int OCM, int KT>
 hipError_t launch_ring_ocm(MfmaArgs a, hipStream_t stream) {
     // 128 x 256 tiles, row-major over m-tiles x n-blocks, one workgroup per
@@ -967,6 +1205,15 @@ hipError_t launch_ring_t(MfmaArgs a, hipStream_t stream) {
             a.tile0 = 0;
             if (a.K % 128) hipLaunchKernelGGL((mfma_wide_kernel<DT, QT, 1>), dim3((unsigned)wide), dim3(512), 0, stream, a);
             else hipLaunchKernelGGL((mfma_wide_kernel<DT, QT, 0>), dim3((unsigned)wide), dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
+    if (!a.one_group) {
+        const int64_t wide = a.m_tiles * ((a.N + 511) / 512);
+        if (wide >= kCUs && (wide % kCUs == 0 || wide >= 4 * kCUs)) {
+            a.n_blocks = (a.N + 511) / 512;
+            a.tile0 = 0;
+            hipLaunchKernelGGL((mfma_wide_grouped_kernel<DT, QT>), dim3((unsigned)wide), dim3(512), 0, stream, a);
             return hipGetLastError();
         }
     }

@@ -627,6 +627,12 @@ RING = [
     (8192, 4096, 256, -1, UINT4, "bf16", True),     # 512 tiles: two rounds
     (8192, 14336, 128, -1, UINT4B8, "bf16", False), # 1792 tiles, a single K step
     (4470, 15872, 128, -1, UINT4B8, "f16", True),   # 1085 tiles: not a multiple of 8 (no XCD grouping)
+    # 128 x 512 tiles with groups of 128 k or more (accumulators rescaled at
+    # each group end).
+    (4096, 4096, 1024, 256, UINT4, "bf16", True),   # 4 groups of 2 steps, zero points
+    (8192, 14336, 512, 128, UINT4, "f16", False),   # 1792 tiles, a group per step
+    (4000, 4008, 768, 256, UINT4B8, "bf16", True),  # ragged M and N, 3 groups
+    (4096, 4096, 384, 128, UINT4B8, "f16", False),  # 3 steps: odd tail step ends the last group
 ]
 
 
@@ -655,6 +661,7 @@ ODD_LDC = [
     (2048, 4096, 512, 256, UINT4, "f16"),    # ring, groups of 256
     (4096, 4096, 256, -1, UINT4, "f16"),     # 128 x 512 tiles
     (4096, 4008, 256, -1, UINT4B8, "bf16"),  # 128 x 512 tiles, N not a multiple of 16
+    (4096, 4096, 512, 256, UINT4, "f16"),    # 128 x 512 tiles, groups of 256
 ]
 
 
@@ -677,6 +684,43 @@ def test_tiled_output_strides(M, N, K, G, qtype, dtype, pad):
     assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "strided and contiguous outputs differ"
 
 
+# Groups on the 128 x 512 tiles: the accumulators are carried in units of
+# the current group's scale and rescaled at each group end, and a group whose
+# scale is zero is masked out of the products. Scales spanning three decades
+# (ratios up to 1000 between neighbouring groups) and zero scales (a single
+# group of some columns, a whole column, the first and the last group) must
+# still match the oracle.
+@pytest.mark.parametrize("qtype,dtype,G", [(UINT4, "bf16", 256), (UINT4B8, "f16", 128)])
+@pytest.mark.parametrize("pattern", ["decades", "zeros"])
+def test_grouped_wide_scales(qtype, dtype, G, pattern):
+    M, N, K = 4096, 4096, 2048
+    print(f"[case] grouped wide scales {pattern} qtype={qtype} {dtype} G={G}", flush=True)
+    case = _case(31, M, N, K, G, qtype, dtype, with_bias=True)
+    sc = case.weight_scale.clone().float()
+    Kg = sc.shape[1]
+    if pattern == "decades":
+        rng = np.random.default_rng(7)
+        sc = sc * torch.from_numpy(10.0 ** -rng.uniform(0, 3, size=sc.shape)).float()
+    else:
+        sc[::7, 1] = 0.0           # one group of every 7th column
+        sc[5, :] = 0.0             # a whole column
+        sc[100:116, 0] = 0.0       # the first group of an n-tile
+        sc[2000:2048, Kg - 1] = 0.0  # the last group of three n-tiles
+    case.weight_scale = sc.to(case.weight_scale.dtype)
+    packed = repack(case)
+    _, _, _, A, b = to_dev(case)
+    C = w4.gemm(A, packed, N, K, G, qtype, bias=b, path=MFMA)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    ref = oracle_ref(case, rows=rows)
+    err = rel_err_rows(C, ref, rows)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
+    if pattern == "zeros":
+        # A column whose scales are all zero is the bias alone (one rounding).
+        got = C[torch.from_numpy(rows).to(DEV), 5].cpu().float()
+        assert torch.equal(got, b[5].cpu().float().expand_as(got))
+
+
 # Long sums of non-zero-mean activations. The offset-corrected kernels feed
 # the MFMA exact operand values with a constant offset (b = c0 + c1*q) and
 # take the offset back out with row sums S = sum A; with A ~ N(mu, 1) the
@@ -694,6 +738,8 @@ SHIFTED = [
     (2048, 4096, 14272, -1, UINT4B8, "f16", 3.0, "centred", MFMA),   # ring with a K tail
     (4096, 4096, 14336, -1, UINT4B8, "f16", 3.0, "centred", MFMA),   # 128 x 512 tiles
     (4096, 4096, 14336, -1, UINT4, "bf16", 3.0, "centred", MFMA),
+    (4096, 4096, 14336, 256, UINT4B8, "f16", 3.0, "centred", MFMA),  # 128 x 512 tiles, rescaled groups
+    (4096, 4096, 14336, 128, UINT4, "bf16", 3.0, "centred", MFMA),
     (64, 4096, 14336, -1, UINT4B8, "f16", 1.0, "uniform", MFMA),     # staged tiles, one group per row
     (64, 4096, 14336, -1, UINT4B8, "f16", 3.0, "centred", MFMA),
     (64, 4096, 14272, -1, UINT4, "f16", 3.0, "centred", MFMA),       # staged tiles with a K tail
