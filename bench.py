@@ -273,7 +273,7 @@ def cpu_baseline(budget_s=12.0):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("skinny.hip", "device_common.h"):
+    for f in ("skinny.hip", "device_common.h", "exchange.h"):
         with open(os.path.join(ROOT, "mixed_precision_w4a16_repack_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -53,6 +53,10 @@ struct SkinnyPlan {
 struct MfmaPlan {
     int BM = 128;  // rows per workgroup
     int BN = 256;  // columns per workgroup
+    bool splitk = false;       // medium-M tiles with K split over workgroups
+    int64_t ksplit = 1;        // workgroups per tile along K
+    int64_t spk = 0;           // K steps of 128 per split
+    size_t partial_bytes = 0;  // fp32 partial tiles in the workspace
 };
 
 // Raises a kernel's dynamic-LDS limit (needed above 64 KB); cached per kernel
@@ -83,7 +87,10 @@ constexpr size_t kScratchBytes = kCounterRegionBytes + ((size_t)8 << 20);
 hipError_t noalloc_scratch(hipStream_t stream, void** out);
 
 SkinnyPlan plan_skinny(int64_t M, const Geometry& g);
-MfmaPlan plan_mfma(int64_t M, const Geometry& g);
+// workspace_cap: the most workspace the call may use (split-K partials and
+// counters); the plan splits K no further than that allows.
+MfmaPlan plan_mfma(int64_t M, const Geometry& g, size_t workspace_cap);
+size_t mfma_workspace(const MfmaPlan& p);
 
 // W4A8 launch plan: MI row blocks of 16 per wave, the grid, and the K split
 // (partial results in the workspace when ksplit > 1).
@@ -121,7 +128,8 @@ hipError_t launch_skinny(const void* A, int64_t M, int64_t lda, const void* pack
                          const void* bias, void* C, int64_t ldc, const SkinnyPlan& p, void* workspace,
                          hipStream_t stream);
 hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed, const Geometry& g, int dtype,
-                       const void* bias, void* C, int64_t ldc, const MfmaPlan& p, hipStream_t stream);
+                       const void* bias, void* C, int64_t ldc, const MfmaPlan& p, void* workspace,
+                       hipStream_t stream);
 hipError_t launch_dequant(const void* packed, const Geometry& g, int dtype, void* dense, int64_t ldw,
                           hipStream_t stream);
 hipError_t launch_a8_quant(const void* A, int64_t M, int64_t K, int64_t lda, int dtype, int8_t* qa, int64_t ldq,

@@ -26,12 +26,29 @@
 // one conflict-free ds_read_b128, reads the packed weight tiles, which are
 // already in B-operand order, and ends with bias in fp32, one rounding to
 // the act dtype, and the store.
+#include <type_traits>
+
 #include "device_common.h"
+#include "exchange.h"
 #include "internal.h"
 #include "lds_stage.h"
 
 namespace w4a16 {
 namespace {
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N - 1 (compile-time
+// indices, e.g. of named LDS stages).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_impl<I + 1, N>(f);
+    }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<0, N>(f);
+}
 
 struct MfmaArgs {
     const uint16_t* A;
@@ -52,6 +69,11 @@ struct MfmaArgs {
     int64_t m_tiles, n_blocks;
     int64_t tile0;  // mfma_ring_kernel: first 128 x 256 tile (row-major over m-tiles x n-blocks)
     int64_t Nst;    // columns of C (N above is rounded up to 16); stores and bias stop at Nst
+    // mfma_splitk_kernel: K steps split over ksplit workgroups of spk steps;
+    // partial tiles and arrival counters in the workspace.
+    int64_t ksplit, spk;
+    float* partials;
+    uint32_t* counters;
 };
 
 // One workgroup's operands as buffer bases and byte extents: rows
@@ -1172,6 +1194,259 @@ __global__ __launch_bounds__(512) void mfma_wide_grouped_kernel(MfmaArgs a) {
     if (vec16) stage_flush<128>(stage, lane, a.C, a.ldc, a.M, a.Nst, m0, nt_of(0) * 16);
 }
 
+// Medium M (up to a few hundred rows), any group size, K a multiple of 128:
+// tiles of BM (32, 64 or 128) rows x 256 columns, K split over `ksplit`
+// workgroups so that the tiles of a narrow M still occupy every CU.
+//  * 8 waves side by side: wave w owns n-tiles 2w and 2w + 1 of the tile and
+//    all BM rows, so each weight word is dequantised once per workgroup and
+//    serves BM/16 row blocks.
+//  * The weight stream sets the pace at these M, so the operands go through
+//    a ring of NS LDS stages (3 for 128 rows, 4 for 64, 6 for 32: as deep as
+//    160 KB allows): the loads of step st + NS - 1 (activation and weight
+//    blocks straight into LDS, the step's scales and zero points into
+//    registers) are requested during step st, and each step ends waiting for
+//    the next one's loads only, with the later NS - 2 steps' loads still in
+//    flight (hand-counted: the counter retires loads in issue order).
+//  * Scale first, as the pages do: each word becomes RN((q - z) * s) in the
+//    act dtype (Dequant), so the MFMA sums are the result; no row sums and no
+//    offset correction, which suits groups of 32 or 64 k.
+//  * With ksplit > 1 each workgroup writes its fp32 partial tile through to
+//    the agent-wide coherence point and bumps the tile's arrival counter; the
+//    last to arrive reads all partials back and adds them in split order (a
+//    fixed order: the result does not depend on which arrives last), adds the
+//    bias and writes C, and clears the counter. The same thread reads the
+//    partials of the accumulators it holds, so no other exchange is needed.
+template <int DT, int QT, int BM, int SPT, int NS>
+__global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
+    static_assert(BM == 32 || BM == 64 || BM == 128, "32, 64 or 128 rows");
+    static_assert(SPT == 1 || SPT == 2 || SPT == 4, "groups per K step");
+    static_assert(NS >= 3 && NS <= 6, "three to six stages");
+    constexpr int MI = BM / 16, NJ = 2;
+    constexpr int ABLK = BM / 16 * 4, BBLK = 16;
+    constexpr int APW = ABLK / 8, BPW = BBLK / 8;  // 1 KB blocks per wave and step
+    constexpr int ASZ = ABLK * 1024, BSZ = BBLK * 1024;
+    // Loads per wave and step: activation and weight blocks, then one scale
+    // (and zero point) per group of the step and n-tile of the wave.
+    constexpr int STEP_LOADS = APW + BPW + SPT * NJ * (1 + QT);
+    static_assert(NS * (ASZ + BSZ) <= 160 * 1024, "stages fit the LDS");
+    static_assert((NS - 2) * STEP_LOADS <= 63, "the loads in flight fit the vmcnt counter");
+    // One LDS object per stage, so that the compiler knows which stage a
+    // direct-to-LDS load writes (the reads of the others need not wait).
+    __shared__ __attribute__((aligned(1024))) unsigned char sa0[ASZ], sb0[BSZ];
+    __shared__ __attribute__((aligned(1024))) unsigned char sa1[ASZ], sb1[BSZ];
+    __shared__ __attribute__((aligned(1024))) unsigned char sa2[ASZ], sb2[BSZ];
+    __shared__ __attribute__((aligned(1024))) unsigned char sa3[NS > 3 ? ASZ : 16], sb3[NS > 3 ? BSZ : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char sa4[NS > 4 ? ASZ : 16], sb4[NS > 4 ? BSZ : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char sa5[NS > 5 ? ASZ : 16], sb5[NS > 5 ? BSZ : 16];
+    __shared__ int s_last;
+    auto abuf = [&](auto I) -> unsigned char* {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return sa0;
+        else if constexpr (i == 1) return sa1;
+        else if constexpr (i == 2) return sa2;
+        else if constexpr (i == 3) return sa3;
+        else if constexpr (i == 4) return sa4;
+        else return sa5;
+    };
+    auto bbuf = [&](auto I) -> unsigned char* {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return sb0;
+        else if constexpr (i == 1) return sb1;
+        else if constexpr (i == 2) return sb2;
+        else if constexpr (i == 3) return sb3;
+        else if constexpr (i == 4) return sb4;
+        else return sb5;
+    };
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g4 = lane >> 4;
+    const int64_t tile = blockIdx.x / a.ksplit, kc = blockIdx.x - tile * a.ksplit;
+    const int64_t ty = tile / a.n_blocks, tx = tile - ty * a.n_blocks;
+    const int64_t m0 = ty * BM;
+    const int64_t NT = a.N / 16;
+    const int64_t ntb = tx * 16;
+    const int64_t st0 = kc * a.spk;
+    const int64_t st1 = st0 + a.spk < a.KTT ? st0 + a.spk : a.KTT;
+    const TileBufs tb = tile_bufs(a, m0, BM, ntb, 16);
+
+    auto rsrc = [&](const void* base, uint32_t bytes, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, live ? (int)bytes : 0, 0x00020000);
+    };
+    // Activation block b = wave*APW + t: row block b/4, K slice b%4.
+    uint32_t a_off[APW];
+#pragma unroll
+    for (int t = 0; t < APW; ++t) {
+        const int b = wave * APW + t;
+        int64_t row = m0 + 16 * (b >> 2) + r;
+        if (row > a.M - 1) row = a.M - 1;
+        a_off[t] = (uint32_t)(((row - tb.mb) * a.lda + 8 * g4) * 2);
+    }
+    uint32_t b_tile[BPW];
+#pragma unroll
+    for (int t = 0; t < BPW; ++t) {
+        const int64_t nt = ntb + wave * BPW + t;
+        b_tile[t] = (uint32_t)((nt < NT ? nt : NT - 1) - ntb);
+    }
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    auto nt_of = [&](int j) { return ntb + wave * NJ + j; };
+    auto nt_ld = [&](int j) { return nt_of(j) < NT ? nt_of(j) : NT - 1; };
+
+    // Scales and zero points of the steps in flight, one slot per stage.
+    uint32_t sraw[NS][SPT][NJ], zraw[NS][SPT][NJ];
+
+    // Requests every load of step st into stage I (past the split's last
+    // step the descriptors have size 0: no memory access, zeros written, and
+    // the same number of loads, which the hand-counted waits rely on).
+    auto issue = [&](int64_t st, auto I) {
+        constexpr int i = decltype(I)::value;
+        const bool live = st < st1;
+#pragma unroll
+        for (int p = 0; p < APW; ++p) {
+            const int b = wave * APW + p;
+            load_lds16(rsrc(tb.A, tb.a_bytes, live), abuf(I) + b * 1024, a_off[p],
+                       (uint32_t)((st * 128 + 32 * (b & 3)) * 2));
+        }
+#pragma unroll
+        for (int p = 0; p < BPW; ++p)
+            load_lds16(rsrc(tb.codes, tb.codes_bytes, live), bbuf(I) + (wave * BPW + p) * 1024, lane16,
+                       (uint32_t)((b_tile[p] * a.KTT + st) * 1024));
+        const __amdgpu_buffer_rsrc_t rs_s = rsrc(tb.scales, tb.scales_bytes, live);
+        const __amdgpu_buffer_rsrc_t rs_z = rsrc(tb.zeros, tb.zeros_bytes, live);
+#pragma unroll
+        for (int gi = 0; gi < SPT; ++gi) {
+            const int64_t g = a.one_group ? 0 : ((st * 128) >> a.gshift) + gi;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t so = (uint32_t)(((nt_ld(j) - ntb) * a.Kg + g) * 16);
+                sraw[i][gi][j] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)r * 2, so * 2, 0);
+                if (QT) zraw[i][gi][j] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, (uint32_t)r, so, 0);
+            }
+        }
+    };
+
+    uint32_t dq_mask = 0x000F000Fu, dq_magic = DT == 0 ? 0x64006400u : 0x43004300u;
+    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
+
+    floatx4 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Step st on stage I; with `more`, it first requests step st + NS - 1
+    // into the stage the previous step freed, and ends waiting for step
+    // st + 1 only; the last NS - 1 steps of the split request nothing and
+    // wait for every load.
+    auto step = [&](int64_t st, auto I, bool more) {
+        constexpr int i = decltype(I)::value;
+        constexpr int inext = (i + NS - 1) % NS;
+        if (more) issue(st + NS - 1, std::integral_constant<int, inext>{});
+        const unsigned char* abase = abuf(I) + lane16;
+        const unsigned char* bb = bbuf(I);
+        typename Dequant<DT>::Params prm[NJ];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (s % (4 / SPT) == 0) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    prm[j] = Dequant<DT>::make((uint16_t)sraw[i][s / (4 / SPT)][j],
+                                               QT ? (int)zraw[i][s / (4 / SPT)][j] : 8);
+            }
+            u32x4 bq[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(bb + (wave * NJ + j) * 1024 + lane16 + 4 * s);
+                bq[j] = Dequant<DT>::apply(w, prm[j], dq_mask, dq_magic);
+            }
+#pragma unroll
+            for (int ii = 0; ii < MI; ++ii) {
+                const u32x4 av = *reinterpret_cast<const u32x4*>(abase + (ii * 4 + s) * 1024);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[ii][j] = mfma16x16x32<DT>(av, bq[j], acc[ii][j]);
+            }
+        }
+        if (more) wait_vmcnt<(NS - 2) * STEP_LOADS>();
+        else wait_vmcnt<0>();
+        stage_barrier();
+    };
+
+    // Prologue: steps st0 .. st0 + NS - 2 into stages 0 .. NS - 2.
+    static_for<NS - 1>([&](auto I) { issue(st0 + decltype(I)::value, I); });
+    wait_vmcnt<(NS - 2) * STEP_LOADS>();
+    stage_barrier();
+    int64_t st = st0;
+    for (; st + NS <= st1; st += NS) static_for<NS>([&](auto I) { step(st + decltype(I)::value, I, true); });
+    // The last (st1 - st) < NS steps: their loads are all requested.
+    static_for<NS - 1>([&](auto I) {
+        if (st + decltype(I)::value < st1) step(st + decltype(I)::value, I, false);
+    });
+    // Every load has landed (the dead ones of the loop's last steps too)
+    // before the workgroup may leave.
+    wait_vmcnt<0>();
+
+    if (a.ksplit > 1) {
+        // Partial tile of split kc: per wave, per (i, j) accumulator, the
+        // 64 lanes' floatx4 (1 KB, one write-through store per lane).
+        float* part = a.partials + (tile * a.ksplit) * (int64_t)(BM * 256) + (int64_t)wave * (MI * NJ * 256);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                store_coherent(part + kc * (int64_t)(BM * 256) + ((i * NJ + j) * 64 + lane) * 4, acc[i][j]);
+        wait_vector_memory();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t prev =
+                __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = prev == (uint32_t)(a.ksplit - 1);
+        }
+        __syncthreads();
+        if (!s_last) return;
+        // Last to arrive: the sum of the ksplit partials in split order
+        // (((p0 + p1) + p2) + ...), whichever split arrived last, all read
+        // back (its own too: the same values it wrote). The loads are
+        // agent-scope atomic loads (sc1), which the compiler tracks; four
+        // accumulators at a time, so 16 reads are in flight together.
+        for (int64_t q0 = 0; q0 < a.ksplit; q0 += 4) {
+#pragma unroll
+            for (int t = 0; t < MI * NJ; ++t) {
+                if (t % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+                const int i = t / NJ, j = t % NJ;
+                floatx4 v[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int64_t q = q0 + b < a.ksplit ? q0 + b : a.ksplit - 1;
+                    v[b] = load_coherent(part + q * (int64_t)(BM * 256) + ((i * NJ + j) * 64 + lane) * 4);
+                }
+                floatx4 sum = q0 == 0 ? v[0] : acc[i][j] + v[0];
+#pragma unroll
+                for (int b = 1; b < 4; ++b)
+                    if (q0 + b < a.ksplit) sum += v[b];
+                acc[i][j] = sum;
+            }
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l%16 of each tile.
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if (nt_of(j) >= NT) continue;
+        const int64_t n = nt_of(j) * 16 + r;
+        if (n >= a.Nst) continue;
+        const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int64_t m = m0 + 16 * i + 4 * g4 + jj;
+                if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(acc[i][j][jj] + bv);
+            }
+    }
+}
+
 template <int DT, int QT, int OCM, int KT>
 hipError_t launch_ring_ocm(MfmaArgs a, hipStream_t stream) {
     // 128 x 256 tiles, row-major over m-tiles x n-blocks, one workgroup per
@@ -1268,8 +1543,40 @@ hipError_t launch_lds_ktail(const MfmaArgs& a, int spt, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Stages of the split-K ring: as many as 160 KB of LDS holds, and as the
+// vmcnt counter (at most 63 outstanding) can count for the steps in flight.
+constexpr int splitk_stages(int BM, int SPT, int QT) {
+    const int by_lds = BM == 128 ? 3 : (BM == 64 ? 4 : 6);
+    const int step_loads = BM / 32 + 2 + SPT * 2 * (1 + QT);
+    const int by_count = 2 + 63 / step_loads;
+    return by_lds < by_count ? by_lds : by_count;
+}
+
+template <int DT, int QT, int BM>
+hipError_t launch_splitk_t(const MfmaArgs& a, const MfmaPlan& p, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.m_tiles * a.n_blocks * a.ksplit));
+    // Groups per K step: 4 (G = 32), 2 (G = 64), else 1.
+    const int spt = a.one_group || a.gshift >= 7 ? 1 : 1 << (7 - a.gshift);
+    switch (spt) {
+        case 4:
+            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 4, splitk_stages(BM, 4, QT)>), grid, dim3(512), 0,
+                               stream, a);
+            break;
+        case 2:
+            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 2, splitk_stages(BM, 2, QT)>), grid, dim3(512), 0,
+                               stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 1, splitk_stages(BM, 1, QT)>), grid, dim3(512), 0,
+                               stream, a);
+            break;
+    }
+    return hipGetLastError();
+}
+
 template <int DT, int QT>
 hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, hipStream_t stream) {
+    if (p.splitk) return launch_splitk_t<DT, QT, 128>(a, p, stream);
     // The ring kernel masks a K tail itself (one group per row); every other
     // K % 128 != 0 case takes the staged kernel's masked instance.
     if (a.K % 128 != 0 && !(p.BN == 256 && spt == 1)) return launch_lds_ktail<DT, QT>(a, spt, stream);
@@ -1286,25 +1593,53 @@ hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, hipStrea
 
 }  // namespace
 
-MfmaPlan plan_mfma(int64_t M, const Geometry& g) {
+MfmaPlan plan_mfma(int64_t M, const Geometry& g, size_t workspace_cap) {
     MfmaPlan p;
-    // 128 x 256 tiles while they give at least one workgroup per CU;
-    // otherwise 64-column tiles (four times the workgroups) with as few rows
-    // as M needs, so that the weight stream still spreads over the chip at
-    // small and medium M.
+    // 128 x 256 tiles while they give at least one workgroup per CU (the
+    // ring kernel, or 128 x 512 tiles when those fill whole rounds).
     const int64_t wide = ((M + 127) / 128) * ((g.Np + 255) / 256);
     if (wide >= kCUs) {
         p.BM = 128;
         p.BN = 256;
-    } else {
-        p.BM = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
-        p.BN = 64;
+        return p;
     }
+    const int64_t KTT = g.Kp / 128;
+    if (M > 128 && g.K % 128 == 0) {
+        // Medium M above 128 rows: 128 x 256 tiles with K split so that the
+        // tiles fill the CUs (each split at least 4 K steps), as far as the
+        // workspace holds the partial tiles. (Up to 128 rows the 64-column
+        // tiles below are faster: the partial-tile exchange costs more than
+        // the split saves.)
+        const int64_t tiles = ((M + 127) / 128) * ((g.Np + 255) / 256);
+        int64_t ks = kCUs / tiles;
+        if (ks > KTT / 4) ks = KTT / 4;
+        if (tiles * (int64_t)sizeof(uint32_t) > (int64_t)kCounterRegionBytes) ks = 1;
+        for (; ks > 1; --ks) {
+            const size_t need = kCounterRegionBytes + (size_t)tiles * ks * 128 * 256 * sizeof(float);
+            if (need <= workspace_cap) break;
+        }
+        if (ks < 1) ks = 1;
+        p.splitk = true;
+        p.BM = 128;
+        p.BN = 256;
+        p.spk = (KTT + ks - 1) / ks;
+        p.ksplit = (KTT + p.spk - 1) / p.spk;
+        p.partial_bytes = p.ksplit > 1 ? (size_t)tiles * p.ksplit * 128 * 256 * sizeof(float) : 0;
+        return p;
+    }
+    // Up to 128 rows, or a K tail: 64-column tiles (four times the
+    // workgroups) with as few rows as M needs, so that the weight stream
+    // still spreads over the chip.
+    p.BM = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+    p.BN = 64;
     return p;
 }
 
+size_t mfma_workspace(const MfmaPlan& p) { return p.ksplit > 1 ? kCounterRegionBytes + p.partial_bytes : 0; }
+
 hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed, const Geometry& g, int dtype,
-                       const void* bias, void* C, int64_t ldc, const MfmaPlan& p, hipStream_t stream) {
+                       const void* bias, void* C, int64_t ldc, const MfmaPlan& p, void* workspace,
+                       hipStream_t stream) {
     const uint8_t* base = static_cast<const uint8_t*>(packed);
     MfmaArgs a;
     a.A = static_cast<const uint16_t*>(A);
@@ -1326,6 +1661,10 @@ hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed
     a.m_tiles = (M + p.BM - 1) / p.BM;
     a.n_blocks = (g.Np + p.BN - 1) / p.BN;
     a.tile0 = 0;
+    a.ksplit = p.ksplit;
+    a.spk = p.splitk ? p.spk : a.KTT;
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.partials = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kCounterRegionBytes) : nullptr;
     const int spt = g.Kg == 1 ? 1 : (g.Ge >= 128 ? 1 : 128 / g.Ge);
     if (dtype == 0) return g.qtype ? launch_mfma_q<0, 1>(a, p, spt, stream) : launch_mfma_q<0, 0>(a, p, spt, stream);
     return g.qtype ? launch_mfma_q<1, 1>(a, p, spt, stream) : launch_mfma_q<1, 0>(a, p, spt, stream);

@@ -29,6 +29,7 @@
 //    implements agent-scope atomic stores and loads (a release fence would
 //    write back the XCD's whole L2).
 #include "device_common.h"
+#include "exchange.h"
 #include "internal.h"
 
 namespace w4a16 {
@@ -62,36 +63,6 @@ struct SkinnyArgs {
     int64_t K;    // activation columns past K read as zero (split kernel; the full-K paths need K % 128 == 0)
     int64_t N;    // columns of C (NT covers N rounded up to 16); the split kernel's stores and bias stop at N
 };
-
-// Cross-workgroup exchange of split-K partial sums. Every access carries the
-// sc1 cache policy (write-through to, or read from, the agent-wide coherence
-// point): stores are agent-scope relaxed atomic stores of 64 bits, which the
-// compiler lowers to sc1 stores; loads are sc1 loads in inline assembly.
-__device__ __forceinline__ void store_coherent(float* p, const floatx4& v) {
-    uint64_t* q = reinterpret_cast<uint64_t*>(p);
-    __hip_atomic_store(q, __builtin_bit_cast(uint64_t, __builtin_shufflevector(v, v, 0, 1)), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, __builtin_shufflevector(v, v, 2, 3)), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-// Four coherent 16-byte loads and the wait for them, in one asm statement so
-// that no compiler-inserted instruction can read the destination registers
-// while the loads are in flight (the compiler does not track asm loads).
-__device__ __forceinline__ void load_coherent4(const float* p0, const float* p1, const float* p2, const float* p3,
-                                               floatx4& v0, floatx4& v1, floatx4& v2, floatx4& v3) {
-    asm volatile(
-        "global_load_dwordx4 %0, %4, off sc1\n\t"
-        "global_load_dwordx4 %1, %5, off sc1\n\t"
-        "global_load_dwordx4 %2, %6, off sc1\n\t"
-        "global_load_dwordx4 %3, %7, off sc1\n\t"
-        "s_waitcnt vmcnt(0)"
-        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
-        : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
-        : "memory");
-}
-// Waits until every vector memory access this wave issued has completed
-// (write-through stores: reached the coherence point).
-__device__ __forceinline__ void wait_vector_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int DT, int QT, int NW, int KT, int SPT>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {

@@ -217,6 +217,10 @@ w4a16_status w4a16_workspace_size(int64_t M, int64_t N, int64_t K, int32_t group
     w4a16_status st = make_geometry(N, K, group_size, W4A16_UINT4B8, &g);
     if (st != W4A16_OK) return st;
     *out_bytes = 0;
+    if (M > 0 && resolve_path(M, path, skinny_max_m) == W4A16_PATH_MFMA) {
+        *out_bytes = mfma_workspace(plan_mfma(M, g, (size_t)-1));
+        return W4A16_OK;
+    }
     if (M > 0 && resolve_path(M, path, skinny_max_m) == W4A16_PATH_SKINNY) {
         const SkinnyPlan p = plan_skinny(M < 16 ? M : 16, g);
         if (p.n_groups * (int64_t)sizeof(uint32_t) > (int64_t)kCounterRegionBytes)
@@ -267,8 +271,20 @@ w4a16_status gemm_impl(const void* A, int64_t M, int64_t lda, const void* packed
         if ((128 * lda + K) * 2 >= (int64_t)1 << 31)
             return fail(W4A16_ERR_UNSUPPORTED, "lda=%lld is too large for the tiled path: need (128*lda + K)*2 < 2^31",
                         (long long)lda);
-        const MfmaPlan p = plan_mfma(M, g);
-        hipError_t e = launch_mfma(A, M, lda, packed, g, dtype, bias, C, ldc, p, stream);
+        // Medium M splits K over workgroups as far as the workspace holds the
+        // partial tiles (none given: no split); the static scratch for the
+        // allocation-free entry.
+        size_t cap = from_scratch ? kScratchBytes : (workspace != nullptr ? workspace_bytes : 0);
+        const MfmaPlan p = plan_mfma(M, g, cap);
+        const size_t need = mfma_workspace(p);
+        if (need > 0 && from_scratch) {
+            hipError_t e = noalloc_scratch(stream, &workspace);
+            if (e != hipSuccess) return hip_fail("static scratch set-up", e);
+        }
+        if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+            return fail(W4A16_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        hipError_t e = launch_mfma(A, M, lda, packed, g, dtype, bias, C, ldc, p, need > 0 ? workspace : nullptr,
+                                   stream);
         if (e != hipSuccess) return hip_fail("mfma kernel launch", e);
         return W4A16_OK;
     }

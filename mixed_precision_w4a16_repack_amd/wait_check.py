@@ -21,7 +21,9 @@ that must have landed:
   two steps back must have landed;
 * ``mfma_lds_kernel`` (two buffers, weights in registers): the step's last
   direct-to-LDS load must have landed, so N must equal the number of
-  vector-memory instructions after it.
+  vector-memory instructions after it;
+* ``mfma_splitk_kernel`` (NS stages, NS its last template argument): every
+  load issued before the barrier NS - 2 steps back must have landed.
 
 A path that reaches the kernel entry (the prologue, which issues more
 stages than it waits for) only needs at least N instructions. Any other
@@ -35,11 +37,22 @@ from __future__ import annotations
 import re
 import sys
 
-# kernel name fragment -> ("barriers", depth) or ("lds", None)
+def _splitk_rule(name: str):
+    """The split-K ring waits across NS - 2 barriers (NS: the last template
+    argument of the mangled name, ...ELi<NS>EEEv...)."""
+    m = re.search(r"ELi(\d+)EEEv", name)
+    if not m:
+        raise ValueError(f"no stage count in {name}")
+    return ("barriers", int(m.group(1)) - 2)
+
+
+# kernel name fragment -> ("barriers", depth), ("lds", None), or a function
+# of the mangled name returning one of those
 RULES = {
     "mfma_ring_kernel": ("barriers", 1),
     "w4a8_ring_kernel": ("barriers", 2),
     "mfma_lds_kernel": ("lds", None),
+    "mfma_splitk_kernel": _splitk_rule,
 }
 
 _VMEM = re.compile(r"^(buffer_|global_|flat_|scratch_)")
@@ -180,7 +193,7 @@ def check_function(name: str, lines) -> list[str]:
             rule = r
     if rule is None:
         return []
-    kind, depth = rule
+    kind, depth = rule(name) if callable(rule) else rule
     blocks, pred = _blocks(lines)
     problems = []
     waits = 0

@@ -221,7 +221,11 @@ def test_select_path(lib):
 
 
 def test_workspace_size(lib):
-    assert w4.workspace_size(256, 4096, 4096, 128) == 0  # tiled path needs none
+    assert w4.workspace_size(2048, 4096, 4096, 128) == 0  # 128 x 256 tiles fill the CUs: no split
+    # medium M: K split over the tiles' workgroups, partial tiles in the workspace
+    assert w4.workspace_size(256, 4096, 4096, 128) > w4.workspace_counter_bytes()
+    assert w4.workspace_size(256, 4096, 4104, -1) == 0  # a K tail takes the unsplit 64-column tiles
+    assert w4.workspace_size(128, 4096, 4096, 128) == 0  # up to 128 rows: the unsplit 64-column tiles
     assert w4.workspace_size(16, 4096, 4096, 128) == 0  # wide weights: K is not split
     ws = w4.workspace_size(16, 1024, 4096, 128)  # narrow weights split K
     assert ws > w4.workspace_counter_bytes()

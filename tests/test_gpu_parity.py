@@ -721,6 +721,42 @@ def test_grouped_wide_scales(qtype, dtype, G, pattern):
         assert torch.equal(got, b[5].cpu().float().expand_as(got))
 
 
+# Medium M (129 up to a few hundred rows, fewer 128 x 256 tiles than CUs):
+# 128 x 256 tiles with K split over workgroups, partial tiles through the
+# workspace, the last to arrive adding them in split order; scale-first
+# dequantisation for every group size. Each case names what it reaches.
+MEDIUM = [
+    # (M, N, K, G, qtype, dtype)
+    (256, 14336, 4096, 64, UINT4B8, "f16"),  # the crossover shape: two m-tiles, 2 splits
+    (129, 4096, 4096, 32, UINT4, "bf16"),    # the first M past the 64-column tiles, 4 groups per K step
+    (200, 4104, 2048, 128, UINT4, "f16"),    # ragged M and N
+    (200, 8192, 4096, -1, UINT4B8, "bf16"),  # one group per row, ragged second m-tile
+    (160, 4096, 14336, 64, UINT4, "f16"),    # long K: 8 splits of 14 steps
+    (256, 1024, 8192, 256, UINT4B8, "bf16"), # 8 tiles, 16 splits
+    (192, 14336, 1664, 64, UINT4B8, "f16"),  # 13 steps in splits of 7 and 6 (odd tails)
+    (384, 14336, 1024, 64, UINT4, "bf16"),   # 168 tiles: no split
+    (512, 14336, 640, 32, UINT4B8, "f16"),   # 224 tiles, 5 steps (a ring of 3 stages: a tail of 2)
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,qtype,dtype", MEDIUM,
+                         ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-G{c[3]}-q{c[4]}-{c[5]}" for c in MEDIUM])
+def test_medium_m_split_k_tiles(M, N, K, G, qtype, dtype):
+    print(f"[case] medium M={M} N={N} K={K} G={G} qtype={qtype} {dtype}", flush=True)
+    case = _case(33, M, N, K, G, qtype, dtype, with_bias=True)
+    packed = repack(case)
+    _, _, _, A, b = to_dev(case)
+    C = w4.gemm(A, packed, N, K, G, qtype, bias=b, path=MFMA)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    err = rel_err_rows(C, oracle_ref(case, rows=rows), rows)
+    assert err <= oracle.TOLERANCE[dtype], f"rel err {err:.3e}"
+    # A second call on the same workspace (its counters were left at zero)
+    # gives the same bits.
+    C2 = w4.gemm(A, packed, N, K, G, qtype, bias=b, path=MFMA)
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+
+
 # Long sums of non-zero-mean activations. The offset-corrected kernels feed
 # the MFMA exact operand values with a constant offset (b = c0 + c1*q) and
 # take the offset back out with row sums S = sum A; with A ~ N(mu, 1) the

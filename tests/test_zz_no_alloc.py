@@ -57,6 +57,24 @@ def test_two_calls_in_a_row_match_the_workspace_entry_point():
         assert err <= oracle.TOLERANCE[dt], f"rel err {err:.3e}"
 
 
+# The medium-M tiles split K over workgroups with their partial tiles in the
+# scratch: two calls in a row, the second smaller, the same split as with a
+# caller workspace.
+SPLIT_K_SEQUENCE = [(256, 2048, 1024, 64, wi.UINT4B8, "f16"), (160, 1024, 1024, 32, wi.UINT4, "bf16")]
+
+
+def test_split_k_tiles_two_calls_in_a_row():
+    for i, (M, N, K, G, qt, dt) in enumerate(SPLIT_K_SEQUENCE):
+        print(f"[case] noalloc split-K tiles call {i}: M={M} N={N} K={K} G={G} qtype={qt} {dt}", flush=True)
+        assert 0 < w4.workspace_size(M, N, K, G, w4.PATH_AUTO) <= 64 * 1024 + (8 << 20)
+        case = wi.make_case(64, M, N, K, G, qt, dt, with_bias=True)
+        C_static, C_ws = _run_pair(case, w4.PATH_AUTO)
+        assert torch.equal(C_static.view(torch.int16), C_ws.view(torch.int16))
+        rows = sample_rows(M)
+        err = rel_err_rows(C_static, oracle_ref(case, rows=rows), rows)
+        assert err <= oracle.TOLERANCE[dt], f"rel err {err:.3e}"
+
+
 def test_tiled_path_needs_no_scratch():
     case = wi.make_case(62, 96, 512, 1024, 128, wi.UINT4B8, "f16", with_bias=True)
     C_static, C_ws = _run_pair(case, w4.PATH_MFMA)
