@@ -163,7 +163,9 @@ w4a16_status w4a16_unpack(const void *packed, int64_t N, int64_t K, int32_t grou
 
 /* Bytes of device workspace w4a16_gemm needs for these arguments (0 if none).
  * out_bytes is a host pointer. The workspace holds split-K partial sums and
- * arrival counters. Its first w4a16_workspace_counter_bytes() bytes must be
+ * arrival counters: of the skinny kernels (M <= 16, narrow weights) and of
+ * the tiled kernel for medium M (129 rows up to where its 128 x 256 tiles
+ * fill the CUs on their own). Its first w4a16_workspace_counter_bytes() bytes must be
  * zero before it is first used; every completed w4a16_gemm call leaves them
  * zero again, so a workspace can be reused for any shape. Calls that share a
  * workspace must be ordered (same stream); overlapping calls race. */
@@ -189,7 +191,10 @@ int32_t w4a16_select_path(int64_t M, int32_t path, int32_t skinny_max_m);
  *           small-M kernel (M > 16 runs it over 16-row slices); MFMA forces
  *           the tiled kernel
  *   workspace, workspace_bytes  device workspace, >= w4a16_workspace_size();
- *           may be NULL when that size is 0
+ *           may be NULL when that size is 0. The skinny path returns
+ *           W4A16_ERR_SIZE for a smaller one; the tiled path splits K no
+ *           further than the given workspace holds (NULL: no split), so it
+ *           only runs slower
  * M == 0 is a no-op. The result does not depend on the workspace contents or
  * on earlier calls (no float atomics: the order of every sum is fixed).
  * The skinny kernel addresses the (at most 16) rows of one launch with 32-bit
@@ -205,12 +210,13 @@ w4a16_status w4a16_gemm(const void *A, int64_t M, int64_t lda, const void *packe
 /* w4a16_gemm for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation.
  * Same arguments, result and errors as w4a16_gemm, without the workspace:
- * the split-K partial sums and arrival counters of the skinny kernels live
- * in a static device array of the library, W4A16_NOALLOC_MAX_WORKSPACE_BYTES
- * bytes (64 KiB of counters + 8 MiB of partial sums) per GPU, held until the
- * process ends. A call that needs more workspace than that (a larger
+ * the split-K partial sums and arrival counters live in a static device
+ * array of the library, W4A16_NOALLOC_MAX_WORKSPACE_BYTES bytes (64 KiB of
+ * counters + 8 MiB of partial sums) per GPU, held until the process ends. A
+ * skinny call that needs more workspace than that (a larger
  * w4a16_workspace_size()) returns W4A16_ERR_SIZE without launching anything;
- * use w4a16_gemm with a caller workspace for it. The call allocates nothing:
+ * use w4a16_gemm with a caller workspace for it. The tiled path splits K no
+ * further than the array holds. The call allocates nothing:
  * no hipMalloc, hipFree or allocating library routine. On the first call
  * that needs the array on a device (that device current), the library looks
  * up its address and clears its counters with a small kernel on `stream`;
