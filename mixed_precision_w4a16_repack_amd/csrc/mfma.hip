@@ -1238,7 +1238,6 @@ __global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char sa3[NS > 3 ? ASZ : 16], sb3[NS > 3 ? BSZ : 16];
     __shared__ __attribute__((aligned(1024))) unsigned char sa4[NS > 4 ? ASZ : 16], sb4[NS > 4 ? BSZ : 16];
     __shared__ __attribute__((aligned(1024))) unsigned char sa5[NS > 5 ? ASZ : 16], sb5[NS > 5 ? BSZ : 16];
-    __shared__ int s_last;
     auto abuf = [&](auto I) -> unsigned char* {
         constexpr int i = decltype(I)::value;
         if constexpr (i == 0) return sa0;
@@ -1388,46 +1387,15 @@ __global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
 
     if (a.ksplit > 1) {
         // Partial tile of split kc: per wave, per (i, j) accumulator, the
-        // 64 lanes' floatx4 (1 KB, one write-through store per lane).
-        float* part = a.partials + (tile * a.ksplit) * (int64_t)(BM * 256) + (int64_t)wave * (MI * NJ * 256);
+        // 64 lanes' floatx4 (1 KB). Ordinary stores: splitk_reduce_kernel,
+        // the next launch on the stream, reads them after the kernel
+        // boundary has made them visible.
+        float* part = a.partials + (tile * a.ksplit + kc) * (int64_t)(BM * 256) + (int64_t)wave * (MI * NJ * 256);
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                store_coherent(part + kc * (int64_t)(BM * 256) + ((i * NJ + j) * 64 + lane) * 4, acc[i][j]);
-        wait_vector_memory();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t prev =
-                __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = prev == (uint32_t)(a.ksplit - 1);
-        }
-        __syncthreads();
-        if (!s_last) return;
-        // Last to arrive: the sum of the ksplit partials in split order
-        // (((p0 + p1) + p2) + ...), whichever split arrived last, all read
-        // back (its own too: the same values it wrote). The loads are
-        // agent-scope atomic loads (sc1), which the compiler tracks; four
-        // accumulators at a time, so 16 reads are in flight together.
-        for (int64_t q0 = 0; q0 < a.ksplit; q0 += 4) {
-#pragma unroll
-            for (int t = 0; t < MI * NJ; ++t) {
-                if (t % 4 == 0) __builtin_amdgcn_sched_barrier(0);
-                const int i = t / NJ, j = t % NJ;
-                floatx4 v[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int64_t q = q0 + b < a.ksplit ? q0 + b : a.ksplit - 1;
-                    v[b] = load_coherent(part + q * (int64_t)(BM * 256) + ((i * NJ + j) * 64 + lane) * 4);
-                }
-                floatx4 sum = q0 == 0 ? v[0] : acc[i][j] + v[0];
-#pragma unroll
-                for (int b = 1; b < 4; ++b)
-                    if (q0 + b < a.ksplit) sum += v[b];
-                acc[i][j] = sum;
-            }
-        }
-        if (threadIdx.x == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int j = 0; j < NJ; ++j) *reinterpret_cast<floatx4*>(part + ((i * NJ + j) * 64 + lane) * 4) = acc[i][j];
+        return;
     }
 
     // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l%16 of each tile.
@@ -1445,6 +1413,34 @@ __global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
                 if (m < a.M) a.C[m * a.ldc + n] = to_act_bits<DT>(acc[i][j][jj] + bv);
             }
     }
+}
+
+// Second half of a split-K launch: C = sum of the ksplit partial tiles in
+// split order (((p0 + p1) + p2) + ..., a fixed order) + bias. Thread t of the
+// grid takes unit t of the partial layout (tile, wave, accumulator (i, j),
+// lane: rows 4*(lane/16) .. +3 of column lane%16 of the 16 x 16 block), so
+// the loads of a wave are 1 KB contiguous per split.
+template <int DT, int BM>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(MfmaArgs a) {
+    constexpr int MI = BM / 16, NJ = 2;
+    constexpr int UNITS = BM * 256 / 4;  // floatx4 units per partial tile
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t tile = u / UNITS;
+    if (tile >= a.m_tiles * a.n_blocks) return;
+    const int rem = (int)(u - tile * UNITS);
+    const int wave = rem / (MI * NJ * 64), acc_idx = (rem / 64) % (MI * NJ), lane = rem % 64;
+    const int i = acc_idx / NJ, j = acc_idx % NJ;
+    const int64_t ty = tile / a.n_blocks, tx = tile - ty * a.n_blocks;
+    const int64_t n = (tx * 16 + wave * NJ + j) * 16 + (lane & 15);
+    const int64_t mrow = ty * BM + 16 * i + 4 * (lane >> 4);
+    if (n >= a.Nst || mrow >= a.M) return;
+    const float* p = a.partials + tile * a.ksplit * (int64_t)(BM * 256) + (int64_t)rem * 4;
+    floatx4 sum = *reinterpret_cast<const floatx4*>(p);
+    for (int64_t q = 1; q < a.ksplit; ++q) sum += *reinterpret_cast<const floatx4*>(p + q * (int64_t)(BM * 256));
+    const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+        if (mrow + jj < a.M) a.C[(mrow + jj) * a.ldc + n] = to_act_bits<DT>(sum[jj] + bv);
 }
 
 template <int DT, int QT, int OCM, int KT>
@@ -1571,12 +1567,23 @@ hipError_t launch_splitk_t(const MfmaArgs& a, const MfmaPlan& p, hipStream_t str
                                stream, a);
             break;
     }
+    if (a.ksplit == 1) return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t units = a.m_tiles * a.n_blocks * (BM * 256 / 4);
+    hipLaunchKernelGGL((splitk_reduce_kernel<DT, BM>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int DT, int QT>
 hipError_t launch_mfma_q(const MfmaArgs& a, const MfmaPlan& p, int spt, hipStream_t stream) {
-    if (p.splitk) return launch_splitk_t<DT, QT, 128>(a, p, stream);
+    if (p.splitk) {
+        switch (p.BM) {
+            case 32: return launch_splitk_t<DT, QT, 32>(a, p, stream);
+            case 64: return launch_splitk_t<DT, QT, 64>(a, p, stream);
+            default: return launch_splitk_t<DT, QT, 128>(a, p, stream);
+        }
+    }
     // The ring kernel masks a K tail itself (one group per row); every other
     // K % 128 != 0 case takes the staged kernel's masked instance.
     if (a.K % 128 != 0 && !(p.BN == 256 && spt == 1)) return launch_lds_ktail<DT, QT>(a, spt, stream);
@@ -1604,30 +1611,32 @@ MfmaPlan plan_mfma(int64_t M, const Geometry& g, size_t workspace_cap) {
         return p;
     }
     const int64_t KTT = g.Kp / 128;
-    if (M > 128 && g.K % 128 == 0) {
-        // Medium M above 128 rows: 128 x 256 tiles with K split so that the
-        // tiles fill the CUs (each split at least 4 K steps), as far as the
-        // workspace holds the partial tiles. (Up to 128 rows the 64-column
-        // tiles below are faster: the partial-tile exchange costs more than
-        // the split saves.)
-        const int64_t tiles = ((M + 127) / 128) * ((g.Np + 255) / 256);
+    if (g.K % 128 == 0) {
+        // Medium M: BM x 256 tiles with K split so that the tiles fill the
+        // CUs (each split at least 4 K steps), as far as the workspace holds
+        // the partial tiles; with too small a workspace for half the CUs,
+        // the 64-column tiles below.
+        const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+        const int64_t tiles = ((M + bm - 1) / bm) * ((g.Np + 255) / 256);
         int64_t ks = kCUs / tiles;
         if (ks > KTT / 4) ks = KTT / 4;
         if (tiles * (int64_t)sizeof(uint32_t) > (int64_t)kCounterRegionBytes) ks = 1;
         for (; ks > 1; --ks) {
-            const size_t need = kCounterRegionBytes + (size_t)tiles * ks * 128 * 256 * sizeof(float);
+            const size_t need = kCounterRegionBytes + (size_t)tiles * ks * bm * 256 * sizeof(float);
             if (need <= workspace_cap) break;
         }
         if (ks < 1) ks = 1;
+        if (tiles * ks < kCUs / 2) goto narrow;
         p.splitk = true;
-        p.BM = 128;
+        p.BM = bm;
         p.BN = 256;
         p.spk = (KTT + ks - 1) / ks;
         p.ksplit = (KTT + p.spk - 1) / p.spk;
-        p.partial_bytes = p.ksplit > 1 ? (size_t)tiles * p.ksplit * 128 * 256 * sizeof(float) : 0;
+        p.partial_bytes = p.ksplit > 1 ? (size_t)tiles * p.ksplit * bm * 256 * sizeof(float) : 0;
         return p;
     }
-    // Up to 128 rows, or a K tail: 64-column tiles (four times the
+narrow:
+    // A K tail (or a small workspace): 64-column tiles (four times the
     // workgroups) with as few rows as M needs, so that the weight stream
     // still spreads over the chip.
     p.BM = M <= 32 ? 32 : (M <= 64 ? 64 : 128);

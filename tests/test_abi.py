@@ -225,7 +225,8 @@ def test_workspace_size(lib):
     # medium M: K split over the tiles' workgroups, partial tiles in the workspace
     assert w4.workspace_size(256, 4096, 4096, 128) > w4.workspace_counter_bytes()
     assert w4.workspace_size(256, 4096, 4104, -1) == 0  # a K tail takes the unsplit 64-column tiles
-    assert w4.workspace_size(128, 4096, 4096, 128) == 0  # up to 128 rows: the unsplit 64-column tiles
+    assert w4.workspace_size(17, 4096, 4096, 128) > 0  # the first M past the skinny path splits K too
+    assert w4.workspace_size(96, 512, 1024, 128) == 0  # too few tiles to fill half the CUs: unsplit
     assert w4.workspace_size(16, 4096, 4096, 128) == 0  # wide weights: K is not split
     ws = w4.workspace_size(16, 1024, 4096, 128)  # narrow weights split K
     assert ws > w4.workspace_counter_bytes()

@@ -58,9 +58,9 @@ def test_two_calls_in_a_row_match_the_workspace_entry_point():
 
 
 # The medium-M tiles split K over workgroups with their partial tiles in the
-# scratch: two calls in a row, the second smaller, the same split as with a
-# caller workspace.
-SPLIT_K_SEQUENCE = [(256, 2048, 1024, 64, wi.UINT4B8, "f16"), (160, 1024, 1024, 32, wi.UINT4, "bf16")]
+# scratch (the first exactly fills its 8 MiB): two calls in a row, the second
+# smaller, the same split as with a caller workspace.
+SPLIT_K_SEQUENCE = [(64, 4096, 4096, 64, wi.UINT4B8, "f16"), (32, 4096, 4096, 32, wi.UINT4, "bf16")]
 
 
 def test_split_k_tiles_two_calls_in_a_row():
