@@ -278,7 +278,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
 // (q - z) * s exactly, rounded once at the end).
 constexpr int kStreamWaves = 8;
 constexpr int kStreamThreads = 64 * kStreamWaves;
-constexpr int kResMaxKt = 4;  // k-tiles per wave in skinny_res_kernel
+constexpr int kResMaxKt = 4;    // K chunks of the split skinny_reg_kernel are multiples of it
+constexpr int kRegKt = 2;       // k-tiles per wave in skinny_reg_kernel (up to 16 waves)
+constexpr int kResShortKt = 2;  // k-tiles per wave in skinny_res_kernel for K <= 4096 (up to 16 waves)
+constexpr int kLongResMaxRows = 4;  // rows of the long-K skinny_res_kernel instances
 constexpr int kStrDepth = 8;  // units in flight per wave in skinny_str_kernel
 
 template <int DT>
@@ -374,16 +377,29 @@ __device__ __forceinline__ void fold(floatx4& acc, const floatx4& P, const float
     for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(sf, __builtin_fmaf(zf, S[jj], P[jj]), acc[jj]);
 }
 
-// Sum over the first nwa waves of red[wave][i][lane], in wave order. The
-// LDS holds 8 waves' slots (launch size 8 * nn_max KB), so all 8 reads are
-// issued at once and only the additions depend on nwa.
-__device__ __forceinline__ floatx4 sum_waves(const floatx4* red, int nn, int i, int nwa, int lane) {
-    floatx4 v[kStreamWaves];
+// fold() where `mine`, else acc unchanged: the scale factor is 0 for the
+// k-tiles another lane group folds (P and S are finite there, so the term is
+// an exact zero).
+template <int DT, int QT>
+__device__ __forceinline__ void fold_if(floatx4& acc, const floatx4& P, const floatx4& S, uint16_t sbits, uint8_t z,
+                                        bool mine) {
+    const float sf = mine ? act_to_float<DT>(sbits) : 0.0f;
+    const float zf = -(magic_base<DT>() + (QT ? (float)z : 8.0f));
 #pragma unroll
-    for (int q = 0; q < kStreamWaves; ++q) v[q] = red[(q * nn + i) * 64 + lane];
+    for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(sf, __builtin_fmaf(zf, S[jj], P[jj]), acc[jj]);
+}
+
+// Sum over the first nwa waves of red[wave][i][lane], in wave order. The
+// LDS holds MAXW waves' slots (launch size MAXW * nn_max KB), so all MAXW
+// reads are issued at once and only the additions depend on nwa.
+template <int MAXW = kStreamWaves>
+__device__ __forceinline__ floatx4 sum_waves(const floatx4* red, int nn, int i, int nwa, int lane) {
+    floatx4 v[MAXW];
+#pragma unroll
+    for (int q = 0; q < MAXW; ++q) v[q] = red[(q * nn + i) * 64 + lane];
     floatx4 tot = v[0];
 #pragma unroll
-    for (int q = 1; q < kStreamWaves; ++q)
+    for (int q = 1; q < MAXW; ++q)
         if (q < nwa) tot += v[q];
     return tot;
 }
@@ -391,14 +407,14 @@ __device__ __forceinline__ floatx4 sum_waves(const floatx4* red, int nn, int i, 
 // The first `nwa` waves have written red[wave][i][lane] for i < nn; wave q
 // of the workgroup's nw waves sums them, in wave order, for n-tiles q,
 // q + nw, ..., adds the bias, rounds once and stores rows < M.
-template <int DT>
+template <int DT, int MAXW = kStreamWaves>
 __device__ __forceinline__ void finish_tiles(const SkinnyArgs& a, const floatx4* red, int nn, int nwa, int64_t g,
                                              int64_t groups) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g4 = lane >> 4;
     const int nw = blockDim.x >> 6;  // short K: fewer than 8 waves
     for (int i = wave; i < nn; i += nw) {
-        const floatx4 tot = sum_waves(red, nn, i, nwa, lane);
+        const floatx4 tot = sum_waves<MAXW>(red, nn, i, nwa, lane);
         const int64_t n = (g + (int64_t)i * groups) * 16 + r;
         const float bv = a.bias ? act_to_float<DT>(a.bias[n]) : 0.f;
 #pragma unroll
@@ -415,7 +431,7 @@ __device__ __forceinline__ void finish_tiles(const SkinnyArgs& a, const floatx4*
 // (agent-scope counter, as in skinny_kernel) reads the ksplit partials back
 // with coherent loads and sums them in chunk order, so the result does not
 // depend on which one arrives last. Partial (g, c, i): 64 lanes x 16 bytes.
-template <int DT>
+template <int DT, int MAXW = kStreamWaves>
 __device__ __forceinline__ void finish_split(const SkinnyArgs& a, const floatx4* red, int* flag, int nn, int nwa,
                                              int64_t g, int c) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -423,7 +439,7 @@ __device__ __forceinline__ void finish_split(const SkinnyArgs& a, const floatx4*
     const int nw = blockDim.x >> 6;
     float* part = a.partials + g * a.ksplit * (int64_t)a.nn_max * 256;
     for (int i = wave; i < nn; i += nw) {
-        const floatx4 tot = sum_waves(red, nn, i, nwa, lane);
+        const floatx4 tot = sum_waves<MAXW>(red, nn, i, nwa, lane);
         store_coherent(part + (((int64_t)c * a.nn_max + i) * 64 + lane) * 4, tot);
     }
     wait_vector_memory();
@@ -475,9 +491,12 @@ __device__ __forceinline__ void fold_scaled(floatx4& acc, const floatx4& P, uint
     for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(sf, P[jj], acc[jj]);
 }
 
+// Waves of skinny_reg_kernel, at most (its K chunks are at most 32 k-tiles).
+constexpr int kRegMaxWaves = (32 + kRegKt - 1) / kRegKt;
+
 template <int DT, int QT, int FW, int NNM>
-__global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a) {
-    constexpr int KTM = kResMaxKt;  // k-tiles per wave (the grid has ceil(KTT / 4) waves)
+__global__ __launch_bounds__(64 * kRegMaxWaves) void skinny_reg_kernel(SkinnyArgs a) {
+    constexpr int KTM = kRegKt;  // k-tiles per wave (the grid has ceil(kc_tiles / KTM) waves)
     constexpr int NB = 4 / FW;      // fold blocks per k-tile
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     floatx4* red = reinterpret_cast<floatx4*>(smem);
@@ -577,12 +596,21 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_reg_kernel(SkinnyArgs a
         red[(wave * nn + i) * 64 + lane] = acc;
     }
     __syncthreads();
-    if (a.ksplit == 1) finish_tiles<DT>(a, red, nn, nwaves, g, a.n_groups);
-    else finish_split<DT>(a, red, reinterpret_cast<int*>(red + kStreamWaves * a.nn_max * 64), nn, nwaves, g, c);
+    if (a.ksplit == 1) finish_tiles<DT, kRegMaxWaves>(a, red, nn, nwaves, g, a.n_groups);
+    else finish_split<DT, kRegMaxWaves>(a, red, reinterpret_cast<int*>(red + kRegMaxWaves * a.nn_max * 64), nn, nwaves, g, c);
+}
+
+// Waves of skinny_res_kernel, at most: 16 with 2 k-tiles per wave (K <=
+// 4096) and with 8 k-tiles per wave (long K, up to 4 rows), else 8. A wave
+// computes only after all of its loads are issued, and the loads of a CU
+// queue up behind each other: with more waves per CU, one wave's MFMAs
+// overlap other waves' loads.
+__host__ __device__ constexpr int res_max_waves(int ktw, int mr) {
+    return ktw <= kResShortKt || (ktw == 8 && mr <= kLongResMaxRows) ? 16 : kStreamWaves;
 }
 
 template <int DT, int QT, int FW, int NNM, int KTW, int MR>
-__global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(64 * res_max_waves(KTW, MR)) void skinny_res_kernel(SkinnyArgs a) {
     constexpr int NB = 4 / FW;  // fold blocks per k-tile
     constexpr int LD = act_lds_ld<KTW>();
     constexpr int kMaxRows = MR;  // largest M this instance is launched for
@@ -592,22 +620,24 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
     const int nwaves = blockDim.x >> 6;
     const int r = lane & 15, g4 = lane >> 4;
-    const int rr = r < a.M ? r : a.M - 1;
     const int nn = (int)((a.NT - blockIdx.x + gridDim.x - 1) / gridDim.x);
-    const int64_t kt0 = (int64_t)wave * KTW;
-    const int kc = (int)(a.KTT - kt0 < KTW ? a.KTT - kt0 : KTW);  // >= 1: the grid has ceil(KTT / KTW) waves
+    // Wave w takes k-tiles w, w + nwaves, w + 2 nwaves, ...: the waves'
+    // loads of one round cover adjacent k-tiles of the n-tile.
+    const int64_t kt0 = wave;
+    const int kc = (int)((a.KTT - wave + nwaves - 1) / nwaves);  // >= 1, <= KTW: the grid has ceil(KTT / KTW) waves
     uint16_t* As = reinterpret_cast<uint16_t*>(smem) + (size_t)wave * a.M * LD;
 
     uint32_t dq_mask = 0x000F000Fu, dq_magic = kMagic<DT>;
     asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
 
-    // 1. The wave's activation slice, rows [0, M) x k in [128*kt0, 128*(kt0+kc)),
-    //    into registers (16-byte chunks, row-major over the slice). Only the M
-    //    real rows are read: the padding rows of the MFMA operand come from
-    //    LDS later, which has about three times the return bandwidth.
-    //    Chunk c is row c / CPR, column chunk c % CPR (CPR = KTW*16, a
-    //    constant); columns past the wave's kc k-tiles are not loaded. K is
-    //    a multiple of 128 here, so every loaded column is < K.
+    // 1. The wave's activation slice, rows [0, M) of its kc k-tiles, into
+    //    registers (16-byte chunks, row-major over the slice, the wave's
+    //    k-tiles side by side). Only the M real rows are read: the padding
+    //    rows of the MFMA operand come from LDS later, which has about three
+    //    times the return bandwidth. Chunk c is row c / CPR, column chunk
+    //    c % CPR (CPR = KTW*16, a constant), that is chunk col % 16 of the
+    //    wave's k-tile col / 16; columns past the wave's kc k-tiles are not
+    //    loaded. K is a multiple of 128 here, so every loaded column is < K.
     constexpr int CPR = KTW * 16;
     const int nch = a.M * CPR;
     const int ccols = kc * 16;
@@ -617,7 +647,8 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
         const int c = lane + 64 * t;
         const int m = c / CPR, col = c - m * CPR;
         if (c < nch && col < ccols)
-            ach[t] = *reinterpret_cast<const u32x4*>(a.A + (int64_t)m * a.lda + kt0 * 128 + 8 * col);
+            ach[t] = *reinterpret_cast<const u32x4*>(a.A + (int64_t)m * a.lda + (kt0 + (col >> 4) * nwaves) * 128 +
+                                                     8 * (col & 15));
     }
     const WeightBufs wb(a);
     // 2. Every weight tile, scale and zero of the wave, in consumption order
@@ -632,9 +663,10 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
         for (int i = 0; i < NNM; ++i) {
             const int64_t nt = blockIdx.x + (int64_t)i * gridDim.x;
             const bool valid = i < nn && j < kc;
-            w[j][i] = load_tile(wb, a, nt, kt0 + j, lane, valid);
+            w[j][i] = load_tile(wb, a, nt, kt0 + j * nwaves, lane, valid);
 #pragma unroll
-            for (int f = 0; f < NB; ++f) load_scale_zero<QT, FW>(wb, a, nt, kt0 + j, f, r, valid, sb[j][i][f], zb[j][i][f]);
+            for (int f = 0; f < NB; ++f)
+                load_scale_zero<QT, FW>(wb, a, nt, kt0 + j * nwaves, f, r, valid, sb[j][i][f], zb[j][i][f]);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -647,40 +679,85 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
         if (c < nch && col < ccols) *reinterpret_cast<u32x4*>(As + m * LD + 8 * col) = ach[t];
     }
 
-    // 4. k-tile by k-tile: the activation fragments (padding rows read row
-    //    M-1) and S once, then every n-tile. P starts from zero, so the S
-    //    and P chains of a k-tile do not wait for each other.
+    // 4. k-tile by k-tile: the activation fragments and P for every n-tile.
+    //    With one fold block per k-tile and at most 8 rows (MR), one S MFMA
+    //    serves TPS = 16 / MR k-tiles: operand row r carries real row
+    //    r % MR of k-tile j0 + r / MR, so lane group g (lanes 16g..16g+15,
+    //    result rows 4g..4g+3) holds S of k-tile j0 + 4g / MR. The P operand
+    //    repeats rows 0..MR-1 in every row block, so every lane group holds
+    //    P of its rows for every k-tile, and lane group g folds only the
+    //    k-tiles j0 + 4g / MR; the groups' sums meet at the end. With
+    //    TPS = 1 this is one S per fold block, every lane folding every
+    //    k-tile. Padding rows (r % RG >= M) repeat row M-1. P starts from
+    //    zero, so the S and P chains of a k-tile do not wait for each other.
+    constexpr int TPS = (FW == 4 && MR <= 8) ? (16 / MR < KTW ? 16 / MR : KTW) : 1;  // k-tiles per S MFMA
+    constexpr int RG = 16 / TPS;                              // operand rows per k-tile
+    static_assert(KTW % TPS == 0, "the k-tiles of a wave come in groups of TPS");
+    const int orow = (r % RG) < a.M ? (r % RG) : a.M - 1;
+    const int mytile = (4 * g4) / RG;  // which k-tile of each group this lane group folds
     const u32x4 ones = ones_operand<DT>();
     floatx4 acc[NNM];
 #pragma unroll
     for (int i = 0; i < NNM; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < KTW; ++j) {
-        if (j < kc) {
-            u32x4 af[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) af[s] = *reinterpret_cast<const u32x4*>(As + rr * LD + j * 128 + 32 * s + 8 * g4);
+    for (int j0 = 0; j0 < KTW; j0 += TPS) {
+        if (j0 < kc) {
             floatx4 S[NB];
+            if constexpr (TPS > 1) {
+                // k-tiles past the wave's kc read k-tile kc - 1 (a finite
+                // value that no lane folds).
+                const int js = j0 + r / RG < kc ? j0 + r / RG : kc - 1;
+                S[0] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int f = 0; f < NB; ++f) {
-                S[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ww = 0; ww < FW; ++ww) S[f] = mfma16x16x32<DT>(af[f * FW + ww], ones, S[f]);
+                for (int q = 0; q < 4; ++q)
+                    S[0] = mfma16x16x32<DT>(*reinterpret_cast<const u32x4*>(As + orow * LD + js * 128 + 32 * q + 8 * g4),
+                                            ones, S[0]);
             }
 #pragma unroll
-            for (int i = 0; i < NNM; ++i) {
-                if (i < nn) {
+            for (int t = 0; t < TPS; ++t) {
+                const int j = j0 + t;
+                if (j < kc) {
+                    u32x4 af[4];
 #pragma unroll
-                    for (int f = 0; f < NB; ++f) {
-                        floatx4 P = {0.f, 0.f, 0.f, 0.f};
+                    for (int q = 0; q < 4; ++q)
+                        af[q] = *reinterpret_cast<const u32x4*>(As + orow * LD + j * 128 + 32 * q + 8 * g4);
+                    if constexpr (TPS == 1) {
 #pragma unroll
-                        for (int ww = 0; ww < FW; ++ww) {
-                            const int word = f * FW + ww;
-                            P = mfma16x16x32<DT>(af[word], magic_operand(w[j][i][word], dq_mask, dq_magic), P);
+                        for (int f = 0; f < NB; ++f) {
+                            S[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int ww = 0; ww < FW; ++ww) S[f] = mfma16x16x32<DT>(af[f * FW + ww], ones, S[f]);
                         }
-                        fold<DT, QT>(acc[i], P, S[f], sb[j][i][f], zb[j][i][f]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < NNM; ++i) {
+                        if (i < nn) {
+#pragma unroll
+                            for (int f = 0; f < NB; ++f) {
+                                floatx4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                                for (int ww = 0; ww < FW; ++ww) {
+                                    const int word = f * FW + ww;
+                                    P = mfma16x16x32<DT>(af[word], magic_operand(w[j][i][word], dq_mask, dq_magic), P);
+                                }
+                                if constexpr (TPS == 1) fold<DT, QT>(acc[i], P, S[f], sb[j][i][f], zb[j][i][f]);
+                                else fold_if<DT, QT>(acc[i], P, S[0], sb[j][i][0], zb[j][i][0], mytile == t);
+                            }
+                        }
                     }
                 }
+            }
+        }
+    }
+    if constexpr (TPS > 1) {
+        // Lane groups 16 (TPS = 4) and 32 apart hold the same rows: sum them,
+        // (g0 + g1) + (g2 + g3) in every group alike.
+#pragma unroll
+        for (int i = 0; i < NNM; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                if constexpr (TPS == 4) acc[i][jj] += __shfl_xor(acc[i][jj], 16);
+                acc[i][jj] += __shfl_xor(acc[i][jj], 32);
             }
         }
     }
@@ -692,7 +769,7 @@ __global__ __launch_bounds__(kStreamThreads) void skinny_res_kernel(SkinnyArgs a
     for (int i = 0; i < NNM; ++i)
         if (i < nn) red[(wave * nn + i) * 64 + lane] = acc[i];
     __syncthreads();
-    finish_tiles<DT>(a, red, nn, nwaves, blockIdx.x, gridDim.x);
+    finish_tiles<DT, res_max_waves(KTW, MR)>(a, red, nn, nwaves, blockIdx.x, gridDim.x);
 }
 
 template <int DT, int QT, int FW>
@@ -801,8 +878,11 @@ hipError_t launch_stream_fw(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_
     const size_t lds = (size_t)kStreamWaves * p.nn_max * 64 * sizeof(floatx4);
     if (p.mode == SkinnyPlan::kRegisters) {
         const dim3 rgrid((unsigned)p.ksplit, (unsigned)p.n_groups);
-        const dim3 block((unsigned)(64 * ((p.kc_tiles + kResMaxKt - 1) / kResMaxKt)));
-        const size_t rlds = lds + 16;  // + the last-arrival flag of a split
+        const int64_t nw = (p.kc_tiles + kRegKt - 1) / kRegKt;
+        if (nw > kRegMaxWaves) return hipErrorInvalidValue;
+        const dim3 block((unsigned)(64 * nw));
+        // kRegMaxWaves partial slots per n-tile + the last-arrival flag of a split
+        const size_t rlds = (size_t)kRegMaxWaves * p.nn_max * 64 * sizeof(floatx4) + 16;
         hipError_t e = hipSuccess;
         if (p.nn_max == 1) e = launch_reg<DT, QT, FW, 1>(a, rgrid, block, rlds, stream);
         else if (p.nn_max == 2 || FW == 1) e = launch_reg<DT, QT, FW, 2>(a, rgrid, block, rlds, stream);
@@ -810,13 +890,33 @@ hipError_t launch_stream_fw(const SkinnyArgs& a, const SkinnyPlan& p, hipStream_
         return e;
     }
     if (p.mode == SkinnyPlan::kResident) {
-        const dim3 block((unsigned)(64 * ((a.KTT + p.ktw - 1) / p.ktw)));
-        const size_t lds_a = (size_t)kStreamWaves * a.M * p.ktw * 128 * 2 + (size_t)kStreamWaves * a.M * 16;
-        const size_t lds_r = lds > lds_a ? lds : lds_a;
+        // One wave per ktw k-tiles; each holds its activation rows (M rows of
+        // ktw*128 + 8 halves) in LDS, and the partial sums reuse the area
+        // (res_max_waves slots per n-tile: 8, or 16 for the long-K instance
+        // with 8 k-tiles per wave).
+        const int64_t nw = (a.KTT + p.ktw - 1) / p.ktw;
+        const int64_t maxw = res_max_waves(p.ktw, p.ktw == 8 ? kLongResMaxRows : 16);
+        if (nw > maxw) return hipErrorInvalidValue;
+        const dim3 block((unsigned)(64 * nw));
+        const size_t lds_a = (size_t)(nw > kStreamWaves ? nw : kStreamWaves) * a.M * (p.ktw * 128 + 8) * 2;
+        const size_t lds_w = (size_t)maxw * p.nn_max * 64 * sizeof(floatx4);
+        const size_t lds_r = lds_w > lds_a ? lds_w : lds_a;
         // The planner picks this variant for one n-tile per workgroup only;
-        // up to 8 rows need half the activation registers.
-        return a.M <= 8 ? launch_res<DT, QT, FW, 1, 4, 8>(a, grid, block, lds_r, stream)
-                        : launch_res<DT, QT, FW, 1, 4, 16>(a, grid, block, lds_r, stream);
+        // up to 8 rows need half the activation registers (and with one fold
+        // block per k-tile, up to 4 and 8 rows share S MFMAs over 4 and 2
+        // k-tiles). Long K (8 k-tiles per wave, up to 16 waves, or 16
+        // k-tiles per wave) only with one fold block per k-tile and up to 4
+        // rows.
+        if constexpr (FW == 4) {
+            if (p.ktw > kResMaxKt && a.M > kLongResMaxRows) return hipErrorInvalidValue;
+            if (p.ktw == 8) return launch_res<DT, QT, FW, 1, 8, kLongResMaxRows>(a, grid, block, lds_r, stream);
+            if (p.ktw == 16) return launch_res<DT, QT, FW, 1, 16, kLongResMaxRows>(a, grid, block, lds_r, stream);
+            if (p.ktw == kResShortKt && a.M <= 4)
+                return launch_res<DT, QT, FW, 1, kResShortKt, 4>(a, grid, block, lds_r, stream);
+        }
+        if (p.ktw != kResShortKt) return hipErrorInvalidValue;
+        return a.M <= 8 ? launch_res<DT, QT, FW, 1, kResShortKt, 8>(a, grid, block, lds_r, stream)
+                        : launch_res<DT, QT, FW, 1, kResShortKt, 16>(a, grid, block, lds_r, stream);
     }
     hipError_t e = allow_lds<skinny_str_kernel<DT, QT, FW>>(lds);
     if (e == hipSuccess)
@@ -864,7 +964,9 @@ void launch_skinny_q(const SkinnyArgs& a, const SkinnyPlan& p, int spt, dim3 gri
 }  // namespace
 
 SkinnyPlan plan_skinny(int64_t M, const Geometry& g) {
-    SkinnyPlan p;  // the workspace is sized for 16 rows, so one serves every M <= 16
+    // The plans that split K do not depend on M, so a workspace sized for 16
+    // rows serves every M <= 16; the long-K resident plan (M <= 4) needs none.
+    SkinnyPlan p;
     const int64_t NT = g.Np / 16, KTT = g.Kp / 128;
     // The wide-weight variants address each region of the packed weight with
     // 32-bit offsets below 2^31 (codes N*K/2 bytes, the largest).
@@ -881,22 +983,34 @@ SkinnyPlan plan_skinny(int64_t M, const Geometry& g) {
         p.nn_max = (int)(per < kMaxTilesPerWG ? per : kMaxTilesPerWG);
         p.n_groups = (NT + p.nn_max - 1) / p.nn_max;
         p.kc_tiles = (int)KTT;
-        // Every weight tile of a wave in registers (at most 16): 4 k-tiles
-        // per wave and up to 4 n-tiles per workgroup (2 with a scale per
+        // Every weight tile of a wave in registers: 2 k-tiles per wave (up
+        // to 16 waves) and up to 4 n-tiles per workgroup (2 with a scale per
         // word). The activation fragments either stay in registers for all
         // of the wave's n-tiles (kRegisters: several n-tiles share them), or
         // the M real rows are loaded compactly and staged per wave in LDS
-        // (kResident: one n-tile per workgroup, where 16 fragment loads per
-        // wave would cost more texture-unit time than the weights). With
-        // K > 4096, K is split into chunks of at most 32 k-tiles (8 waves)
-        // and the n-groups shrink so that the chunks of all n-groups still
-        // make about one workgroup per CU; the chunk partials meet in the
-        // workspace. Otherwise the streamed variant.
+        // (kResident: one n-tile per workgroup, where the fragment loads of
+        // 16 rows would cost more texture-unit time than the weights). With
+        // K > 4096, K is split into chunks of at most 32 k-tiles and the
+        // n-groups shrink so that the chunks of all n-groups still make
+        // about one workgroup per CU; the chunk partials meet in the
+        // workspace (or, for one n-tile per workgroup and up to 4 rows, all
+        // of K stays in one workgroup, below). Otherwise the streamed
+        // variant.
         const int nb = g.Kg == 1 || g.Ge >= 128 ? 1 : (int)(128 / g.Ge);  // fold blocks per k-tile
         const int nn_cap = nb < 4 ? 4 : 2;
         if (KTT <= 32 && p.nn_max <= nn_cap) {
             p.mode = p.nn_max >= 2 ? SkinnyPlan::kRegisters : SkinnyPlan::kResident;
-            p.ktw = kResMaxKt;
+            p.ktw = p.nn_max >= 2 ? kResMaxKt : kResShortKt;
+            return p;
+        }
+        // One n-tile per workgroup, at most 4 rows and one fold block per
+        // k-tile: all of K in one workgroup (8 k-tiles per wave, up to 16
+        // waves), its activation rows staged in LDS (4 rows x 8 k-tiles x
+        // 16 waves: 132 KB). No K chunks, so no exchange through the
+        // workspace.
+        if (p.nn_max == 1 && M <= kLongResMaxRows && nb == 1 && KTT <= 8 * 16) {
+            p.mode = SkinnyPlan::kResident;
+            p.ktw = 8;
             return p;
         }
         int64_t ks = (KTT + 31) / 32;

@@ -228,6 +228,12 @@ def test_workspace_size(lib):
     assert w4.workspace_size(17, 4096, 4096, 128) > 0  # the first M past the skinny path splits K too
     assert w4.workspace_size(96, 512, 1024, 128) == 0  # too few tiles to fill half the CUs: unsplit
     assert w4.workspace_size(16, 4096, 4096, 128) == 0  # wide weights: K is not split
+    # long K, one n-tile per workgroup: all of K in one workgroup up to 4 rows
+    assert w4.workspace_size(4, 4096, 14336, 128) == 0
+    assert w4.workspace_size(1, 4096, 16384, -1) == 0
+    assert w4.workspace_size(5, 4096, 14336, 128) > w4.workspace_counter_bytes()  # 5 rows: K chunks
+    assert w4.workspace_size(1, 4096, 14336, 64) > w4.workspace_counter_bytes()  # 2 fold blocks per 128 k
+    assert w4.workspace_size(16, 4096, 14336, 128) >= w4.workspace_size(1, 4096, 14336, 64)
     ws = w4.workspace_size(16, 1024, 4096, 128)  # narrow weights split K
     assert ws > w4.workspace_counter_bytes()
     # sized for 16 rows, so every M <= 16 fits the same workspace

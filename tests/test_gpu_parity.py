@@ -805,6 +805,9 @@ SHIFTED = [
     (16, 4096, 14336, -1, UINT4B8, "f16", 3.0, "centred", SKINNY),   # skinny fold blocks, K split in chunks
     (16, 14336, 4096, 128, UINT4, "f16", 3.0, "centred", SKINNY),
     (8, 1024, 14336, 256, UINT4B8, "f16", 3.0, "centred", SKINNY),   # split-K kernel
+    (4, 4096, 14336, 128, UINT4B8, "f16", 3.0, "centred", SKINNY),   # long K in one workgroup, S over 4 k-tiles
+    (1, 4096, 16384, -1, UINT4, "f16", 3.0, "centred", SKINNY),
+    (8, 4096, 4096, 128, UINT4B8, "f16", 3.0, "centred", SKINNY),    # S over 2 k-tiles
 ]
 
 
@@ -845,8 +848,8 @@ def test_shifted_activations_long_k(M, N, K, G, qtype, dtype, mean, codes, path)
 FULL_K = [
     # (N, K, M, G, qtype, dtype, bias)
     (4096, 128, 16, 128, UINT4B8, "f16", True),   # one k-tile, one wave, LDS activations
-    (4096, 384, 3, 64, UINT4, "bf16", False),     # one wave with 3 k-tiles, LDS activations (up to 8 rows)
-    (4096, 640, 9, 32, UINT4, "f16", True),       # two waves (4 and 1 k-tiles), a scale per word
+    (4096, 384, 3, 64, UINT4, "bf16", False),     # two waves (2 and 1 k-tiles), LDS activations (up to 8 rows)
+    (4096, 640, 9, 32, UINT4, "f16", True),       # three waves (2, 2 and 1 k-tiles), a scale per word
     (4112, 1024, 5, 128, UINT4B8, "bf16", False), # 257 n-tiles: 2 per workgroup, the last has 1
     (14416, 512, 2, 64, UINT4, "f16", True),      # 901 n-tiles: 4 per workgroup, ragged last ones
     (14336, 4096, 2, 64, UINT4, "f16", False),    # 4 n-tiles per workgroup with zeros, 2 fold blocks
@@ -855,11 +858,28 @@ FULL_K = [
     (4096, 16384, 12, -1, UINT4B8, "f16", False), # K split in 4 chunks, one group per row
     (14336, 4096, 7, 32, UINT4, "bf16", True),    # streamed: 4 n-tiles per workgroup, a scale per word
     (6144, 4096, 16, 32, UINT4, "bf16", True),    # 2 n-tiles per workgroup, a scale per word
-    # Long K with K split over workgroups (partials through the workspace).
+    # One n-tile per workgroup, one fold block per k-tile: up to 8 rows share
+    # each S MFMA over a wave's 2 k-tiles; waves take every nwaves-th k-tile.
+    (4096, 640, 3, 128, UINT4, "f16", True),      # 5 k-tiles over 3 waves (2, 2 and 1): a partial pair
+    (4096, 128, 2, -1, UINT4B8, "bf16", False),   # one k-tile: the S operand repeats it for the pair
+    (4096, 1280, 7, 256, UINT4, "bf16", True),    # 10 k-tiles over 5 waves, up to 8 rows
+    (4096, 4096, 6, 128, UINT4B8, "f16", False),
+    (4096, 4096, 1, 128, UINT4, "bf16", True),
+    (4096, 4096, 4, -1, UINT4, "f16", False),
+    # Long K, one n-tile per workgroup, up to 4 rows: all of K in one
+    # workgroup, 8 k-tiles per wave (up to 16 waves), S over 4 k-tiles,
+    # activation rows in LDS.
     (4096, 14336, 1, 128, UINT4B8, "f16", False),
     (4096, 14336, 4, 128, UINT4, "bf16", True),
-    (3072, 13952, 3, 128, UINT4B8, "f16", True),  # 109 k-tiles
-    (4096, 16384, 2, -1, UINT4, "f16", False),    # one group per row
+    (3072, 13952, 3, 128, UINT4B8, "f16", True),  # 109 k-tiles: 14 waves of 8 or 7
+    (4096, 16384, 2, -1, UINT4, "f16", False),    # one group per row, 16 waves of 8
+    (4096, 4224, 4, 128, UINT4, "f16", True),     # 33 k-tiles: 5 waves of 7 or 6
+    (3200, 8192, 1, -1, UINT4B8, "bf16", True),   # 64 k-tiles: 8 waves of 8
+    (4096, 8320, 3, 128, UINT4, "bf16", False),   # 65 k-tiles: 9 waves of 8 or 7
+    # Long K with K split over workgroups (partials through the workspace).
+    (4096, 14336, 2, 64, UINT4, "f16", True),     # two fold blocks per 128 k
+    (4096, 14336, 5, 128, UINT4B8, "bf16", False),  # 5 rows
+    (4096, 16512, 1, 128, UINT4B8, "f16", False),  # 129 k-tiles: the streamed variant
 ]
 
 
@@ -886,6 +906,24 @@ def test_identity_through_full_k(N, dtype, qtype, G):
     packed = repack(case)
     A = torch.eye(K, dtype=case.torch_dtype, device=DEV)
     C = w4.gemm(A, packed, N, K, G, qtype, path=SKINNY)
+    W = oracle.dequant(case.weight_packed, case.weight_scale, case.weight_zero_point, qtype, G)
+    expect = torch.from_numpy(W.T.copy()).to(case.torch_dtype)
+    bad = (C.cpu().view(torch.int16) != expect.view(torch.int16)).sum().item()
+    assert bad == 0, f"{bad} of {C.numel()} values differ from RN((q - z) * s)"
+
+
+@pytest.mark.parametrize("rows,dtype,qtype,G", [(4, "f16", UINT4B8, 128), (1, "bf16", UINT4, -1),
+                                                 (8, "bf16", UINT4B8, 256), (3, "f16", UINT4, 128)])
+def test_identity_small_m_slices(rows, dtype, qtype, G):
+    # A = I_512 in slices of `rows` rows through the one-n-tile skinny kernel,
+    # where up to 4 (8) rows share each S MFMA over 4 (2) k-tiles and lane
+    # groups fold different k-tiles: still bit-exact RN_act((q - z) * s).
+    N, K = 4096, 512
+    print(f"[case] identity small-M slices rows={rows} {dtype} qtype={qtype} G={G}", flush=True)
+    case = _case(26, 1, N, K, G, qtype, dtype)
+    packed = repack(case)
+    eye = torch.eye(K, dtype=case.torch_dtype, device=DEV)
+    C = torch.cat([w4.gemm(eye[i:i + rows], packed, N, K, G, qtype, path=SKINNY) for i in range(0, K, rows)])
     W = oracle.dequant(case.weight_packed, case.weight_scale, case.weight_zero_point, qtype, G)
     expect = torch.from_numpy(W.T.copy()).to(case.torch_dtype)
     bad = (C.cpu().view(torch.int16) != expect.view(torch.int16)).sum().item()
