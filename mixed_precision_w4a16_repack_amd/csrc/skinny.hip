@@ -282,6 +282,7 @@ constexpr int kResMaxKt = 4;    // K chunks of the split skinny_reg_kernel are m
 constexpr int kRegKt = 2;       // k-tiles per wave in skinny_reg_kernel (up to 16 waves)
 constexpr int kResShortKt = 2;  // k-tiles per wave in skinny_res_kernel for K <= 4096 (up to 16 waves)
 constexpr int kLongResMaxRows = 4;  // rows of the long-K skinny_res_kernel instances
+constexpr int kResAhead = 3;        // k-tiles a wave of skinny_res_kernel requests ahead of the one consumed
 constexpr int kStrDepth = 8;  // units in flight per wave in skinny_str_kernel
 
 template <int DT>
@@ -653,12 +654,18 @@ __global__ __launch_bounds__(64 * res_max_waves(KTW, MR)) void skinny_res_kernel
     const WeightBufs wb(a);
     // 2. Every weight tile, scale and zero of the wave, in consumption order
     //    (k-tile outer, n-tile inner). Units past the workgroup's n-tiles or
-    //    the wave's k-tiles use zero-size descriptors (see make_rsrc).
+    //    the wave's k-tiles use zero-size descriptors (see make_rsrc). The
+    //    first AHEAD k-tiles are requested here, each later one right after
+    //    the k-tile AHEAD before it is consumed. (A wave whose request waits
+    //    for room in the CU's full memory queue computes nothing meanwhile;
+    //    requesting all 8 k-tiles of a long-K wave first left all of its
+    //    MFMAs until after its last request. 3 ahead measured fastest with
+    //    16 waves.)
+    constexpr int AHEAD = KTW < kResAhead ? KTW : kResAhead;
     u32x4 w[KTW][NNM];
     uint16_t sb[KTW][NNM][NB];
     uint8_t zb[KTW][NNM][NB];
-#pragma unroll
-    for (int j = 0; j < KTW; ++j) {
+    auto issue = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NNM; ++i) {
             const int64_t nt = blockIdx.x + (int64_t)i * gridDim.x;
@@ -668,7 +675,9 @@ __global__ __launch_bounds__(64 * res_max_waves(KTW, MR)) void skinny_res_kernel
             for (int f = 0; f < NB; ++f)
                 load_scale_zero<QT, FW>(wb, a, nt, kt0 + j * nwaves, f, r, valid, sb[j][i][f], zb[j][i][f]);
         }
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j) issue(j);
     __builtin_amdgcn_sched_barrier(0);
     // 3. Activation slice into this wave's LDS region (no other wave reads
     //    it, and a wave's LDS accesses complete in order: no barrier).
@@ -745,6 +754,10 @@ __global__ __launch_bounds__(64 * res_max_waves(KTW, MR)) void skinny_res_kernel
                             }
                         }
                     }
+                }
+                if (j + AHEAD < KTW) {
+                    issue(j + AHEAD);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
