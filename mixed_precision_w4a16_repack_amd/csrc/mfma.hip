@@ -1464,14 +1464,25 @@ hipError_t launch_ring_ocm(MfmaArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Whether `wide` 128 x 512 tiles beat the 128 x 256 ring tiles: when they
+// fill whole rounds of the CUs, or the last, partial round is at most a fifth
+// of the work, or (`late_round`) it is at least three quarters full. Measured
+// on 2048 x 14336 x 4096 (448 wide tiles, 1.75 rounds, against 3.5 rounds of
+// ring tiles): one group per row 170 us wide against 183 us ring; groups of
+// 256 with zero points 242 against 259 us; without zero points 236 against
+// 227 us, so that mode does not take the late round.
+inline bool wide_tiles_fit(int64_t wide, bool late_round) {
+    if (wide < kCUs) return false;
+    if (wide % kCUs == 0 || wide >= 4 * kCUs) return true;
+    return late_round && 4 * (wide % kCUs) >= 3 * kCUs;
+}
+
 template <int DT, int QT>
 hipError_t launch_ring_t(MfmaArgs a, hipStream_t stream) {
     a.m_tiles = (a.M + 127) / 128;
     if (a.one_group) {
-        // 128 x 512 tiles when they fill whole rounds of the CUs (or the
-        // last, partial round is at most a fifth of the work).
         const int64_t wide = a.m_tiles * ((a.N + 511) / 512);
-        if (wide >= kCUs && (wide % kCUs == 0 || wide >= 4 * kCUs)) {
+        if (wide_tiles_fit(wide, true)) {
             a.n_blocks = (a.N + 511) / 512;
             a.tile0 = 0;
             if (a.K % 128) hipLaunchKernelGGL((mfma_wide_kernel<DT, QT, 1>), dim3((unsigned)wide), dim3(512), 0, stream, a);
@@ -1481,7 +1492,7 @@ hipError_t launch_ring_t(MfmaArgs a, hipStream_t stream) {
     }
     if (!a.one_group) {
         const int64_t wide = a.m_tiles * ((a.N + 511) / 512);
-        if (wide >= kCUs && (wide % kCUs == 0 || wide >= 4 * kCUs)) {
+        if (wide_tiles_fit(wide, QT == 1)) {
             a.n_blocks = (a.N + 511) / 512;
             a.tile0 = 0;
             hipLaunchKernelGGL((mfma_wide_grouped_kernel<DT, QT>), dim3((unsigned)wide), dim3(512), 0, stream, a);

@@ -621,9 +621,9 @@ RING = [
     (4096, 4096, 512, 128, UINT4B8, "f16", False),  # a group per step, tail of 1
     (2048, 8192, 1536, 256, UINT4, "bf16", True),   # 2 steps per group, 12 steps: no tail
     (1930, 8192, 896, -1, UINT4, "f16", False),     # 7 steps: tail of 1, ragged M
-    (2048, 14336, 512, 256, UINT4, "bf16", True),   # 896 tiles: the last 128 as 64-row halves
-    (1990, 14336, 256, -1, UINT4B8, "f16", False),  # halves over m-tiles 13-15, ragged M
-    (1930, 14336, 256, 128, UINT4, "f16", True),    # a half tile lies wholly past M
+    (2048, 14336, 512, 256, UINT4B8, "bf16", True), # 896 tiles: the last 128 as 64-row halves
+    (1390, 14336, 256, -1, UINT4B8, "f16", False),  # halves over m-tiles 9-10, ragged M
+    (1930, 14336, 256, 128, UINT4B8, "f16", True),  # a half tile lies wholly past M
     (2048, 4096, 1024, 64, UINT4, "bf16", True),    # G = 64: staged tiles, scale first
     (1000, 8192, 512, 32, UINT4B8, "f16", False),   # G = 32: staged tiles, scale first, ragged M
     # Two tail steps after the loop (steps % 3 == 2) in the grouped mode:
@@ -632,20 +632,25 @@ RING = [
     (2048, 4096, 640, 128, UINT4, "f16", True),     # 5 steps, a group per step, zero points
     (2048, 4096, 1024, 256, UINT4B8, "bf16", False),# 8 steps, two steps per group
     (2048, 4096, 4096, 256, UINT4, "f16", True),    # 32 steps, the K of the 14336 x 4096 prefill weight
-    # 128 x 512 tiles (one group per row, whole rounds of 256 tiles or at
-    # least 1024 tiles): two LDS stages, tiles ordered per XCD.
+    # 128 x 512 tiles (one group per row, whole rounds of 256 tiles, at
+    # least 1024 tiles, or a last round at least three quarters full): two
+    # LDS stages, tiles ordered per XCD.
     (4096, 4096, 1024, -1, UINT4B8, "bf16", False), # 256 tiles, 8 steps
     (4096, 4000, 896, -1, UINT4, "f16", True),      # ragged N (250 n-tiles), 7 steps: odd tail step
     (4000, 4096, 1000, -1, UINT4B8, "f16", False),  # ragged M, K tail
     (8192, 4096, 256, -1, UINT4, "bf16", True),     # 512 tiles: two rounds
     (8192, 14336, 128, -1, UINT4B8, "bf16", False), # 1792 tiles, a single K step
     (4470, 15872, 128, -1, UINT4B8, "f16", True),   # 1085 tiles: not a multiple of 8 (no XCD grouping)
+    (1990, 14336, 256, -1, UINT4B8, "f16", False),  # 448 tiles: a last round three quarters full, ragged M
     # 128 x 512 tiles with groups of 128 k or more (accumulators rescaled at
-    # each group end).
+    # each group end); with zero points also for a last round at least three
+    # quarters full.
     (4096, 4096, 1024, 256, UINT4, "bf16", True),   # 4 groups of 2 steps, zero points
     (8192, 14336, 512, 128, UINT4, "f16", False),   # 1792 tiles, a group per step
     (4000, 4008, 768, 256, UINT4B8, "bf16", True),  # ragged M and N, 3 groups
     (4096, 4096, 384, 128, UINT4B8, "f16", False),  # 3 steps: odd tail step ends the last group
+    (2048, 14336, 512, 256, UINT4, "bf16", True),   # zero points: 448 tiles, a last round three quarters full
+    (1930, 14336, 256, 128, UINT4, "f16", True),    # the same with ragged M
 ]
 
 
