@@ -8,18 +8,24 @@
 // zero, scale, and accumulate a dot product in fp32. Three kernels keep that
 // arithmetic and lay the work out for CDNA4:
 //
+//  * mfma_wide_kernel / mfma_wide_grouped_kernel: 128 x 512 tiles for large
+//    M and N (one group per row; groups of 128 k or more), double-buffered
+//    in LDS, the group scales of the grouped one applied by rescaling one
+//    set of accumulators.
 //  * mfma_ring_kernel: 128 x 256 tiles when they give at least one
 //    workgroup per CU, for one group per row or groups of 128 k or more.
 //    Activation and weight tiles go from HBM/L2 straight into a three-stage
-//    LDS ring (direct 16-byte buffer loads), and the weights are
-//    dequantised offset-corrected: exact values 1 + q/16 into the MFMA
-//    (TopNibble), the offset removed with row sums and the scale applied
-//    once per group.
-//  * mfma_lds_kernel: the other tile shapes (64-column tiles at small and
-//    medium M) and groups of 32 or 64 k (scale first, per weight, as the
-//    pages do); activation tiles go straight into two LDS buffers, the
+//    LDS ring (direct 16-byte buffer loads).
+//    These three dequantise offset-corrected: exact values 1 + q/16 into
+//    the MFMA (TopNibble), the offset removed with row sums and the scale
+//    applied once per row or group.
+//  * mfma_splitk_kernel + splitk_reduce_kernel: medium M (tens to a few
+//    hundred rows), any group size, K split over workgroups so that the
+//    tiles fill the CUs; scale first, per weight, as the pages do.
+//  * mfma_lds_kernel: 64-column tiles (a K tail, or a workspace too small
+//    for split-K); activation tiles go straight into two LDS buffers, the
 //    weights into registers.
-// Both address a workgroup's operands through buffer descriptors based at
+// All address a workgroup's operands through buffer descriptors based at
 // its own tile, so A and the packed weight may be of any size.
 // Every kernel stages activations in LDS in "fragment order" (1 KB per
 // 16 rows x 32 k, lane l's 16 bytes at 16*l) so that each A-operand read is
