@@ -28,6 +28,20 @@
 //    workgroups travels with the sc1 policy, which is how the compiler
 //    implements agent-scope atomic stores and loads (a release fence would
 //    write back the XCD's whole L2).
+//
+// That kernel serves narrow weights (fewer than 192 n-tiles) and N or K
+// tails. Wide weights (the decode layers) use three variants that keep K
+// whole in a workgroup where they can and give each CU up to 16 waves:
+//  * skinny_reg_kernel: 2-4 n-tiles per workgroup sharing the activation
+//    fragments, 2 k-tiles per wave; K over 4096 split in chunks whose
+//    partials meet as above.
+//  * skinny_res_kernel: one n-tile per workgroup, the M real activation rows
+//    staged in LDS; 2 k-tiles per wave, or 8 for K up to 16384 at up to 4
+//    rows; at up to 8 rows one row-sum MFMA serves several k-tiles.
+//  * skinny_str_kernel: a ring of weight units in flight per wave.
+// A wave computes only after its loads are issued, and issuing waits for
+// room in the CU's memory queue, so more waves per CU (and, for the long-K
+// waves, requesting a few k-tiles ahead) let MFMAs overlap loads.
 #include "device_common.h"
 #include "exchange.h"
 #include "internal.h"
