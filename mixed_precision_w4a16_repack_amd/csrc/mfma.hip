@@ -1350,26 +1350,39 @@ __global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
         const unsigned char* abase = abuf(I) + lane16;
         const unsigned char* bb = bbuf(I);
         typename Dequant<DT>::Params prm[NJ];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            __builtin_amdgcn_sched_barrier(0);
+        // The dequantised words of slice s (bq) are ready before its MFMAs;
+        // the words of slice s + 1 are dequantised in slice s's scheduling
+        // region, so that their VALU work interleaves with slice s's MFMAs.
+        u32x4 bq[NJ];
+        auto dequant_slice = [&](int s, u32x4 (&out)[NJ]) __attribute__((always_inline)) {
             if (s % (4 / SPT) == 0) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
                     prm[j] = Dequant<DT>::make((uint16_t)sraw[i][s / (4 / SPT)][j],
                                                QT ? (int)zraw[i][s / (4 / SPT)][j] : 8);
             }
-            u32x4 bq[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const uint32_t w = *reinterpret_cast<const uint32_t*>(bb + (wave * NJ + j) * 1024 + lane16 + 4 * s);
-                bq[j] = Dequant<DT>::apply(w, prm[j], dq_mask, dq_magic);
+                out[j] = Dequant<DT>::apply(w, prm[j], dq_mask, dq_magic);
             }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        dequant_slice(0, bq);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4 bqn[NJ];
+            if (s < 3) dequant_slice(s + 1, bqn);
 #pragma unroll
             for (int ii = 0; ii < MI; ++ii) {
                 const u32x4 av = *reinterpret_cast<const u32x4*>(abase + (ii * 4 + s) * 1024);
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) acc[ii][j] = mfma16x16x32<DT>(av, bq[j], acc[ii][j]);
+            }
+            if (s < 3) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) bq[j] = bqn[j];
             }
         }
         if (more) wait_vmcnt<(NS - 2) * STEP_LOADS>();
