@@ -1350,9 +1350,10 @@ __global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
         const unsigned char* abase = abuf(I) + lane16;
         const unsigned char* bb = bbuf(I);
         typename Dequant<DT>::Params prm[NJ];
-        // The dequantised words of slice s (bq) are ready before its MFMAs;
-        // the words of slice s + 1 are dequantised in slice s's scheduling
-        // region, so that their VALU work interleaves with slice s's MFMAs.
+        // The dequantised words (bq) and activation fragments (av) of slice s
+        // are ready before its MFMAs; those of slice s + 1 are read and
+        // dequantised in slice s's scheduling region, so that their LDS and
+        // VALU work interleaves with slice s's MFMAs.
         u32x4 bq[NJ];
         auto dequant_slice = [&](int s, u32x4 (&out)[NJ]) __attribute__((always_inline)) {
             if (s % (4 / SPT) == 0) {
@@ -1367,22 +1368,31 @@ __global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
                 out[j] = Dequant<DT>::apply(w, prm[j], dq_mask, dq_magic);
             }
         };
+        u32x4 av[MI];
+        auto read_a = [&](int s, u32x4 (&out)[MI]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ii = 0; ii < MI; ++ii) out[ii] = *reinterpret_cast<const u32x4*>(abase + (ii * 4 + s) * 1024);
+        };
         __builtin_amdgcn_sched_barrier(0);
+        read_a(0, av);
         dequant_slice(0, bq);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             __builtin_amdgcn_sched_barrier(0);
-            u32x4 bqn[NJ];
-            if (s < 3) dequant_slice(s + 1, bqn);
-#pragma unroll
-            for (int ii = 0; ii < MI; ++ii) {
-                const u32x4 av = *reinterpret_cast<const u32x4*>(abase + (ii * 4 + s) * 1024);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) acc[ii][j] = mfma16x16x32<DT>(av, bq[j], acc[ii][j]);
+            u32x4 bqn[NJ], avn[MI];
+            if (s < 3) {
+                read_a(s + 1, avn);
+                dequant_slice(s + 1, bqn);
             }
+#pragma unroll
+            for (int ii = 0; ii < MI; ++ii)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[ii][j] = mfma16x16x32<DT>(av[ii], bq[j], acc[ii][j]);
             if (s < 3) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) bq[j] = bqn[j];
+#pragma unroll
+                for (int ii = 0; ii < MI; ++ii) av[ii] = avn[ii];
             }
         }
         if (more) wait_vmcnt<(NS - 2) * STEP_LOADS>();
