@@ -1200,6 +1200,11 @@ __global__ __launch_bounds__(512) void mfma_wide_grouped_kernel(MfmaArgs a) {
     if (vec16) stage_flush<128>(stage, lane, a.C, a.ldc, a.M, a.Nst, m0, nt_of(0) * 16);
 }
 
+// Waves of the split-K tiled kernel; each owns kSplitkNJ of the tile's 16
+// n-tiles and all of its rows.
+constexpr int kSplitkWaves = 8;
+constexpr int kSplitkNJ = 16 / kSplitkWaves;
+
 // Medium M (up to a few hundred rows), any group size, K a multiple of 128:
 // tiles of BM (32, 64 or 128) rows x 256 columns, K split over `ksplit`
 // workgroups so that the tiles of a narrow M still occupy every CU.
@@ -1223,13 +1228,15 @@ __global__ __launch_bounds__(512) void mfma_wide_grouped_kernel(MfmaArgs a) {
 //    bias and writes C, and clears the counter. The same thread reads the
 //    partials of the accumulators it holds, so no other exchange is needed.
 template <int DT, int QT, int BM, int SPT, int NS>
-__global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(64 * kSplitkWaves) void mfma_splitk_kernel(MfmaArgs a) {
     static_assert(BM == 32 || BM == 64 || BM == 128, "32, 64 or 128 rows");
     static_assert(SPT == 1 || SPT == 2 || SPT == 4, "groups per K step");
     static_assert(NS >= 3 && NS <= 6, "three to six stages");
-    constexpr int MI = BM / 16, NJ = 2;
+    constexpr int NW = kSplitkWaves;
+    constexpr int MI = BM / 16, NJ = kSplitkNJ;
     constexpr int ABLK = BM / 16 * 4, BBLK = 16;
-    constexpr int APW = ABLK / 8, BPW = BBLK / 8;  // 1 KB blocks per wave and step
+    constexpr int APW = ABLK / NW, BPW = BBLK / NW;  // 1 KB blocks per wave and step
+    static_assert(ABLK % NW == 0, "whole activation blocks per wave");
     constexpr int ASZ = ABLK * 1024, BSZ = BBLK * 1024;
     // Loads per wave and step: activation and weight blocks, then one scale
     // (and zero point) per group of the step and n-tile of the wave.
@@ -1451,7 +1458,7 @@ __global__ __launch_bounds__(512) void mfma_splitk_kernel(MfmaArgs a) {
 // the loads of a wave are 1 KB contiguous per split.
 template <int DT, int BM>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(MfmaArgs a) {
-    constexpr int MI = BM / 16, NJ = 2;
+    constexpr int MI = BM / 16, NJ = kSplitkNJ;
     constexpr int UNITS = BM * 256 / 4;  // floatx4 units per partial tile
     const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t tile = u / UNITS;
@@ -1583,7 +1590,7 @@ hipError_t launch_lds_ktail(const MfmaArgs& a, int spt, hipStream_t stream) {
 // vmcnt counter (at most 63 outstanding) can count for the steps in flight.
 constexpr int splitk_stages(int BM, int SPT, int QT) {
     const int by_lds = BM == 128 ? 3 : (BM == 64 ? 4 : 6);
-    const int step_loads = BM / 32 + 2 + SPT * 2 * (1 + QT);
+    const int step_loads = BM / (4 * kSplitkWaves) + 16 / kSplitkWaves + SPT * kSplitkNJ * (1 + QT);
     const int by_count = 2 + 63 / step_loads;
     return by_lds < by_count ? by_lds : by_count;
 }
@@ -1595,15 +1602,15 @@ hipError_t launch_splitk_t(const MfmaArgs& a, const MfmaPlan& p, hipStream_t str
     const int spt = a.one_group || a.gshift >= 7 ? 1 : 1 << (7 - a.gshift);
     switch (spt) {
         case 4:
-            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 4, splitk_stages(BM, 4, QT)>), grid, dim3(512), 0,
+            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 4, splitk_stages(BM, 4, QT)>), grid, dim3(64 * kSplitkWaves), 0,
                                stream, a);
             break;
         case 2:
-            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 2, splitk_stages(BM, 2, QT)>), grid, dim3(512), 0,
+            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 2, splitk_stages(BM, 2, QT)>), grid, dim3(64 * kSplitkWaves), 0,
                                stream, a);
             break;
         default:
-            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 1, splitk_stages(BM, 1, QT)>), grid, dim3(512), 0,
+            hipLaunchKernelGGL((mfma_splitk_kernel<DT, QT, BM, 1, splitk_stages(BM, 1, QT)>), grid, dim3(64 * kSplitkWaves), 0,
                                stream, a);
             break;
     }
