@@ -76,10 +76,10 @@ struct MfmaArgs {
     int64_t tile0;  // mfma_ring_kernel: first 128 x 256 tile (row-major over m-tiles x n-blocks)
     int64_t Nst;    // columns of C (N above is rounded up to 16); stores and bias stop at Nst
     // mfma_splitk_kernel: K steps split over ksplit workgroups of spk steps;
-    // partial tiles and arrival counters in the workspace.
+    // partial tiles in the workspace, after its counter region (which the
+    // tiled kernels leave untouched).
     int64_t ksplit, spk;
     float* partials;
-    uint32_t* counters;
 };
 
 // One workgroup's operands as buffer bases and byte extents: rows
@@ -1221,12 +1221,12 @@ constexpr int kSplitkNJ = 16 / kSplitkWaves;
 //  * Scale first, as the pages do: each word becomes RN((q - z) * s) in the
 //    act dtype (Dequant), so the MFMA sums are the result; no row sums and no
 //    offset correction, which suits groups of 32 or 64 k.
-//  * With ksplit > 1 each workgroup writes its fp32 partial tile through to
-//    the agent-wide coherence point and bumps the tile's arrival counter; the
-//    last to arrive reads all partials back and adds them in split order (a
-//    fixed order: the result does not depend on which arrives last), adds the
-//    bias and writes C, and clears the counter. The same thread reads the
-//    partials of the accumulators it holds, so no other exchange is needed.
+//  * With ksplit > 1 each workgroup writes its fp32 partial tile to the
+//    workspace with ordinary stores, and splitk_reduce_kernel, the next
+//    launch on the stream, adds the partials in split order (a fixed order),
+//    adds the bias and writes C. The kernel boundary makes the partials
+//    visible, which costs less than write-through stores and coherent
+//    reads by the last workgroup of a tile to arrive.
 template <int DT, int QT, int BM, int SPT, int NS>
 __global__ __launch_bounds__(64 * kSplitkWaves) void mfma_splitk_kernel(MfmaArgs a) {
     static_assert(BM == 32 || BM == 64 || BM == 128, "32, 64 or 128 rows");
@@ -1310,7 +1310,7 @@ __global__ __launch_bounds__(64 * kSplitkWaves) void mfma_splitk_kernel(MfmaArgs
     // Requests every load of step st into stage I (past the split's last
     // step the descriptors have size 0: no memory access, zeros written, and
     // the same number of loads, which the hand-counted waits rely on).
-    auto issue = [&](int64_t st, auto I) {
+    auto issue = [&](int64_t st, auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         const bool live = st < st1;
 #pragma unroll
@@ -1350,7 +1350,7 @@ __global__ __launch_bounds__(64 * kSplitkWaves) void mfma_splitk_kernel(MfmaArgs
     // into the stage the previous step freed, and ends waiting for step
     // st + 1 only; the last NS - 1 steps of the split request nothing and
     // wait for every load.
-    auto step = [&](int64_t st, auto I, bool more) {
+    auto step = [&](int64_t st, auto I, bool more) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value;
         constexpr int inext = (i + NS - 1) % NS;
         if (more) issue(st + NS - 1, std::integral_constant<int, inext>{});
@@ -1667,7 +1667,6 @@ MfmaPlan plan_mfma(int64_t M, const Geometry& g, size_t workspace_cap) {
         const int64_t tiles = ((M + bm - 1) / bm) * ((g.Np + 255) / 256);
         int64_t ks = kCUs / tiles;
         if (ks > KTT / 4) ks = KTT / 4;
-        if (tiles * (int64_t)sizeof(uint32_t) > (int64_t)kCounterRegionBytes) ks = 1;
         for (; ks > 1; --ks) {
             const size_t need = kCounterRegionBytes + (size_t)tiles * ks * bm * 256 * sizeof(float);
             if (need <= workspace_cap) break;
@@ -1719,7 +1718,6 @@ hipError_t launch_mfma(const void* A, int64_t M, int64_t lda, const void* packed
     a.tile0 = 0;
     a.ksplit = p.ksplit;
     a.spk = p.splitk ? p.spk : a.KTT;
-    a.counters = static_cast<uint32_t*>(workspace);
     a.partials = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kCounterRegionBytes) : nullptr;
     const int spt = g.Kg == 1 ? 1 : (g.Ge >= 128 ? 1 : 128 / g.Ge);
     if (dtype == 0) return g.qtype ? launch_mfma_q<0, 1>(a, p, spt, stream) : launch_mfma_q<0, 0>(a, p, spt, stream);
