@@ -4,9 +4,10 @@
 
 Each source compiles to an object under ``_build/`` (in parallel), then one
 shared library is linked next to this file, where the binding loads it.
-The sources with staged GEMM kernels are also compiled to gfx950 assembly,
-and ``wait_check`` verifies their hand-counted memory waits against it; a
-mismatch fails the build.
+The sources with MFMA kernels are also compiled to gfx950 assembly:
+``wait_check`` verifies the hand-counted memory waits of the staged kernels
+against it, and that no MFMA reads an inline-asm VALU result without the
+wait states the hardware needs; either problem fails the build.
 """
 
 from __future__ import annotations
@@ -27,6 +28,7 @@ CEILING_SRC = "ceiling.hip"
 CEILING_LIB = os.path.join(PKG, "libw4a16_ceiling.so")
 SOURCES = ["w4a16_api.cpp", "repack.hip", "skinny.hip", "mfma.hip", "dense.hip", "w4a8.hip", "scratch.hip"]
 STAGED = ["mfma.hip", "w4a8.hip"]  # kernels with hand-counted waits (wait_check)
+ASSEMBLED = STAGED + ["skinny.hip"]  # every source with MFMA kernels (operand hazard check)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -84,6 +86,19 @@ def check_waits(asm_paths) -> None:
         raise RuntimeError("wait check failed:\n" + "\n".join(problems))
 
 
+def check_mfma_operands(asm_paths) -> None:
+    """Fails when an MFMA reads an inline-asm VALU result too soon (see
+    wait_check.mfma_operand_hazards)."""
+    from . import wait_check
+
+    problems = []
+    for p in asm_paths:
+        with open(p) as f:
+            problems += wait_check.mfma_operand_hazards(f.read())
+    if problems:
+        raise RuntimeError("MFMA operand check failed:\n" + "\n".join(problems[:20]))
+
+
 def _build_ceiling() -> None:
     tmp = CEILING_LIB + ".tmp"
     cmd = [HIPCC, "-x", "hip", *FLAGS, "-shared", os.path.join(CSRC, CEILING_SRC), "-o", tmp]
@@ -98,10 +113,11 @@ def build(verbose: bool = False) -> str:
     libw4a16.so. Returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
-        asm = [ex.submit(_assembly, s) for s in STAGED]
+        asm = {s: ex.submit(_assembly, s) for s in ASSEMBLED}
         objs = list(ex.map(_compile, SOURCES))
-        asm_paths = [f.result() for f in asm]
-    check_waits(asm_paths)
+        asm_paths = {s: f.result() for s, f in asm.items()}
+    check_waits([asm_paths[s] for s in STAGED])
+    check_mfma_operands(list(asm_paths.values()))
     _build_ceiling()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lhipblaslt"]

@@ -37,14 +37,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // representable); v_cvt_pk_bf16_f32 then rounds to nearest even once.
 //
 // The pair extraction (w >> 4p) & 0x000F000F | magic is one v_and_or_b32 per
-// pair (plus the shift). The mask and magic are passed in registers: gfx9
-// VOP3 instructions cannot encode two literal constants, and given literals
-// the compiler splits the operation into v_and_b32 + v_or_b32.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(magic));
-    return r;
-}
+// pair (plus the shift). The mask and magic are passed in registers (callers
+// keep them opaque with an empty asm): gfx9 VOP3 instructions cannot encode
+// two literal constants, and given literals the compiler splits the
+// operation into v_and_b32 + v_or_b32. Plain C rather than inline asm: the
+// result often feeds an MFMA directly, and only an instruction the compiler
+// knows gets the wait states the hardware needs between a VALU write of a
+// register and an MFMA that reads it (an asm result does not).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) { return (x & mask) | magic; }
 
 template <int DT>
 struct Dequant;

@@ -157,7 +157,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
     // loads into the compute below to save registers, serialising round trips.
     __builtin_amdgcn_sched_barrier(0);
 
-    // 4. Dequantise and multiply.
+    // 4. Dequantise and multiply (mask and magic in opaque registers, so
+    // that each pair is one v_and_or_b32).
+    uint32_t dq_mask = a.mask, dq_magic = a.magic;
+    asm volatile("" : "+v"(dq_mask), "+v"(dq_magic));
     floatx4 acc[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -168,8 +171,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
             const int u = s / (4 / SPT);
 #pragma unroll
             for (int i = 0; i < NW; ++i) {
-                const u32x4 b = Dequant<DT>::apply(wq[j][i][s], Dequant<DT>::make(sb[i][j][u], zb[i][j][u]), a.mask,
-                                                   a.magic);
+                const u32x4 b = Dequant<DT>::apply(wq[j][i][s], Dequant<DT>::make(sb[i][j][u], zb[i][j][u]), dq_mask,
+                                                   dq_magic);
                 acc[i] = mfma16x16x32<DT>(av[j][s], b, acc[i]);
             }
         }

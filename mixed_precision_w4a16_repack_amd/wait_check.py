@@ -230,6 +230,69 @@ def check_asm(text: str) -> tuple[int, list[str]]:
     return checked, problems
 
 
+# gfx950 needs 2 wait states between a VALU instruction that writes a VGPR
+# and an MFMA that reads it as an operand; the compiler inserts them for the
+# instructions it emits, but an inline-asm instruction is opaque to its hazard
+# tracking. An MFMA that reads an inline-asm VALU result too soon reads the
+# register's old value (seen on MI355X as a wrong operand dword).
+MFMA_VALU_WAIT_STATES = 2
+
+_VREG = re.compile(r"^v\[(\d+):(\d+)\]$|^v(\d+)$")
+
+
+def _vregs(tok: str) -> set[int]:
+    m = _VREG.match(tok)
+    if not m:
+        return set()
+    if m.group(3) is not None:
+        return {int(m.group(3))}
+    return set(range(int(m.group(1)), int(m.group(2)) + 1))
+
+
+def mfma_operand_hazards(text: str) -> list[str]:
+    """Every MFMA that reads a register written by an inline-asm VALU
+    instruction fewer than MFMA_VALU_WAIT_STATES wait states before it, in
+    listing order (which covers the straight-line code the dequantisation
+    runs in; a label does not reset the history, which can only add
+    reports)."""
+    problems = []
+    for name, lines in _functions(text):
+        hist: list[tuple[int, set[int], bool]] = []  # (wait states, VGPRs written, inline-asm VALU)
+        in_asm = False
+        for raw in lines:
+            t = raw.strip()
+            if t.startswith(";;#ASMSTART"):
+                in_asm = True
+                continue
+            if t.startswith(";;#ASMEND"):
+                in_asm = False
+                continue
+            t = t.split(";")[0].strip()
+            if not t or t.startswith(".") or t.endswith(":"):
+                continue
+            parts = t.replace(",", " ").split()
+            op = parts[0]
+            if op == "s_nop":
+                hist.append((int(parts[1], 0) + 1 if len(parts) > 1 else 1, set(), False))
+                continue
+            if op.startswith("v_mfma"):
+                srcs: set[int] = set()
+                for tok in parts[2:5]:
+                    srcs |= _vregs(tok)
+                ws = 0
+                for w, regs, asm_valu in reversed(hist):
+                    if ws >= MFMA_VALU_WAIT_STATES:
+                        break
+                    if asm_valu and regs & srcs:
+                        problems.append(f"{name}: '{t}' reads an inline-asm VALU result after {ws} wait states")
+                        break
+                    ws += w
+            written = _vregs(parts[1]) if len(parts) > 1 else set()
+            hist.append((1, written, in_asm and op.startswith("v_")))
+            hist = hist[-8:]
+    return problems
+
+
 def main(paths) -> int:
     total, bad = 0, []
     for p in paths:

@@ -4,11 +4,13 @@ The check reads gfx950 assembly; here it runs on small hand-written
 listings whose counts are known (a matching pipeline, a dropped load, an
 extra load on one branch, loads reordered across the last direct-to-LDS
 load, a prologue that issues more stages than it waits for) and on the
-assembly of the committed kernel sources.
+assembly of the committed kernel sources. The same holds for the MFMA
+operand check (an inline-asm VALU result read by an MFMA too soon).
 """
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 
@@ -97,8 +99,59 @@ def test_other_kernels_are_ignored():
     assert n == 0 and probs == []
 
 
-@pytest.mark.skipif(not os.path.exists(lib_build.HIPCC) and shutil.which("hipcc") is None, reason="needs hipcc")
-def test_committed_kernels_pass():
+# MFMA operand hazard: an inline-asm VALU result read by an MFMA needs 2
+# wait states first.
+ASM_AND_OR = "\t;;#ASMSTART\n\tv_and_or_b32 v58, v37, v63, v65\n\t;;#ASMEND\n"
+MFMA = "\tv_mfma_f32_16x16x32_f16 v[50:53], v[14:17], v[58:61], v[50:53]\n"
+
+
+def hazards(body: str):
+    return wait_check.mfma_operand_hazards(listing("_Z18skinny_reg_kernelv", body))
+
+
+def test_asm_result_read_one_wait_state_later_is_found():
+    probs = hazards(ASM_AND_OR + "\ts_nop 0\n" + MFMA)
+    assert probs and "after 1 wait states" in probs[0]
+
+
+def test_asm_result_read_at_once_is_found():
+    assert hazards(ASM_AND_OR + MFMA)
+
+
+def test_two_wait_states_or_other_registers_pass():
+    assert hazards(ASM_AND_OR + "\ts_nop 1\n" + MFMA) == []
+    assert hazards(ASM_AND_OR + "\tv_add_u32_e32 v1, 4, v0\n\tv_add_u32_e32 v2, 4, v0\n" + MFMA) == []
+    other = ASM_AND_OR.replace("v58", "v70")
+    assert hazards(other + MFMA) == []
+
+
+def test_compiler_emitted_valu_is_left_to_the_compiler():
+    assert hazards("\tv_and_or_b32 v58, v37, v63, v65\n" + MFMA) == []
+
+
+def test_accumulator_operand_is_checked_too():
+    acc = ASM_AND_OR.replace("v58", "v51")
+    assert hazards(acc + MFMA)
+
+
+needs_hipcc = pytest.mark.skipif(not os.path.exists(lib_build.HIPCC) and shutil.which("hipcc") is None,
+                                 reason="needs hipcc")
+
+
+@pytest.fixture(scope="module")
+def committed_assembly():
+    """gfx950 assembly of every committed source with MFMA kernels, compiled
+    once for the tests below (in parallel)."""
     os.makedirs(lib_build.BUILD, exist_ok=True)
-    paths = [lib_build._assembly(s) for s in lib_build.STAGED]
-    lib_build.check_waits(paths)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(lib_build.ASSEMBLED)) as ex:
+        return dict(zip(lib_build.ASSEMBLED, ex.map(lib_build._assembly, lib_build.ASSEMBLED)))
+
+
+@needs_hipcc
+def test_committed_kernels_pass(committed_assembly):
+    lib_build.check_waits([committed_assembly[s] for s in lib_build.STAGED])
+
+
+@needs_hipcc
+def test_committed_kernels_have_no_mfma_operand_hazard(committed_assembly):
+    lib_build.check_mfma_operands(list(committed_assembly.values()))
