@@ -137,18 +137,22 @@ __device__ __forceinline__ uint32_t top_pair_shift(uint32_t w) {
 
 // The same shift of two consecutive words held as one 64-bit value (word 0
 // low): one v_lshlrev_b64 / v_lshrrev_b64 serves both. The bits that cross
-// between the halves land outside the nibble masks.
+// between the halves land outside the nibble masks. The empty asm (no
+// instruction) keeps the compiler from narrowing the shift into one per
+// word; the shift itself stays a compiler-emitted instruction, so its
+// register hazards against in-flight MFMAs are tracked.
 template <int DT, int P>
 __device__ __forceinline__ uint64_t top_pair_shift64(uint64_t x) {
     constexpr int sh = TopNibble<DT>::kPos - 4 * P;
     uint64_t y;
     if constexpr (sh > 0) {
-        asm("v_lshlrev_b64 %0, %2, %1" : "=v"(y) : "v"(x), "n"(sh));
+        y = x << sh;
     } else if constexpr (sh < 0) {
-        asm("v_lshrrev_b64 %0, %2, %1" : "=v"(y) : "v"(x), "n"(-sh));
+        y = x >> -sh;
     } else {
         y = x;
     }
+    asm("" : "+v"(y));
     return y;
 }
 

@@ -230,12 +230,16 @@ def check_asm(text: str) -> tuple[int, list[str]]:
     return checked, problems
 
 
-# gfx950 needs 2 wait states between a VALU instruction that writes a VGPR
-# and an MFMA that reads it as an operand; the compiler inserts them for the
-# instructions it emits, but an inline-asm instruction is opaque to its hazard
-# tracking. An MFMA that reads an inline-asm VALU result too soon reads the
-# register's old value (seen on MI355X as a wrong operand dword).
-MFMA_VALU_WAIT_STATES = 2
+# gfx950 needs wait states between a VALU instruction and an MFMA that share
+# a VGPR: 2 between a VALU write and an MFMA that reads the register, and,
+# the other way round, up to a pass count's worth between an MFMA that reads
+# a register (its accumulator input is read late) and a VALU write of it.
+# The compiler inserts them for the instructions it emits, but an inline-asm
+# instruction is opaque to its hazard tracking. An MFMA that read an
+# inline-asm VALU result too soon was seen on MI355X to read the register's
+# old value (a wrong operand dword).
+MFMA_VALU_WAIT_STATES = 2  # VALU write -> MFMA read
+VALU_AFTER_MFMA_WAIT_STATES = 16  # MFMA read -> VALU write (16 passes, the longest here)
 
 _VREG = re.compile(r"^v\[(\d+):(\d+)\]$|^v(\d+)$")
 
@@ -251,13 +255,15 @@ def _vregs(tok: str) -> set[int]:
 
 def mfma_operand_hazards(text: str) -> list[str]:
     """Every MFMA that reads a register written by an inline-asm VALU
-    instruction fewer than MFMA_VALU_WAIT_STATES wait states before it, in
-    listing order (which covers the straight-line code the dequantisation
-    runs in; a label does not reset the history, which can only add
-    reports)."""
+    instruction fewer than MFMA_VALU_WAIT_STATES wait states before it, and
+    every inline-asm VALU instruction that writes a register an MFMA read
+    fewer than VALU_AFTER_MFMA_WAIT_STATES wait states before, in listing
+    order (which covers the straight-line code the dequantisation runs in;
+    a label does not reset the history, which can only add reports)."""
     problems = []
     for name, lines in _functions(text):
-        hist: list[tuple[int, set[int], bool]] = []  # (wait states, VGPRs written, inline-asm VALU)
+        # (wait states, VGPRs written, inline-asm VALU, VGPRs an MFMA read)
+        hist: list[tuple[int, set[int], bool, set[int]]] = []
         in_asm = False
         for raw in lines:
             t = raw.strip()
@@ -273,23 +279,33 @@ def mfma_operand_hazards(text: str) -> list[str]:
             parts = t.replace(",", " ").split()
             op = parts[0]
             if op == "s_nop":
-                hist.append((int(parts[1], 0) + 1 if len(parts) > 1 else 1, set(), False))
+                hist.append((int(parts[1], 0) + 1 if len(parts) > 1 else 1, set(), False, set()))
                 continue
+            written = _vregs(parts[1]) if len(parts) > 1 else set()
+            asm_valu = in_asm and op.startswith("v_")
+            read: set[int] = set()
             if op.startswith("v_mfma"):
-                srcs: set[int] = set()
                 for tok in parts[2:5]:
-                    srcs |= _vregs(tok)
+                    read |= _vregs(tok)
                 ws = 0
-                for w, regs, asm_valu in reversed(hist):
+                for w, regs, prev_asm, _ in reversed(hist):
                     if ws >= MFMA_VALU_WAIT_STATES:
                         break
-                    if asm_valu and regs & srcs:
+                    if prev_asm and regs & read:
                         problems.append(f"{name}: '{t}' reads an inline-asm VALU result after {ws} wait states")
                         break
                     ws += w
-            written = _vregs(parts[1]) if len(parts) > 1 else set()
-            hist.append((1, written, in_asm and op.startswith("v_")))
-            hist = hist[-8:]
+            if asm_valu and written:
+                ws = 0
+                for w, _, _, mread in reversed(hist):
+                    if ws >= VALU_AFTER_MFMA_WAIT_STATES:
+                        break
+                    if mread & written:
+                        problems.append(f"{name}: inline-asm '{t}' writes a register an MFMA read {ws} wait states before")
+                        break
+                    ws += w
+            hist.append((1, written, asm_valu, read))
+            hist = hist[-40:]
     return problems
 
 

@@ -134,6 +134,16 @@ def test_accumulator_operand_is_checked_too():
     assert hazards(acc + MFMA)
 
 
+ASM_SHIFT = "\t;;#ASMSTART\n\tv_lshlrev_b64 v[50:51], 2, v[114:115]\n\t;;#ASMEND\n"
+
+
+def test_asm_write_of_a_register_an_mfma_just_read_is_found():
+    probs = hazards(MFMA + ASM_SHIFT)
+    assert probs and "writes a register an MFMA read 0 wait states before" in probs[0]
+    assert hazards(MFMA + "\ts_nop 7\n" * 2 + ASM_SHIFT) == []
+    assert hazards(MFMA + ASM_SHIFT.replace("v[50:51]", "v[80:81]")) == []
+
+
 needs_hipcc = pytest.mark.skipif(not os.path.exists(lib_build.HIPCC) and shutil.which("hipcc") is None,
                                  reason="needs hipcc")
 
