@@ -162,11 +162,13 @@ w4a16_status w4a16_unpack(const void *packed, int64_t N, int64_t K, int32_t grou
                           uint8_t *codes, uint16_t *scale_bits, uint8_t *zeros, hipStream_t stream);
 
 /* Bytes of device workspace w4a16_gemm needs for these arguments (0 if none).
- * out_bytes is a host pointer. The workspace holds split-K partial sums and
- * arrival counters: of the skinny kernels (M <= 16: narrow weights, and
- * K > 4096 unless M <= 4 with one fold block per 128 k) and of the tiled
- * kernel for medium M (17 rows up to where its 128 x 256 tiles fill the CUs
- * on their own). The size for M = 16 serves every M <= 16. Its first
+ * out_bytes is a host pointer. The workspace starts with a region of
+ * w4a16_workspace_counter_bytes() bytes of arrival counters, followed by
+ * split-K partial sums: of the skinny kernels (M <= 16: narrow weights, and
+ * K > 4096 unless M <= 4 with one fold block per 128 k; these also use the
+ * counters) and of the tiled kernel for medium M (17 rows up to where its
+ * 128 x 256 tiles fill the CUs on their own; partial sums only). The size
+ * for M = 16 serves every M <= 16. Its first
  * w4a16_workspace_counter_bytes() bytes must be
  * zero before it is first used; every completed w4a16_gemm call leaves them
  * zero again, so a workspace can be reused for any shape. Calls that share a
